@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the InfiniGen hot path on one MI355X.
+
+Workload: OPT-6.7B-shaped decode layer (hidden 4096, 32 heads of 128, batch 8,
+context 2048, 32 partial channels, bf16 storage, fp32 accumulation), top-k 128
+per head (``--mode threshold``: alpha 5 with the 20% cap).  One step = one
+decode step through ``--layers`` distinct layers (distinct HBM buffers with the
+same contents, so that the 256 MB Infinity Cache cannot serve the working set),
+each running the whole hot path: ig_rehearse -> ig_select ->
+ig_sparse_decode_attn -> ig_pool_touch.
+
+Prints one JSON line: tokens/s per layer (= batch x layers x steps / time),
+the roofline of the dominant call (algorithmic bytes per launch over its
+average duration from HIP events, against 8 TB/s), and the CPU oracle timed on
+a bounded sample of the same workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode step tokens/s per layer (rehearse+select+sparse attn) + % HBM peak"
+
+
+def alg_bytes(spec, c: float) -> dict:
+    """Algorithmic bytes of one layer-step by call (c = mean selected rows per head)."""
+    s = 2 if spec.dtype == "bf16" else 4
+    B, H, D, d, r, n = spec.B, spec.H, spec.D, spec.d, spec.r, spec.n
+    return {
+        "rehearse": D * H * r * s + B * D * s + B * H * n * r * s,
+        "select": 0.0,                                   # scores are an implementation round trip
+        "attn": B * H * c * 2 * d * s + B * H * d * s + B * H * d * 4 + B * H * c * 4,
+        "touch": B * H * c * 4,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=32, help="distinct layer buffers per step")
+    ap.add_argument("--mode", choices=["topk", "threshold"], default="topk")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path has no multi-GPU "
+              f"mode: the path would shard over (batch, head) with no exchange)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from sparse_attention_ig_amd import _lib, gen
+    from sparse_attention_ig_amd.runtime import DeviceLayer, prepare_layer, to_host
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        return 1
+    _lib.load()
+
+    spec = gen.opt_6_7b()
+    if args.mode == "topk":
+        step_kw = dict(mode="topk", k=spec.topk, max_out=spec.topk)
+        wl = f"opt-6.7b decode layer B{spec.B} H{spec.H} d{spec.d} D{spec.D} n{spec.n} r{spec.r} bf16 top-{spec.topk}"
+    else:
+        step_kw = dict(mode="threshold", alpha=spec.alpha, max_sel=spec.max_sel, max_out=spec.max_sel)
+        wl = (f"opt-6.7b decode layer B{spec.B} H{spec.H} d{spec.d} D{spec.D} n{spec.n} r{spec.r} bf16 "
+              f"alpha={spec.alpha} cap={spec.max_sel}")
+    print(f"[bench] preparing {wl} x {args.layers} layers", file=sys.stderr, flush=True)
+    host = prepare_layer(spec)
+    base = DeviceLayer(host, max_out=step_kw["max_out"])
+    layers = [base] + [base.clone() for _ in range(args.layers - 1)]
+    torch.cuda.synchronize()
+    footprint = sum(l.nbytes() for l in layers)
+    stream = torch.cuda.current_stream()
+
+    def one_step(events=None, li_events=None):
+        for i, l in enumerate(layers):
+            l.step(**step_kw, stream=stream, events=(li_events[i] if li_events else None))
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly --steps steps, synchronised on both sides
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    tok_s_layer = spec.B * args.layers * args.steps / (ms_total / 1e3)
+
+    # per-call durations: HIP events around every call of every layer, over the same number of steps
+    names = ("rehearse", "select", "attn", "touch")
+    per = {n: 0.0 for n in names}
+    inst_steps = args.steps
+    for _ in range(inst_steps):
+        evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+               for _ in layers]
+        one_step(li_events=evs)
+        torch.cuda.synchronize()
+        for e in evs:
+            for n in names:
+                per[n] += e[n][0].elapsed_time(e[n][1])
+    calls = inst_steps * len(layers)
+    per_us = {n: 1e3 * per[n] / calls for n in names}
+
+    res = to_host(layers[0].count)
+    c_mean = float(res.mean())
+    ab = alg_bytes(spec, c_mean)
+    step_bytes = sum(ab.values())
+    t_layer_s = ms_step / 1e3 / args.layers
+    dominant = max(per_us, key=per_us.get)
+    dom_bytes = ab[dominant]
+    dom_gbs = dom_bytes / (per_us[dominant] * 1e-6) / 1e9 if dom_bytes else 0.0
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s_layer, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded OPT-6.7B-shaped draws, no weights or datasets)",
+        "config": {"workload": wl, "layers_per_step": args.layers, "footprint_GB": round(footprint / 1e9, 2),
+                   "mean_selected_per_head": round(c_mean, 1)},
+        "t_layer_us": round(t_layer_s * 1e6, 3),
+        "step_alg_bytes_per_layer": int(step_bytes),
+        "step_hbm_GBs": round(step_bytes / t_layer_s / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / t_layer_s / 1e9 / HBM_PEAK_GBS, 4),
+        "per_call_us": {k: round(v, 3) for k, v in per_us.items()},
+        "roofline": {"kernel": f"ig_{dominant}", "bound": "hbm", "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "alg_bytes_per_launch": int(dom_bytes)},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, step_kw, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(spec, step_kw, seconds: float) -> dict:
+    """The CPU oracle (float64 NumPy, one thread) on the same layer-step, repeated for ~seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from tests import harness
+
+    with threadpool_limits(1):
+        oi = harness.oracle_inputs(spec)
+        kw = dict(step_kw)
+        C0 = np.zeros((spec.B, spec.cap), np.uint32)
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            harness.oracle_step(oi, counters=C0, **kw)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(spec.B * reps / el, 2), "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full layer-steps of the same workload (1 layer, all {spec.B}x{spec.H} heads), "
+                      f"{el:.1f} s, BLAS limited to 1 thread"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,227 @@
+/*
+ * ig.h -- C ABI of the MI355X (gfx950) InfiniGen decode hot path.
+ *
+ * Method: "InfiniGen: Efficient Generative Inference of Large Language Models
+ * with Dynamic KV Cache Management" (arXiv 2406.19707), as summarised on the
+ * paper-graph-ui page for that paper, section 3.4 ("Detailed, Sentence-Based
+ * Technical Breakdown") and section 2 ("Context and Motivation").
+ *
+ * Conventions for every call
+ *  - Return value: IG_OK, or an error code.  IG_EINVAL: an argument is
+ *    invalid; detected on the host before anything is launched, nothing is
+ *    written.  IG_EHIP: the HIP runtime reported an error.  IG_EUNSUPPORTED:
+ *    a valid but unimplemented shape.  ig_last_error() returns the message of
+ *    the last failing call on the calling thread.  No C++ exception crosses
+ *    this boundary.
+ *  - Ownership: the caller owns every buffer.  The library keeps no state and
+ *    allocates no device memory; scratch comes from the caller through
+ *    `ws` / `ws_bytes`, sized by ig_workspace_size().  Workspace contents on
+ *    entry are ignored.
+ *  - Device calls are asynchronous on `stream`; they never synchronise and
+ *    never read device buffers on the host.  Device pointers must be 16-byte
+ *    aligned.  Host calls (ig_skew_*, ig_store, ig_partial_weight_index) are
+ *    synchronous and touch no GPU.
+ *  - Layouts are row-major.  B = batch, H = heads, d = head dim, D = hidden
+ *    (the attention input width), r = partial channels per head, n = valid
+ *    cached rows (N + i), n_cap = allocated rows per (b, h).  Element dtype is
+ *    IG_F32 (float) or IG_BF16 (bfloat16 bits in uint16_t); accumulation and
+ *    every produced score, logit and output is float32.
+ *  - Constraints checked: all sizes >= 1; r <= d; r / (16 / sizeof(element))
+ *    a power of two <= 32 (r in {8, 16, 32, 64, 128, 256} for bf16,
+ *    {8, 16, 32, 64, 128} for f32); d / (16 / sizeof(element)) a power of two
+ *    between 4 and 32 (d in {32, 64, 128, 256} for bf16, {16, 32, 64, 128} for
+ *    f32); n <= n_cap.
+ */
+#ifndef IG_H_
+#define IG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { IG_OK = 0, IG_EINVAL = 1, IG_EHIP = 2, IG_EUNSUPPORTED = 3 };
+enum { IG_F32 = 0, IG_BF16 = 1 };
+enum { IG_SEL_THRESHOLD = 0, IG_SEL_TOPK = 1, IG_SEL_HEADAVG = 2 };
+enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2 };
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* ig_last_error(void);
+/* ABI version: bumped on any signature change. */
+int ig_version(void);
+
+/* ------------------------------------------------------------------ host, offline setup */
+
+/* Arguments of ig_skew_weights.  All host memory, float64. */
+typedef struct {
+    int D, H, d;                /* hidden, heads, head dim (weights are [D][H*d]) */
+    int m;                      /* rows of each head's skew source, m >= d */
+    const double* skew_src;     /* [H][m][d]: the sample query of each head (or any matrix whose
+                                   right singular vectors define that head's rotation) */
+    const double* Wq;           /* [D][H*d] or NULL */
+    const double* Wk;           /* [D][H*d] or NULL */
+    const double* bq;           /* [H*d] or NULL */
+    const double* bk;           /* [H*d] or NULL */
+    double* A;                  /* out [H][d][d]; column j = j-th right singular vector */
+    double* sigma;              /* out [H][d] singular values, descending; may be NULL */
+    double* Wq_s;               /* out [D][H*d] = Wq A (per head block); NULL iff Wq is NULL */
+    double* Wk_s;               /* out, NULL iff Wk is NULL */
+    double* bq_s;               /* out [H*d], NULL iff bq is NULL */
+    double* bk_s;               /* out, NULL iff bk is NULL */
+    int nthreads;               /* host threads (<= 0: all hardware threads) */
+} ig_skew_args;
+
+/*
+ * Offline skewing (section 3.4, "Skewed Partial Weights"): for each head,
+ * A_h = V_h from the SVD skew_src_h = U S V^T (one-sided Jacobi in float64),
+ * columns ordered by descending singular value, each column signed so that its
+ * largest-magnitude entry is positive (lowest row index on equal magnitudes).
+ * Then W~ = W A and b~ = b A per head block, so that Q~ K~^T = Q K^T.
+ * The rotation is unique up to those signs only when the singular values are
+ * distinct and m >= d.  IG_EINVAL on NULL required pointers, m < d, d < 1.
+ */
+int ig_skew_weights(const ig_skew_args* args);
+
+/*
+ * Rotate every head block of a row-major [rows][H*d] float64 matrix by that
+ * head's A_h: out[:, h*d:(h+1)*d] = M[:, h*d:(h+1)*d] A_h (queries or keys
+ * given in the unrotated basis; same section).  out must not alias M.
+ */
+int ig_skew_apply(const double* A, int H, int d, const double* M, int64_t rows,
+                  double* out, int nthreads);
+
+/*
+ * Store float64 setup results in the element dtype: round to float32
+ * (nearest-even); for IG_BF16 round that float32 to bfloat16 (nearest-even).
+ */
+int ig_store(const double* vals, int64_t count, int dtype, void* out);
+
+/*
+ * Partial weight index generation (section 3.4, "Prefill Stage: Partial
+ * Weight Index Generation", steps 2-3).  Per head h, channel score
+ *   score[c] = sum_i |Wq_s[i][h*d+c]| + sum_{b, j<n} |K_s[b][h][j][c]|
+ * (float64 sums of the stored values); chan[h] = the r highest-scoring
+ * channels (ties: lower channel), ascending.  Wq_part[i][h*r+k] =
+ * Wq_s[i][h*d + chan[h][k]] (a copy of the stored elements).
+ * Host pointers: Wq_s [D][H*d] dtype; K_s [B][H][n_cap][d] dtype (rows < n
+ * used); chan [H][r] int32 out; Wq_part [D][H*r] dtype out.
+ */
+int ig_partial_weight_index(const void* Wq_s, int D, int H, int d, int r,
+                            const void* K_s, int B, int n_cap, int n, int dtype,
+                            int32_t* chan, void* Wq_part, int nthreads);
+
+/* ------------------------------------------------------------------ device calls */
+
+/*
+ * Bytes of scratch a call needs (0 if none).  op = IG_OP_REHEARSE: B, H, D,
+ * r used.  IG_OP_SELECT: B, H, n, max_out used.  IG_OP_ATTN: B, H, d,
+ * max_out used.  Unused arguments are ignored.
+ */
+size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int max_out);
+
+/*
+ * Speculation for the next layer (section 3.4, "Decoding Stage", steps 1-2):
+ *   q_part[b][h][c]  = sum_i x[b][i] Wq_part[i][h*r+c] (+ bq_part[h*r+c])
+ *   scores[b][h][j]  = scale * sum_c q_part[b][h][c] Kp[b][h][j][c],  j < n
+ * x [B][D] dtype (this layer's attention input); Wq_part [D][H*r] dtype (the
+ * next layer's partial query weight); bq_part [H*r] float or NULL;
+ * Kp [B][H][n_cap][r] dtype (the next layer's partial key cache);
+ * q_part [B][H][r] float out; scores [B][H][ld] float out (ld >= n; columns
+ * >= n untouched).  scale: the softmax scale of the attention (e.g. 1/sqrt(d)).
+ */
+int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
+                int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
+                float* q_part, float* scores, int ld,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Per-head token selection (section 3.4, "Decoding Stage", steps 3-5).
+ *  IG_SEL_THRESHOLD: S = {j < n : s_j >= max_j s_j - alpha} (alpha >= 0,
+ *    +inf allowed); if |S| exceeds max_sel (> 0) or max_out, S keeps its
+ *    largest scores (the per-layer cap).
+ *  IG_SEL_TOPK: S = the min(k, n, max_out) largest scores (k >= 1).
+ *  IG_SEL_HEADAVG: every head of a sequence takes the same count, the mean
+ *    over heads of its threshold counts rounded up (then limited by max_sel
+ *    and max_out); each head keeps its largest scores.
+ * Ties go to the lower index; the comparison is in float32.  Output:
+ * idx [B][H][max_out] int32 ascending (entries >= count unspecified),
+ * count [B][H] int32 in [1, max_out].  Scores must not be NaN.
+ */
+int ig_select(const float* scores, int B, int H, int n, int ld, int mode,
+              float alpha, int k, int max_sel,
+              int32_t* idx, int32_t* count, int max_out,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Fetch the full key and value rows of the selected tokens into compact
+ * buffers (section 3.4, "Decoding Stage", step 5):
+ *   Kc[b][h][i][:] = K[b][h][idx[b][h][i]][:],  i < count[b][h]  (same for V)
+ * K, V [B][H][n_cap][d] dtype, in device memory or in pinned host memory
+ * mapped into the device address space (zero-copy reads over the host link);
+ * Kc, Vc [B][H][max_out][d] device.  Rows >= count are untouched.  Index
+ * values outside [0, n_cap) are clamped into it.
+ */
+int ig_gather_kv(const void* K, const void* V, const int32_t* idx, const int32_t* count,
+                 int B, int H, int d, int n_cap, int max_out, int dtype,
+                 void* Kc, void* Vc, hipStream_t stream);
+
+/*
+ * Attention over the selected rows only (section 3.2, Inference Controller;
+ * section 2, softmax(QK^T)V):
+ *   o[b][h] = sum_{i<c} p_i V[b][h][row_i],  p = softmax_i(scale q[b][h].K[b][h][row_i])
+ *   lse[b][h] = log sum_i exp(scale q.K_row_i)     (natural log)
+ * with c = min(count[b][h], max_out) and row_i = idx[b][h][i], or row_i = i
+ * when idx is NULL (dense over the first count rows, or a compact buffer).
+ * q [B][H][d] dtype; K, V [B][H][ld_rows][d] dtype; out [B][H][d] float;
+ * lse [B][H] float or NULL.  c = 0 gives o = 0, lse = -inf.  Index values
+ * outside [0, ld_rows) are clamped into it.
+ */
+int ig_sparse_decode_attn(const void* q, const void* K, const void* V, int ld_rows,
+                          const int32_t* idx, const int32_t* count,
+                          int B, int H, int d, int max_out, int dtype, float scale,
+                          float* out, float* lse,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Counter-based pool policy (section 3.4, "KV Cache Pool Management Under
+ * Memory Pressure"): every (head, selected slot) adds 1 to the slot's counter;
+ * C <- min(C + inc, cmax); if any slot j < n of a sequence then holds cmax,
+ * all its slots j < n are halved (floor).  victim[b] (if not NULL) = the
+ * lowest index among the minima of C[b][0..n).  counters [B][n_cap] uint32,
+ * updated in place; precondition C[b][j] < cmax for j < n.  Indices of one
+ * head must be distinct; values outside [0, n) are ignored.  cmax >= 2.
+ */
+int ig_pool_touch(uint32_t* counters, const int32_t* idx, const int32_t* count,
+                  int B, int H, int n, int n_cap, int max_out, uint32_t cmax,
+                  int32_t* victim, hipStream_t stream);
+
+/*
+ * Build rows [row0, row1) of the partial key cache from the skewed key cache
+ * (section 3.4, prefill step 3): Kp[b][h][j][c] = K[b][h][j][chan[h][c]].
+ * K [B][H][n_cap][d], Kp [B][H][n_cap][r] dtype; chan [H][r] int32 device.
+ */
+int ig_build_partial_cache(const void* K, const int32_t* chan, void* Kp,
+                           int B, int H, int d, int r, int n_cap, int row0, int row1,
+                           int dtype, hipStream_t stream);
+
+/*
+ * Append one decoded token per sequence (section 3.4, "Partial Key Cache
+ * Updates During Decoding" and the pool paragraph): slot = n if n < n_cap,
+ * else victim[b] (victim required then); K[b][h][slot] = k_new[b][h],
+ * V[b][h][slot] = v_new[b][h], Kp[b][h][slot][c] = k_new[b][h][chan[h][c]],
+ * counters[b][slot] = 0 (if counters not NULL); slot_out[b] = slot (if not
+ * NULL).  k_new, v_new [B][H][d] dtype.
+ */
+int ig_append_kv(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan,
+                 const void* k_new, const void* v_new, const int32_t* victim,
+                 int B, int H, int d, int r, int n_cap, int n, int dtype,
+                 int32_t* slot_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IG_H_ */

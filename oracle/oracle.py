@@ -106,7 +106,7 @@ def skew_weights(Wq, Wk, src, bq=None, bk=None):
 
 # ---------------------------------------------------------------- prefill: partial weight index generation
 def partial_weight_index(Wq_s: np.ndarray, K_s: np.ndarray, H: int, d: int, r: int,
-                         n: Optional[int] = None) -> np.ndarray:
+                         n: Optional[int] = None, dtype: Optional[str] = None) -> np.ndarray:
     """Channel pick of section 3.4, "Prefill Stage: Partial Weight Index Generation", step 2:
     take element-wise absolute values of the skewed query weight and of the skewed key cache,
     sum each over its rows, add the two column-sum vectors, keep the top r columns.
@@ -114,16 +114,16 @@ def partial_weight_index(Wq_s: np.ndarray, K_s: np.ndarray, H: int, d: int, r: i
     Readings: r columns per head (the pages' "k" read per head); the element-wise sum of the
     two differently shaped matrices is read as the sum of their column-sum vectors; ties go to
     the lower channel index; indices are returned ascending.
-    Wq_s: [D][H*d] values; K_s: [B][H][rows][d] values (first n rows used) -> chan [H][r] int32.
+    Wq_s: [D][H*d]; K_s: [B][H][rows][d] (first n rows used); values, or stored bits when dtype
+    is given (decoded one head at a time) -> chan [H][r] int32.
     """
-    Wq_s = np.asarray(Wq_s, dtype=np.float64)
-    K_s = np.asarray(K_s, dtype=np.float64)
+    dec = (lambda a: np.asarray(a, dtype=np.float64)) if dtype is None else (lambda a: decode(a, dtype))
     if n is None:
         n = K_s.shape[2]
     chan = np.zeros((H, r), dtype=np.int32)
     for h in range(H):
-        score = np.abs(Wq_s[:, h * d:(h + 1) * d]).sum(axis=0) \
-            + np.abs(K_s[:, h, :n, :]).sum(axis=(0, 1))
+        score = np.abs(dec(Wq_s[:, h * d:(h + 1) * d])).sum(axis=0) \
+            + np.abs(dec(K_s[:, h, :n, :])).sum(axis=(0, 1))
         order = sorted(range(d), key=lambda c: (-score[c], c))
         chan[h] = np.sort(np.asarray(order[:r], dtype=np.int32))
     return chan

@@ -1,0 +1,196 @@
+// C ABI of the InfiniGen decode hot path (include/ig.h): argument validation,
+// error reporting and dispatch to the kernel launchers.  Every check happens
+// on the host before anything is enqueued, so an IG_EINVAL call writes
+// nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include <hip/hip_runtime.h>
+
+#include "ig_internal.h"
+
+namespace ig {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return IG_OK;
+}
+
+static int hip_status(int e, const char* what) {
+    if (e == 0) return ok();
+    return fail(IG_EHIP, "%s: HIP error %d (%s)", what, e, hipGetErrorString(static_cast<hipError_t>(e)));
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int elem_size(int dtype) { return dtype == IG_BF16 ? 2 : 4; }
+
+static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// d / (16 / element size) must be 4, 8, 16 or 32 lanes per row
+static bool head_dim_ok(int d, int dtype) {
+    const int vec = 16 / elem_size(dtype);
+    if (d % vec) return false;
+    const int lpr = d / vec;
+    return pow2(lpr) && lpr >= 4 && lpr <= 32;
+}
+
+#define IG_REQUIRE(cond, ...)                                  \
+    do {                                                       \
+        if (!(cond)) return fail(IG_EINVAL, __VA_ARGS__);      \
+    } while (0)
+
+#define IG_REQUIRE_DTYPE(fn, dtype) IG_REQUIRE((dtype) == IG_F32 || (dtype) == IG_BF16, fn ": unknown dtype %d", dtype)
+
+}  // namespace ig
+
+using namespace ig;
+
+extern "C" {
+
+const char* ig_last_error(void) { return g_err; }
+
+int ig_version(void) { return 1; }
+
+int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
+
+int ig_skew_apply(const double* A, int H, int d, const double* M, int64_t rows, double* out, int nthreads) {
+    return skew_apply(A, H, d, M, rows, out, nthreads);
+}
+
+int ig_store(const double* vals, int64_t count, int dtype, void* out) { return store(vals, count, dtype, out); }
+
+int ig_partial_weight_index(const void* Wq_s, int D, int H, int d, int r, const void* K_s, int B, int n_cap, int n,
+                            int dtype, int32_t* chan, void* Wq_part, int nthreads) {
+    return partial_weight_index(Wq_s, D, H, d, r, K_s, B, n_cap, n, dtype, chan, Wq_part, nthreads);
+}
+
+size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int max_out) {
+    if (B < 1 || H < 1) return 0;
+    switch (op) {
+        case IG_OP_REHEARSE:
+            if (D < 1 || r < 1 || n < 1) return 0;
+            return plan_rehearse(B, H, D, r, n, IG_BF16).ws_bytes;
+        case IG_OP_SELECT:
+            return select_ws_bytes(B, H, n, max_out);
+        case IG_OP_ATTN:
+            if (d < 1 || max_out < 1) return 0;
+            return plan_attn(B, H, d, max_out).ws_bytes;
+        default:
+            return 0;
+    }
+}
+
+int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H, int r,
+                int n, int n_cap, int dtype, float scale, float* q_part, float* scores, int ld, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_rehearse", dtype);
+    IG_REQUIRE(x && Wq_part && Kp && q_part && scores, "ig_rehearse: NULL required pointer");
+    IG_REQUIRE(B >= 1 && D >= 1 && H >= 1 && r >= 1 && n >= 1 && n <= n_cap && ld >= n,
+               "ig_rehearse: bad sizes (B=%d D=%d H=%d r=%d n=%d n_cap=%d ld=%d)", B, D, H, r, n, n_cap, ld);
+    IG_REQUIRE(r % 8 == 0 && pow2(r / (16 / elem_size(dtype))) && r / (16 / elem_size(dtype)) <= 32,
+               "ig_rehearse: r / (16 / element size) must be a power of two <= 32 (got r=%d)", r);
+    IG_REQUIRE(std::isfinite(scale), "ig_rehearse: scale must be finite");
+    IG_REQUIRE(aligned16(Wq_part) && aligned16(Kp), "ig_rehearse: Wq_part and Kp must be 16-byte aligned");
+    const RehearsePlan p = plan_rehearse(B, H, D, r, n, dtype);
+    IG_REQUIRE(ws && ws_bytes >= p.ws_bytes, "ig_rehearse: workspace of %zu bytes needed (got %zu)", p.ws_bytes,
+               ws ? ws_bytes : static_cast<size_t>(0));
+    return hip_status(launch_rehearse(x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, q_part, scores,
+                                      ld, ws, stream),
+                      "ig_rehearse");
+}
+
+int ig_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k, int max_sel,
+              int32_t* idx, int32_t* count, int max_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    IG_REQUIRE(scores && idx && count, "ig_select: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && n >= 1 && ld >= n && max_out >= 1,
+               "ig_select: bad sizes (B=%d H=%d n=%d ld=%d max_out=%d)", B, H, n, ld, max_out);
+    IG_REQUIRE(mode == IG_SEL_THRESHOLD || mode == IG_SEL_TOPK || mode == IG_SEL_HEADAVG,
+               "ig_select: unknown mode %d", mode);
+    IG_REQUIRE(max_sel >= 0, "ig_select: max_sel must be >= 0");
+    if (mode != IG_SEL_TOPK)
+        IG_REQUIRE(alpha >= 0.f && !std::isnan(alpha), "ig_select: alpha must be >= 0 (inf allowed)");
+    else
+        IG_REQUIRE(k >= 1, "ig_select: k must be >= 1");
+    const size_t need = mode == IG_SEL_HEADAVG ? select_ws_bytes(B, H, n, max_out) : 0;
+    IG_REQUIRE(need == 0 || (ws && ws_bytes >= need), "ig_select: workspace of %zu bytes needed", need);
+    return hip_status(launch_select(scores, B, H, n, ld, mode, alpha, k, max_sel, idx, count, max_out, ws, stream),
+                      "ig_select");
+}
+
+int ig_gather_kv(const void* K, const void* V, const int32_t* idx, const int32_t* count, int B, int H, int d,
+                 int n_cap, int max_out, int dtype, void* Kc, void* Vc, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_gather_kv", dtype);
+    IG_REQUIRE(K && V && idx && count && Kc && Vc, "ig_gather_kv: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && n_cap >= 1 && max_out >= 1, "ig_gather_kv: bad sizes");
+    IG_REQUIRE(head_dim_ok(d, dtype), "ig_gather_kv: unsupported head dim %d", d);
+    IG_REQUIRE(aligned16(K) && aligned16(V) && aligned16(Kc) && aligned16(Vc),
+               "ig_gather_kv: K, V, Kc, Vc must be 16-byte aligned");
+    return hip_status(launch_gather(K, V, idx, count, B, H, d, n_cap, max_out, dtype, Kc, Vc, stream),
+                      "ig_gather_kv");
+}
+
+int ig_sparse_decode_attn(const void* q, const void* K, const void* V, int ld_rows, const int32_t* idx,
+                          const int32_t* count, int B, int H, int d, int max_out, int dtype, float scale, float* out,
+                          float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_sparse_decode_attn", dtype);
+    IG_REQUIRE(q && K && V && count && out, "ig_sparse_decode_attn: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && ld_rows >= 1 && max_out >= 1,
+               "ig_sparse_decode_attn: bad sizes (B=%d H=%d ld_rows=%d max_out=%d)", B, H, ld_rows, max_out);
+    IG_REQUIRE(head_dim_ok(d, dtype), "ig_sparse_decode_attn: unsupported head dim %d", d);
+    IG_REQUIRE(std::isfinite(scale), "ig_sparse_decode_attn: scale must be finite");
+    IG_REQUIRE(aligned16(q) && aligned16(K) && aligned16(V), "ig_sparse_decode_attn: q, K, V must be 16-byte aligned");
+    const AttnPlan p = plan_attn(B, H, d, max_out);
+    IG_REQUIRE(p.ws_bytes == 0 || (ws && ws_bytes >= p.ws_bytes),
+               "ig_sparse_decode_attn: workspace of %zu bytes needed", p.ws_bytes);
+    return hip_status(launch_attn(q, K, V, ld_rows, idx, count, B, H, d, max_out, dtype, scale, out, lse, ws, stream),
+                      "ig_sparse_decode_attn");
+}
+
+int ig_pool_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n, int n_cap,
+                  int max_out, uint32_t cmax, int32_t* victim, hipStream_t stream) {
+    IG_REQUIRE(counters && idx && count, "ig_pool_touch: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && n >= 1 && n <= n_cap && max_out >= 1,
+               "ig_pool_touch: bad sizes (B=%d H=%d n=%d n_cap=%d max_out=%d)", B, H, n, n_cap, max_out);
+    IG_REQUIRE(cmax >= 2, "ig_pool_touch: cmax must be >= 2");
+    return hip_status(launch_touch(counters, idx, count, B, H, n, n_cap, max_out, cmax, victim, stream),
+                      "ig_pool_touch");
+}
+
+int ig_build_partial_cache(const void* K, const int32_t* chan, void* Kp, int B, int H, int d, int r, int n_cap,
+                           int row0, int row1, int dtype, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_build_partial_cache", dtype);
+    IG_REQUIRE(K && chan && Kp, "ig_build_partial_cache: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && d >= 1 && r >= 1 && r <= d && 0 <= row0 && row0 <= row1 && row1 <= n_cap,
+               "ig_build_partial_cache: bad sizes");
+    if (row0 == row1) return ok();
+    return hip_status(launch_build_partial(K, chan, Kp, B, H, d, r, n_cap, row0, row1, dtype, stream),
+                      "ig_build_partial_cache");
+}
+
+int ig_append_kv(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan, const void* k_new,
+                 const void* v_new, const int32_t* victim, int B, int H, int d, int r, int n_cap, int n, int dtype,
+                 int32_t* slot_out, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_append_kv", dtype);
+    IG_REQUIRE(K && V && Kp && chan && k_new && v_new, "ig_append_kv: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && d >= 1 && r >= 1 && r <= d && 0 <= n && n <= n_cap && n_cap >= 1,
+               "ig_append_kv: bad sizes");
+    IG_REQUIRE(n < n_cap || victim, "ig_append_kv: the pool is full (n == n_cap): victim is required");
+    return hip_status(launch_append(K, V, Kp, counters, chan, k_new, v_new, victim, B, H, d, r, n_cap, n, dtype,
+                                    slot_out, stream),
+                      "ig_append_kv");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the C-ABI layer, the host setup and the
+// kernel launchers.  Not part of the public interface (include/ig.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/ig.h"
+
+namespace ig {
+
+// Record an error message for ig_last_error() (thread-local) and return code.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int ok();
+
+// host setup (ig_setup.cpp)
+int skew_weights(const ig_skew_args* a);
+int skew_apply(const double* A, int H, int d, const double* M, int64_t rows, double* out, int nthreads);
+int store(const double* vals, int64_t count, int dtype, void* out);
+int partial_weight_index(const void* Wq_s, int D, int H, int d, int r, const void* K_s, int B,
+                         int n_cap, int n, int dtype, int32_t* chan, void* Wq_part, int nthreads);
+
+// Launch plans: every workspace size and grid is derived from these, so the
+// size query and the launch always agree.
+struct RehearsePlan {
+    int tiles;       // 64-column tiles of H*r
+    int splits;      // split of the D reduction
+    int rows_per_split;
+    int bblocks;     // batch blocks
+    int bb;          // batch rows per block (1, 2, 4, 8 or 16)
+    int chunk;       // Kp rows per score workgroup
+    int chunks;
+    size_t ws_bytes; // split partials [splits][B][H*r] float
+};
+RehearsePlan plan_rehearse(int B, int H, int D, int r, int n, int dtype);
+
+struct AttnPlan {
+    int rows_per_split;
+    int nsplit;
+    size_t ws_bytes; // [B*H][nsplit][2 + d] float when nsplit > 1
+};
+AttnPlan plan_attn(int B, int H, int d, int max_out);
+
+size_t select_ws_bytes(int B, int H, int n, int max_out);
+
+// kernel launchers (return hipError_t as int)
+int launch_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
+                    int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
+                    float* q_part, float* scores, int ld, void* ws, hipStream_t s);
+int launch_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k,
+                  int max_sel, int32_t* idx, int32_t* count, int max_out, void* ws, hipStream_t s);
+int launch_attn(const void* q, const void* K, const void* V, int ld_rows, const int32_t* idx,
+                const int32_t* count, int B, int H, int d, int max_out, int dtype, float scale,
+                float* out, float* lse, void* ws, hipStream_t s);
+int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_t* count, int B, int H,
+                  int d, int n_cap, int max_out, int dtype, void* Kc, void* Vc, hipStream_t s);
+int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n,
+                 int n_cap, int max_out, uint32_t cmax, int32_t* victim, hipStream_t s);
+int launch_build_partial(const void* K, const int32_t* chan, void* Kp, int B, int H, int d, int r,
+                         int n_cap, int row0, int row1, int dtype, hipStream_t s);
+int launch_append(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan,
+                  const void* k_new, const void* v_new, const int32_t* victim, int B, int H, int d,
+                  int r, int n_cap, int n, int dtype, int32_t* slot_out, hipStream_t s);
+
+}  // namespace ig

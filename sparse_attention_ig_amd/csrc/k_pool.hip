@@ -1,0 +1,220 @@
+// KV pool kernels (InfiniGen, arXiv 2406.19707, paper-graph-ui summary,
+// section 3.4: "KV Cache Pool Management Under Memory Pressure" for the access
+// counters and the victim, "Decoding Stage" step 5 for fetching the selected
+// rows, "Prefill Stage" step 3 and "Partial Key Cache Updates During Decoding"
+// for building and extending the partial key cache).
+//
+// Counters: one uint32 per pool slot and sequence.  k_touch_inc adds 1 per
+// (head, selected slot) with integer atomics, so the result does not depend on
+// the order of the additions.  k_touch_finish (one workgroup per sequence)
+// re-reads the selected slots to see whether any reached cmax (with counters
+// below cmax on entry only a selected slot can), then clamps and halves the
+// whole pool of that sequence, and picks the victim as the lowest index among
+// the minima.  Re-reading the selection instead of keeping a flag means the
+// call needs no zeroed state.
+//
+// Gather: 16-byte copies of whole rows; the source may be pinned host memory
+// mapped into the device address space, in which case the reads travel over
+// the host link (zero-copy) and the writes land in HBM.
+#include "ig_device.h"
+#include "ig_internal.h"
+
+namespace ig {
+
+constexpr int kTouchThreads = 256;
+constexpr int kFinishThreads = 1024;
+constexpr int kGatherThreads = 256;
+
+__global__ __launch_bounds__(kTouchThreads) void k_touch_inc(uint32_t* __restrict__ C, const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ count, int H, int n, int n_cap,
+                                                            int max_out) {
+    const int bh = blockIdx.y, b = bh / H;
+    const int c = min(count[bh], max_out);
+    const int i = blockIdx.x * kTouchThreads + threadIdx.x;
+    if (i < c) {
+        const int j = idx[static_cast<size_t>(bh) * max_out + i];
+        if (j >= 0 && j < n) atomicAdd(&C[static_cast<size_t>(b) * n_cap + j], 1u);
+    }
+}
+
+__global__ __launch_bounds__(kFinishThreads) void k_touch_finish(uint32_t* __restrict__ C,
+                                                                const int32_t* __restrict__ idx,
+                                                                const int32_t* __restrict__ count, int H, int n,
+                                                                int n_cap, int max_out, uint32_t cmax,
+                                                                int32_t* __restrict__ victim) {
+    __shared__ uint32_t s_val[kFinishThreads / kWave];
+    __shared__ int s_idx[kFinishThreads / kWave];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    uint32_t* row = C + static_cast<size_t>(b) * n_cap;
+
+    int sat = 0;
+    for (int h = 0; h < H; ++h) {
+        const int bh = b * H + h;
+        const int c = min(count[bh], max_out);
+        for (int i = tid; i < c; i += kFinishThreads) {
+            const int j = idx[static_cast<size_t>(bh) * max_out + i];
+            if (j >= 0 && j < n && row[j] >= cmax) sat = 1;
+        }
+    }
+    sat = __syncthreads_or(sat);
+    if (sat) {
+        for (int j = tid; j < n; j += kFinishThreads) {
+            const uint32_t v = row[j];
+            row[j] = (v < cmax ? v : cmax) >> 1;
+        }
+    }
+    if (!victim) return;
+    // argmin over j < n, lowest index on ties (each thread reads only slots it wrote)
+    uint32_t best = 0xFFFFFFFFu;
+    int bi = n;
+    for (int j = tid; j < n; j += kFinishThreads) {
+        const uint32_t v = row[j];
+        if (v < best) {
+            best = v;
+            bi = j;
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t ov = __shfl_xor(best, m, kWave);
+        const int oi = __shfl_xor(bi, m, kWave);
+        if (ov < best || (ov == best && oi < bi)) {
+            best = ov;
+            bi = oi;
+        }
+    }
+    const int lane = tid % kWave, wave = tid / kWave;
+    if (lane == 0) {
+        s_val[wave] = best;
+        s_idx[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < kFinishThreads / kWave; ++w)
+            if (s_val[w] < best || (s_val[w] == best && s_idx[w] < bi)) {
+                best = s_val[w];
+                bi = s_idx[w];
+            }
+        // s_val[0], s_idx[0] hold wave 0's result, already in best / bi
+        victim[b] = bi;
+    }
+}
+
+int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n, int n_cap,
+                 int max_out, uint32_t cmax, int32_t* victim, hipStream_t s) {
+    const dim3 g1((max_out + kTouchThreads - 1) / kTouchThreads, B * H);
+    hipLaunchKernelGGL(k_touch_inc, g1, dim3(kTouchThreads), 0, s, counters, idx, count, H, n, n_cap, max_out);
+    int e = static_cast<int>(hipGetLastError());
+    if (e) return e;
+    hipLaunchKernelGGL(k_touch_finish, dim3(B), dim3(kFinishThreads), 0, s, counters, idx, count, H, n, n_cap,
+                       max_out, cmax, victim);
+    return static_cast<int>(hipGetLastError());
+}
+
+// rows of RB bytes (RB % 16 == 0), LPR = RB / 16 lanes per row
+__global__ __launch_bounds__(kGatherThreads) void k_gather(const char* __restrict__ K, const char* __restrict__ V,
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ count, int row_bytes,
+                                                          int n_cap, int max_out, int rows_per_block,
+                                                          char* __restrict__ Kc, char* __restrict__ Vc) {
+    const int bh = blockIdx.y;
+    const int c = min(count[bh], max_out);
+    const int lpr = row_bytes / 16;
+    const int rows_per_step = kGatherThreads / lpr;
+    const int li = threadIdx.x % lpr, ri = threadIdx.x / lpr;
+    if (ri >= rows_per_step) return;
+    const int i0 = blockIdx.x * rows_per_block;
+    const int i1 = min(c, i0 + rows_per_block);
+    const size_t src_head = static_cast<size_t>(bh) * n_cap * row_bytes;
+    const size_t dst_head = static_cast<size_t>(bh) * max_out * row_bytes;
+    for (int i = i0 + ri; i < i1; i += rows_per_step) {
+        int j = idx[static_cast<size_t>(bh) * max_out + i];
+        j = min(max(j, 0), n_cap - 1);
+        const size_t so = src_head + static_cast<size_t>(j) * row_bytes + li * 16;
+        const size_t dof = dst_head + static_cast<size_t>(i) * row_bytes + li * 16;
+        const uint4 kv = load_raw16(K + so);
+        const uint4 vv = load_raw16(V + so);
+        store_raw16(Kc + dof, kv);
+        store_raw16(Vc + dof, vv);
+    }
+}
+
+int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_t* count, int B, int H, int d,
+                  int n_cap, int max_out, int dtype, void* Kc, void* Vc, hipStream_t s) {
+    const int row_bytes = d * (dtype == IG_BF16 ? 2 : 4);
+    const int rows_per_block = 64;
+    const dim3 grid((max_out + rows_per_block - 1) / rows_per_block, B * H);
+    hipLaunchKernelGGL(k_gather, grid, dim3(kGatherThreads), 0, s, static_cast<const char*>(K),
+                       static_cast<const char*>(V), idx, count, row_bytes, n_cap, max_out, rows_per_block,
+                       static_cast<char*>(Kc), static_cast<char*>(Vc));
+    return static_cast<int>(hipGetLastError());
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_build_partial(const T* __restrict__ K, const int32_t* __restrict__ chan,
+                                                      T* __restrict__ Kp, int H, int d, int r, int n_cap, int row0,
+                                                      int row1) {
+    const int bh = blockIdx.y, h = bh % H;
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * 256 * 4;
+    const int64_t total = static_cast<int64_t>(row1 - row0) * r;
+    for (int u = 0; u < 4; ++u) {
+        const int64_t e = e0 + u * 256 + threadIdx.x;
+        if (e >= total) return;
+        const int j = row0 + static_cast<int>(e / r), c = static_cast<int>(e % r);
+        const int ch = min(max(chan[h * r + c], 0), d - 1);
+        Kp[(static_cast<size_t>(bh) * n_cap + j) * r + c] = K[(static_cast<size_t>(bh) * n_cap + j) * d + ch];
+    }
+}
+
+int launch_build_partial(const void* K, const int32_t* chan, void* Kp, int B, int H, int d, int r, int n_cap,
+                         int row0, int row1, int dtype, hipStream_t s) {
+    const int64_t total = static_cast<int64_t>(row1 - row0) * r;
+    const dim3 grid(static_cast<unsigned>((total + 1023) / 1024), B * H);
+    if (dtype == IG_BF16)
+        hipLaunchKernelGGL((k_build_partial<uint16_t>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(K), chan,
+                           static_cast<uint16_t*>(Kp), H, d, r, n_cap, row0, row1);
+    else
+        hipLaunchKernelGGL((k_build_partial<float>), grid, dim3(256), 0, s, static_cast<const float*>(K), chan,
+                           static_cast<float*>(Kp), H, d, r, n_cap, row0, row1);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_append(T* __restrict__ K, T* __restrict__ V, T* __restrict__ Kp,
+                                               uint32_t* __restrict__ C, const int32_t* __restrict__ chan,
+                                               const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                               const int32_t* __restrict__ victim, int H, int d, int r, int n_cap,
+                                               int n, int32_t* __restrict__ slot_out) {
+    const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+    int slot = n < n_cap ? n : victim[b];
+    slot = min(max(slot, 0), n_cap - 1);
+    const size_t row = (static_cast<size_t>(bh) * n_cap + slot);
+    for (int t = threadIdx.x; t < d; t += 256) {
+        K[row * d + t] = k_new[static_cast<size_t>(bh) * d + t];
+        V[row * d + t] = v_new[static_cast<size_t>(bh) * d + t];
+    }
+    for (int c = threadIdx.x; c < r; c += 256)
+        Kp[row * r + c] = k_new[static_cast<size_t>(bh) * d + min(max(chan[h * r + c], 0), d - 1)];
+    if (h == 0 && threadIdx.x == 0) {
+        if (C) C[static_cast<size_t>(b) * n_cap + slot] = 0u;
+        if (slot_out) slot_out[b] = slot;
+    }
+}
+
+int launch_append(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan, const void* k_new,
+                  const void* v_new, const int32_t* victim, int B, int H, int d, int r, int n_cap, int n, int dtype,
+                  int32_t* slot_out, hipStream_t s) {
+    if (dtype == IG_BF16)
+        hipLaunchKernelGGL((k_append<uint16_t>), dim3(B * H), dim3(256), 0, s, static_cast<uint16_t*>(K),
+                           static_cast<uint16_t*>(V), static_cast<uint16_t*>(Kp), counters, chan,
+                           static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), victim, H, d, r,
+                           n_cap, n, slot_out);
+    else
+        hipLaunchKernelGGL((k_append<float>), dim3(B * H), dim3(256), 0, s, static_cast<float*>(K),
+                           static_cast<float*>(V), static_cast<float*>(Kp), counters, chan,
+                           static_cast<const float*>(k_new), static_cast<const float*>(v_new), victim, H, d, r, n_cap,
+                           n, slot_out);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace ig

@@ -29,8 +29,10 @@ numpy's SeedSequence, so any (b, h) slice can be re-drawn alone.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -116,6 +118,14 @@ def llama2_7b_long(n: int = 32768, B: int = 1, frac: float = 0.01) -> Spec:
     return Spec("llama2-7b-long", B=B, H=32, d=128, n=n, r=32, dtype="bf16", wstd=1.0 / 64,
                 heavy=int(round(0.01 * n)), gamma=3.0, frame="skewed", skew="gauss_block",
                 seed=1005, alpha=5.0, topk=int(math.ceil(frac * n)))
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _rng(spec: Spec, layer: int, purpose: int, *keys: int) -> np.random.Generator:
@@ -266,12 +276,17 @@ def draw_cache(spec: Spec, layer: int, q_skewed: np.ndarray):
     Kb = np.zeros((B, H, cap, d), dtype=enc)
     Vb = np.zeros((B, H, cap, d), dtype=enc)
     heavy = np.zeros((B, H, max(spec.heavy, 0)), dtype=np.int64)
-    for b in range(B):
-        for h in range(H):
-            K, V, pos = draw_cache_slice(spec, layer, b, h, q_skewed[b, h * d:(h + 1) * d])
-            Kb[b, h, :n] = encode(K.astype(np.float32), spec.dtype)
-            Vb[b, h, :n] = encode(V, spec.dtype)
-            heavy[b, h, :len(pos)] = pos
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        K, V, pos = draw_cache_slice(spec, layer, b, h, q_skewed[b, h * d:(h + 1) * d])
+        Kb[b, h, :n] = encode(K.astype(np.float32), spec.dtype)
+        Vb[b, h, :n] = encode(V, spec.dtype)
+        heavy[b, h, :len(pos)] = pos
+
+    # numpy's generators release the GIL while filling, so slices draw in parallel
+    with cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(B * H)))
     return Kb, Vb, heavy
 
 

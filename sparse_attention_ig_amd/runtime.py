@@ -1,0 +1,158 @@
+"""Layer preparation and the decode layer-step on the GPU, through libig.so only.
+
+``prepare_layer`` runs the library's host setup on one layer's raw draws:
+skew rotation (ig_skew_weights), rotation of the raw query / keys
+(ig_skew_apply), storage rounding (ig_store) and the channel pick with the
+partial query weight (ig_partial_weight_index).  ``DeviceLayer`` holds a
+layer's decode-path tensors in HBM and builds the partial key cache with
+ig_build_partial_cache.  ``DeviceLayer.step`` is one layer-step of the hot
+path: ig_rehearse -> ig_select -> ig_sparse_decode_attn -> ig_pool_touch, all
+enqueued on one stream with no host synchronisation.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import gen
+
+
+@dataclass
+class HostLayer:
+    spec: gen.Spec
+    x: np.ndarray          # [B][D] stored
+    Wq_part: np.ndarray    # [D][H*r] stored
+    chan: np.ndarray       # [H][r] int32
+    q: np.ndarray          # [B][H][d] stored (skewed full query)
+    K: np.ndarray          # [B][H][n_cap][d] stored (skewed keys)
+    V: np.ndarray          # [B][H][n_cap][d] stored
+    extra: Dict = field(default_factory=dict)
+
+
+def rows_layout(K: np.ndarray) -> np.ndarray:
+    """[B][H][n][d] -> [B*n][H*d] (head blocks side by side), for per-head rotation."""
+    B, H, n, d = K.shape
+    return np.ascontiguousarray(K.transpose(0, 2, 1, 3).reshape(B * n, H * d))
+
+
+def heads_layout(M: np.ndarray, B: int, H: int, n: int, d: int) -> np.ndarray:
+    return np.ascontiguousarray(M.reshape(B, n, H, d).transpose(0, 2, 1, 3))
+
+
+def prepare_layer(spec: gen.Spec, layer: int = 0, lay: Optional[gen.Layer] = None) -> HostLayer:
+    """Library route from the raw draws of one layer to its stored decode-path inputs."""
+    from . import _lib as L
+    B, H, d, r = spec.B, spec.H, spec.d, spec.r
+    lay = lay or gen.draw_layer(spec, layer, with_wk=False)
+    sk = L.ig_skew_weights(lay.skew_src, Wq=lay.Wq)
+    Wq_s = L.ig_store(sk["Wq_s"], spec.dtype)
+    q = L.ig_store(L.ig_skew_apply(sk["A"], lay.q_raw), spec.dtype)
+    if spec.frame == "raw":
+        Kr = L.ig_skew_apply(sk["A"], rows_layout(lay.K_raw))
+        K = L.ig_store(heads_layout(Kr, B, H, spec.cap, d), spec.dtype)
+        V, heavy = lay.V, lay.heavy_pos
+    else:
+        K, V, heavy = gen.draw_cache(spec, layer, gen.values(q, spec.dtype))
+    chan, Wq_part = L.ig_partial_weight_index(Wq_s, K, r, spec.n, spec.dtype)
+    return HostLayer(spec, lay.x, Wq_part, chan, q.reshape(B, H, d), K, V,
+                     extra={"A": sk["A"], "sigma": sk["sigma"], "heavy": heavy, "Wq_s": Wq_s})
+
+
+def to_device(a: np.ndarray):
+    """numpy -> cuda tensor; uint16 arrays are bf16 bits, uint32 counters ride as int32."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class DeviceLayer:
+    """One layer's decode-path inputs resident in HBM, plus preallocated outputs and workspaces."""
+
+    def __init__(self, host: HostLayer, counters: Optional[np.ndarray] = None, max_out: Optional[int] = None):
+        import torch
+        from . import _lib as L
+        s = host.spec
+        self.spec = s
+        self.x = to_device(host.x)
+        self.Wq_part = to_device(host.Wq_part)
+        self.chan = to_device(host.chan)
+        self.q = to_device(host.q)
+        self.K = to_device(host.K)
+        self.V = to_device(host.V)
+        self.Kp = torch.zeros((s.B, s.H, s.cap, s.r), dtype=self.K.dtype, device="cuda")
+        L.ig_build_partial_cache(self.K, self.chan, self.Kp, 0, s.n)
+        self.counters = to_device(counters if counters is not None else np.zeros((s.B, s.cap), dtype=np.uint32))
+        self.max_out = max_out or s.cap
+        dv = "cuda"
+        self.q_part = torch.empty((s.B, s.H, s.r), dtype=torch.float32, device=dv)
+        self.scores = torch.empty((s.B, s.H, s.cap), dtype=torch.float32, device=dv)
+        self.idx = torch.empty((s.B, s.H, self.max_out), dtype=torch.int32, device=dv)
+        self.count = torch.empty((s.B, s.H), dtype=torch.int32, device=dv)
+        self.out = torch.empty((s.B, s.H, s.d), dtype=torch.float32, device=dv)
+        self.lse = torch.empty((s.B, s.H), dtype=torch.float32, device=dv)
+        self.victim = torch.empty((s.B,), dtype=torch.int32, device=dv)
+        nb = max(L.ig_workspace_size(L.IG_OP_REHEARSE, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out),
+                 L.ig_workspace_size(L.IG_OP_SELECT, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out),
+                 L.ig_workspace_size(L.IG_OP_ATTN, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out), 16)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dv)
+
+    def clone(self) -> "DeviceLayer":
+        """A copy in distinct HBM buffers (device-to-device copies of every tensor)."""
+        import copy
+        other = copy.copy(self)
+        for name, v in vars(self).items():
+            if hasattr(v, "is_cuda") and v.is_cuda:
+                setattr(other, name, v.clone())
+        return other
+
+    def nbytes(self) -> int:
+        return sum(v.numel() * v.element_size() for v in vars(self).values() if hasattr(v, "is_cuda"))
+
+    def step(self, *, mode: str, alpha: float = math.inf, k: int = 0, max_sel: int = 0,
+             max_out: Optional[int] = None, cmax: int = 65535, want_victim: bool = False,
+             n: Optional[int] = None, stream=None, events=None) -> Dict:
+        """One layer-step.  ``events``: optional dict name -> (start, end) torch events recorded
+        around each call on ``stream``."""
+        from . import _lib as L
+        s = self.spec
+        n = s.n if n is None else n
+        max_out = self.max_out if max_out is None else max_out
+        idx = self.idx if max_out == self.max_out else self.idx.view(-1)[:s.B * s.H * max_out].view(s.B, s.H, max_out)
+        ev = events or {}
+
+        def mark(name, i):
+            if name in ev:
+                ev[name][i].record(stream)
+
+        mark("rehearse", 0)
+        L.ig_rehearse(self.x, self.Wq_part, self.Kp, n, s.softmax_scale, q_part=self.q_part, scores=self.scores,
+                      ld=s.cap, ws=self.ws, stream=stream)
+        mark("rehearse", 1)
+        mark("select", 0)
+        L.ig_select(self.scores, mode, max_out, n=n, alpha=alpha, k=k, max_sel=max_sel, idx=idx, count=self.count,
+                    ws=self.ws, stream=stream)
+        mark("select", 1)
+        mark("attn", 0)
+        L.ig_sparse_decode_attn(self.q, self.K, self.V, idx, self.count, s.softmax_scale, out=self.out, lse=self.lse,
+                                ws=self.ws, stream=stream)
+        mark("attn", 1)
+        mark("touch", 0)
+        L.ig_pool_touch(self.counters, idx, self.count, n, cmax, victim=self.victim if want_victim else None,
+                        stream=stream)
+        mark("touch", 1)
+        return dict(q_part=self.q_part, scores=self.scores, idx=idx, count=self.count, out=self.out, lse=self.lse,
+                    counters=self.counters, victim=self.victim if want_victim else None)

@@ -1,0 +1,148 @@
+"""Two independent routes from the same raw draws to the decode-path inputs.
+
+``lib_inputs`` runs the library's own host setup (libig.so: Jacobi skew,
+rotation, storage rounding, channel pick) and ``oracle_inputs`` runs the
+oracle's (numpy SVD, ...).  Only ``gen`` is shared.  The two routes agree to
+float64 rounding, so the stored bits they produce coincide; ``compare_inputs``
+checks that as a setup-parity result.  Comparison helpers implement the parity
+rules: scores within 1e-3 (row-normwise), index sets and counters exact except
+rows whose oracle score lies within 1e-4 of the cut, attention within 1e-2
+(bf16 inputs) or 1e-5 (float32 inputs).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+from sparse_attention_ig_amd import gen
+from sparse_attention_ig_amd.runtime import HostLayer, heads_layout, prepare_layer, rows_layout
+
+SCORE_RTOL = 1e-3
+BAND = 1e-4
+ATTN_TOL = {"bf16": 1e-2, "f32": 1e-5}
+
+
+Inputs = HostLayer
+_rows_layout = rows_layout
+_heads_layout = heads_layout
+
+
+def lib_inputs(spec: gen.Spec, layer: int = 0, lay: Optional[gen.Layer] = None) -> Inputs:
+    return prepare_layer(spec, layer, lay)
+
+
+def oracle_inputs(spec: gen.Spec, layer: int = 0, lay: Optional[gen.Layer] = None) -> Inputs:
+    from oracle import oracle as O
+    B, H, d, r = spec.B, spec.H, spec.d, spec.r
+    lay = lay or gen.draw_layer(spec, layer, with_wk=False)
+    A, Wq_s64, _, _, _ = O.skew_weights(lay.Wq, None, lay.skew_src)
+    Wq_s = O.store(Wq_s64, spec.dtype)
+    q = O.store(O.skew_apply(A, lay.q_raw), spec.dtype)
+    if spec.frame == "raw":
+        K = O.store(_heads_layout(O.skew_apply(A, _rows_layout(lay.K_raw)), B, H, spec.cap, d), spec.dtype)
+        V, heavy = lay.V, lay.heavy_pos
+    else:
+        K, V, heavy = gen.draw_cache(spec, layer, O.decode(q, spec.dtype))
+    chan = O.partial_weight_index(Wq_s, K, H, d, r, spec.n, dtype=spec.dtype)
+    Wq_part = O.pack_partial_weight(Wq_s, chan, d)
+    return Inputs(spec, lay.x, Wq_part, chan, q.reshape(B, H, d), K, V,
+                  extra={"A": A, "heavy": heavy, "Kp": O.partial_key_cache(K, chan)})
+
+
+def ulp_mismatch(a: np.ndarray, b: np.ndarray) -> int:
+    """Number of stored elements whose bits differ (float32 / bf16 arrays)."""
+    return int(np.count_nonzero(a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+                                != b.view(np.uint32 if b.dtype == np.float32 else np.uint16)))
+
+
+def compare_inputs(a: Inputs, b: Inputs) -> Dict[str, int]:
+    """Setup parity: bits of every derived input, and the channel sets."""
+    return {
+        "chan": int(np.count_nonzero(a.chan != b.chan)),
+        "Wq_part": ulp_mismatch(a.Wq_part, b.Wq_part),
+        "q": ulp_mismatch(a.q, b.q),
+        "K": ulp_mismatch(a.K, b.K),
+        "V": ulp_mismatch(a.V, b.V),
+        "x": ulp_mismatch(a.x, b.x),
+    }
+
+
+# ---------------------------------------------------------------- oracle side of a step
+def oracle_step(inp: Inputs, *, mode: str, alpha: float = math.inf, k: int = 0, max_sel: int = 0,
+                max_out: int = 0, cmax: int = 65535, counters: Optional[np.ndarray] = None,
+                want_victim: bool = False, heads=None):
+    """The oracle's decode layer-step on its own inputs.  ``heads``: optional list of (b, h) to
+    evaluate (sampled parity at large sizes); counters are then not computed."""
+    from oracle import oracle as O
+    s = inp.spec
+    dt = s.dtype
+    x = O.decode(inp.x, dt)
+    Wp = O.decode(inp.Wq_part, dt)
+    Kp = inp.extra.get("Kp")
+    if Kp is None:
+        Kp = O.partial_key_cache(inp.K, inp.chan)
+    if heads is None:
+        qp, sc = O.rehearse(x, Wp, O.decode(Kp, dt), s.n, s.H, s.r, s.softmax_scale)
+        idx, cnt = _oracle_select(sc, mode, alpha, k, max_sel, max_out)
+        o, lse = O.sparse_decode_attn(O.decode(inp.q, dt), O.decode(inp.K, dt), O.decode(inp.V, dt), idx, cnt,
+                                      s.softmax_scale)
+        res = dict(q_part=qp, scores=sc, idx=idx, count=cnt, out=o, lse=lse)
+        if counters is not None:
+            C2, v = O.pool_touch(counters, idx, cnt, s.n, cmax, want_victim)
+            res.update(counters=C2, victim=v)
+        return res
+    out = {}
+    for (b, h) in heads:
+        sub_x = x[b:b + 1]
+        qp, sc = O.rehearse(sub_x, Wp[:, h * s.r:(h + 1) * s.r], O.decode(Kp[b:b + 1, h:h + 1], dt), s.n, 1, s.r,
+                            s.softmax_scale)
+        idx, cnt = _oracle_select(sc, mode, alpha, k, max_sel, max_out)
+        c = int(cnt[0, 0])
+        rows = idx[0, 0, :c].astype(np.int64)
+        o, lse = O.attention_rows(O.decode(inp.q[b, h], dt), O.decode(inp.K[b, h, rows], dt),
+                                  O.decode(inp.V[b, h, rows], dt), s.softmax_scale)
+        out[(b, h)] = dict(q_part=qp[0, 0], scores=sc[0, 0], idx=rows, out=o, lse=lse)
+    return out
+
+
+def _oracle_select(sc, mode, alpha, k, max_sel, max_out):
+    from oracle import oracle as O
+    if mode == "headavg":
+        return O.select_head_average(sc, alpha, max_sel, max_out)
+    return O.select(sc, mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out)
+
+
+# ---------------------------------------------------------------- comparisons
+def score_error(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of max_j |gpu - ref| / max_j |ref| (row-normwise)."""
+    g = gpu.reshape(-1, gpu.shape[-1]).astype(np.float64)
+    r = ref.reshape(-1, ref.shape[-1])
+    den = np.maximum(np.abs(r).max(axis=1), 1e-30)
+    return float((np.abs(g - r).max(axis=1) / den).max())
+
+
+def cut_of(ref_scores: np.ndarray, ref_sel: np.ndarray, mode: str, alpha: float) -> float:
+    """The value the selection was cut at: max - alpha, or the smallest kept score when the
+    set was cut by count (top-k, head average, or a threshold set hitting its cap)."""
+    if mode == "threshold":
+        cut = ref_scores.max() - alpha
+        kept_all = np.count_nonzero(ref_scores >= cut)
+        if kept_all == len(ref_sel):
+            return cut
+    return float(ref_scores[ref_sel].min()) if len(ref_sel) else math.inf
+
+
+def band_rows(ref_scores: np.ndarray, cut: float) -> np.ndarray:
+    return np.flatnonzero(np.abs(ref_scores - cut) <= BAND)
+
+
+def compare_sets(gpu_sel: np.ndarray, ref_sel: np.ndarray, ref_scores: np.ndarray, mode: str, alpha: float):
+    """Returns (ok, exact, band) -- ok: sets equal outside the band; exact: equal outright."""
+    g = set(int(v) for v in gpu_sel)
+    r = set(int(v) for v in ref_sel)
+    cut = cut_of(ref_scores, np.asarray(sorted(r), dtype=np.int64), mode, alpha)
+    band = set(int(v) for v in band_rows(ref_scores, cut))
+    ok = (g - band) == (r - band)
+    return ok, g == r, band
