@@ -83,45 +83,59 @@ def main() -> int:
     layers = [base] + [base.clone() for _ in range(args.layers - 1)]
     torch.cuda.synchronize()
     footprint = sum(l.nbytes() for l in layers)
-    stream = torch.cuda.current_stream()
+    PARTS = DeviceLayer.PARTS
 
-    def one_step(events=None, li_events=None):
-        for i, l in enumerate(layers):
-            l.step(**step_kw, stream=stream, events=(li_events[i] if li_events else None))
+    def run(parts=PARTS):
+        # stream=None: torch's current stream, which is the capture stream inside a graph capture
+        for l in layers:
+            l.step(**step_kw, parts=parts)
 
+    def capture(parts):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run(parts)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(parts)
+        return g
+
+    def timed_ms(fn, reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    # eager launches (every call goes through Python and ctypes)
     for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
+        run()
+    ms_eager = timed_ms(run, args.steps) / args.steps
 
-    # timed region: exactly --steps steps, synchronised on both sides
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # the whole step captured once as a HIP graph; the timed region is exactly --steps replays
+    graph = capture(PARTS)
+    for _ in range(args.warmup):
+        graph.replay()
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        one_step()
-    t1.record(stream)
-    torch.cuda.synchronize()
+    ms_total = timed_ms(graph.replay, args.steps)
     wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
     tok_s_layer = spec.B * args.layers * args.steps / (ms_total / 1e3)
 
-    # per-call durations: HIP events around every call of every layer, over the same number of steps
-    names = ("rehearse", "select", "attn", "touch")
-    per = {n: 0.0 for n in names}
-    inst_steps = args.steps
-    for _ in range(inst_steps):
-        evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
-               for _ in layers]
-        one_step(li_events=evs)
-        torch.cuda.synchronize()
-        for e in evs:
-            for n in names:
-                per[n] += e[n][0].elapsed_time(e[n][1])
-    calls = inst_steps * len(layers)
-    per_us = {n: 1e3 * per[n] / calls for n in names}
+    # per-call launch durations: each call alone over every layer in its own graph, HIP events
+    # on the stream the kernels run on, averaged over --steps replays
+    per_us = {}
+    for part in PARTS:
+        gp = capture((part,))
+        for _ in range(3):
+            gp.replay()
+        per_us[part] = 1e3 * timed_ms(gp.replay, args.steps) / (args.steps * args.layers)
 
     res = to_host(layers[0].count)
     c_mean = float(res.mean())
@@ -152,6 +166,8 @@ def main() -> int:
         "step_hbm_GBs": round(step_bytes / t_layer_s / 1e9, 1),
         "step_hbm_frac": round(step_bytes / t_layer_s / 1e9 / HBM_PEAK_GBS, 4),
         "per_call_us": {k: round(v, 3) for k, v in per_us.items()},
+        "eager_ms_per_step": round(ms_eager, 4),
+        "eager_tokens_s_layer": round(spec.B * args.layers / (ms_eager / 1e3), 1),
         "roofline": {"kernel": f"ig_{dominant}", "bound": "hbm", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None, "alg_bytes_per_launch": int(dom_bytes)},

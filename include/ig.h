@@ -192,7 +192,9 @@ int ig_sparse_decode_attn(const void* q, const void* K, const void* V, int ld_ro
  * all its slots j < n are halved (floor).  victim[b] (if not NULL) = the
  * lowest index among the minima of C[b][0..n).  counters [B][n_cap] uint32,
  * updated in place; precondition C[b][j] < cmax for j < n.  Indices of one
- * head must be distinct; values outside [0, n) are ignored.  cmax >= 2.
+ * head must be distinct; values outside [0, n) are ignored.  cmax >= 2,
+ * H <= 1024.  One workgroup per sequence, so calls for different sequences
+ * never touch the same counters.
  */
 int ig_pool_touch(uint32_t* counters, const int32_t* idx, const int32_t* count,
                   int B, int H, int n, int n_cap, int max_out, uint32_t cmax,

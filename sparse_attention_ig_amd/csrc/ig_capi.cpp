@@ -165,6 +165,7 @@ int ig_pool_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, 
     IG_REQUIRE(B >= 1 && H >= 1 && n >= 1 && n <= n_cap && max_out >= 1,
                "ig_pool_touch: bad sizes (B=%d H=%d n=%d n_cap=%d max_out=%d)", B, H, n, n_cap, max_out);
     IG_REQUIRE(cmax >= 2, "ig_pool_touch: cmax must be >= 2");
+    IG_REQUIRE(H <= 1024, "ig_pool_touch: at most 1024 heads");
     return hip_status(launch_touch(counters, idx, count, B, H, n, n_cap, max_out, cmax, victim, stream),
                       "ig_pool_touch");
 }

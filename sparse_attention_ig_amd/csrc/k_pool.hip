@@ -4,14 +4,14 @@
 // rows, "Prefill Stage" step 3 and "Partial Key Cache Updates During Decoding"
 // for building and extending the partial key cache).
 //
-// Counters: one uint32 per pool slot and sequence.  k_touch_inc adds 1 per
-// (head, selected slot) with integer atomics, so the result does not depend on
-// the order of the additions.  k_touch_finish (one workgroup per sequence)
-// re-reads the selected slots to see whether any reached cmax (with counters
-// below cmax on entry only a selected slot can), then clamps and halves the
-// whole pool of that sequence, and picks the victim as the lowest index among
-// the minima.  Re-reading the selection instead of keeping a flag means the
-// call needs no zeroed state.
+// Counters: one uint32 per pool slot and sequence.  k_touch runs one
+// workgroup per sequence: it adds 1 per (head, selected slot) with integer
+// atomics, so the result does not depend on the order of the additions; the
+// atomics' return values tell whether any slot reached cmax (with counters
+// below cmax on entry only a selected slot can), in which case the whole pool
+// of that sequence is clamped and halved; the victim is the lowest index among
+// the minima.  Keeping the whole sequence in one workgroup means the call
+// needs no zeroed state and no second launch.
 //
 // Gather: 16-byte copies of whole rows; the source may be pinned host memory
 // mapped into the device address space, in which case the reads travel over
@@ -21,54 +21,54 @@
 
 namespace ig {
 
-constexpr int kTouchThreads = 256;
-constexpr int kFinishThreads = 1024;
+constexpr int kTouchThreads = 1024;
+constexpr int kTouchMaxHeads = 1024;
 constexpr int kGatherThreads = 256;
 
-__global__ __launch_bounds__(kTouchThreads) void k_touch_inc(uint32_t* __restrict__ C, const int32_t* __restrict__ idx,
-                                                            const int32_t* __restrict__ count, int H, int n, int n_cap,
-                                                            int max_out) {
-    const int bh = blockIdx.y, b = bh / H;
-    const int c = min(count[bh], max_out);
-    const int i = blockIdx.x * kTouchThreads + threadIdx.x;
-    if (i < c) {
-        const int j = idx[static_cast<size_t>(bh) * max_out + i];
-        if (j >= 0 && j < n) atomicAdd(&C[static_cast<size_t>(b) * n_cap + j], 1u);
-    }
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kFinishThreads) void k_touch_finish(uint32_t* __restrict__ C,
-                                                                const int32_t* __restrict__ idx,
-                                                                const int32_t* __restrict__ count, int H, int n,
-                                                                int n_cap, int max_out, uint32_t cmax,
-                                                                int32_t* __restrict__ victim) {
-    __shared__ uint32_t s_val[kFinishThreads / kWave];
-    __shared__ int s_idx[kFinishThreads / kWave];
+// One workgroup per sequence: every (head, selected slot) of that sequence adds
+// 1 with an integer atomic; an increment that returns cmax - 1 or more means
+// the slot saturated (counters are below cmax on entry), in which case the
+// whole pool of the sequence is clamped to cmax and halved.  Then the victim.
+__global__ __launch_bounds__(kTouchThreads) void k_touch(uint32_t* __restrict__ C, const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ count, int H, int n, int n_cap,
+                                                        int max_out, uint32_t cmax, int32_t* __restrict__ victim) {
+    __shared__ int s_cnt[kTouchMaxHeads];
+    __shared__ uint32_t s_val[kTouchThreads / kWave];
+    __shared__ int s_idx[kTouchThreads / kWave];
     const int b = blockIdx.x, tid = threadIdx.x;
     uint32_t* row = C + static_cast<size_t>(b) * n_cap;
+    for (int h = tid; h < H; h += kTouchThreads) s_cnt[h] = min(max(count[b * H + h], 0), max_out);
+    __syncthreads();
 
     int sat = 0;
-    for (int h = 0; h < H; ++h) {
-        const int bh = b * H + h;
-        const int c = min(count[bh], max_out);
-        for (int i = tid; i < c; i += kFinishThreads) {
-            const int j = idx[static_cast<size_t>(bh) * max_out + i];
-            if (j >= 0 && j < n && row[j] >= cmax) sat = 1;
+    const int total = H * max_out;
+    for (int e = tid; e < total; e += kTouchThreads) {
+        const int h = e / max_out, i = e - h * max_out;
+        if (i < s_cnt[h]) {
+            const int j = idx[(static_cast<size_t>(b) * H + h) * max_out + i];
+            if (j >= 0 && j < n) {
+                const uint32_t old = atomicAdd(&row[j], 1u);
+                if (old + 1u >= cmax) sat = 1;
+            }
         }
     }
     sat = __syncthreads_or(sat);
     if (sat) {
-        for (int j = tid; j < n; j += kFinishThreads) {
-            const uint32_t v = row[j];
+        for (int j = tid; j < n; j += kTouchThreads) {
+            const uint32_t v = coherent_load(&row[j]);
             row[j] = (v < cmax ? v : cmax) >> 1;
         }
     }
     if (!victim) return;
-    // argmin over j < n, lowest index on ties (each thread reads only slots it wrote)
+    // argmin over j < n, lowest index on ties; a thread re-reads only slots it wrote itself
     uint32_t best = 0xFFFFFFFFu;
     int bi = n;
-    for (int j = tid; j < n; j += kFinishThreads) {
-        const uint32_t v = row[j];
+    for (int j = tid; j < n; j += kTouchThreads) {
+        const uint32_t v = coherent_load(&row[j]);
         if (v < best) {
             best = v;
             bi = j;
@@ -90,24 +90,19 @@ __global__ __launch_bounds__(kFinishThreads) void k_touch_finish(uint32_t* __res
     }
     __syncthreads();
     if (tid == 0) {
-        for (int w = 1; w < kFinishThreads / kWave; ++w)
+        for (int w = 1; w < kTouchThreads / kWave; ++w)
             if (s_val[w] < best || (s_val[w] == best && s_idx[w] < bi)) {
                 best = s_val[w];
                 bi = s_idx[w];
             }
-        // s_val[0], s_idx[0] hold wave 0's result, already in best / bi
         victim[b] = bi;
     }
 }
 
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n, int n_cap,
                  int max_out, uint32_t cmax, int32_t* victim, hipStream_t s) {
-    const dim3 g1((max_out + kTouchThreads - 1) / kTouchThreads, B * H);
-    hipLaunchKernelGGL(k_touch_inc, g1, dim3(kTouchThreads), 0, s, counters, idx, count, H, n, n_cap, max_out);
-    int e = static_cast<int>(hipGetLastError());
-    if (e) return e;
-    hipLaunchKernelGGL(k_touch_finish, dim3(B), dim3(kFinishThreads), 0, s, counters, idx, count, H, n, n_cap,
-                       max_out, cmax, victim);
+    hipLaunchKernelGGL(k_touch, dim3(B), dim3(kTouchThreads), 0, s, counters, idx, count, H, n, n_cap, max_out, cmax,
+                       victim);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -122,11 +122,14 @@ class DeviceLayer:
     def nbytes(self) -> int:
         return sum(v.numel() * v.element_size() for v in vars(self).values() if hasattr(v, "is_cuda"))
 
+    PARTS = ("rehearse", "select", "attn", "touch")
+
     def step(self, *, mode: str, alpha: float = math.inf, k: int = 0, max_sel: int = 0,
              max_out: Optional[int] = None, cmax: int = 65535, want_victim: bool = False,
-             n: Optional[int] = None, stream=None, events=None) -> Dict:
-        """One layer-step.  ``events``: optional dict name -> (start, end) torch events recorded
-        around each call on ``stream``."""
+             n: Optional[int] = None, stream=None, events=None, parts=PARTS) -> Dict:
+        """One layer-step (or the listed ``parts`` of it), enqueued on ``stream`` (default: the
+        current stream).  ``events``: optional dict part -> (start, end) torch events recorded
+        around each call."""
         from . import _lib as L
         s = self.spec
         n = s.n if n is None else n
@@ -134,25 +137,24 @@ class DeviceLayer:
         idx = self.idx if max_out == self.max_out else self.idx.view(-1)[:s.B * s.H * max_out].view(s.B, s.H, max_out)
         ev = events or {}
 
-        def mark(name, i):
-            if name in ev:
-                ev[name][i].record(stream)
-
-        mark("rehearse", 0)
-        L.ig_rehearse(self.x, self.Wq_part, self.Kp, n, s.softmax_scale, q_part=self.q_part, scores=self.scores,
-                      ld=s.cap, ws=self.ws, stream=stream)
-        mark("rehearse", 1)
-        mark("select", 0)
-        L.ig_select(self.scores, mode, max_out, n=n, alpha=alpha, k=k, max_sel=max_sel, idx=idx, count=self.count,
-                    ws=self.ws, stream=stream)
-        mark("select", 1)
-        mark("attn", 0)
-        L.ig_sparse_decode_attn(self.q, self.K, self.V, idx, self.count, s.softmax_scale, out=self.out, lse=self.lse,
-                                ws=self.ws, stream=stream)
-        mark("attn", 1)
-        mark("touch", 0)
-        L.ig_pool_touch(self.counters, idx, self.count, n, cmax, victim=self.victim if want_victim else None,
-                        stream=stream)
-        mark("touch", 1)
+        for part in parts:
+            if part in ev:
+                ev[part][0].record(stream)
+            if part == "rehearse":
+                L.ig_rehearse(self.x, self.Wq_part, self.Kp, n, s.softmax_scale, q_part=self.q_part,
+                              scores=self.scores, ld=s.cap, ws=self.ws, stream=stream)
+            elif part == "select":
+                L.ig_select(self.scores, mode, max_out, n=n, alpha=alpha, k=k, max_sel=max_sel, idx=idx,
+                            count=self.count, ws=self.ws, stream=stream)
+            elif part == "attn":
+                L.ig_sparse_decode_attn(self.q, self.K, self.V, idx, self.count, s.softmax_scale, out=self.out,
+                                        lse=self.lse, ws=self.ws, stream=stream)
+            elif part == "touch":
+                L.ig_pool_touch(self.counters, idx, self.count, n, cmax,
+                                victim=self.victim if want_victim else None, stream=stream)
+            else:
+                raise ValueError(part)
+            if part in ev:
+                ev[part][1].record(stream)
         return dict(q_part=self.q_part, scores=self.scores, idx=idx, count=self.count, out=self.out, lse=self.lse,
                     counters=self.counters, victim=self.victim if want_victim else None)

@@ -272,9 +272,15 @@ def test_determinism():
     for _ in range(2):
         layer = DeviceLayer(li)
         runs.append(to_host(layer.step(mode="threshold", alpha=5.0, max_sel=409, max_out=409)))
-    for key in ("q_part", "scores", "idx", "count", "out", "lse", "counters"):
+    assert np.array_equal(runs[0]["count"], runs[1]["count"])
+    for key in ("q_part", "scores", "out", "lse", "counters"):
         a, b = runs[0][key], runs[1][key]
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), key
+    cnt = runs[0]["count"]
+    for b in range(spec.B):
+        for h in range(spec.H):
+            c = cnt[b, h]     # entries past count are unspecified
+            assert np.array_equal(runs[0]["idx"][b, h, :c], runs[1]["idx"][b, h, :c])
 
 
 def test_long_context_full_size_sampled():
@@ -298,3 +304,38 @@ def test_long_context_full_size_sampled():
             assert np.abs(g["out"][b, h] - r["out"]).max() <= harness.ATTN_TOL["bf16"]
     # counters: each head adds exactly k increments
     assert int(g["counters"].sum()) == spec.H * spec.topk
+
+
+def test_graph_replay_matches_eager():
+    """The layer-step captured once in a HIP graph and replayed (with eager work and
+    synchronisations between replays) gives the eager results on every replay."""
+    import torch
+    spec = gen.opt_6_7b()
+    say("[graph replay]")
+    li = harness.lib_inputs(spec)
+    layer = DeviceLayer(li, max_out=128)
+    kw = dict(mode="topk", k=128, max_out=128)
+    C0 = layer.counters.clone()
+    eager = to_host(layer.step(**kw))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.counters.copy_(C0)
+        layer.step(**kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step(**kw)
+    for rep in range(3):
+        layer.counters.copy_(C0)
+        layer.scores.fill_(-1.0)
+        layer.out.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host(dict(scores=layer.scores, count=layer.count, idx=layer.idx, out=layer.out, lse=layer.lse,
+                           counters=layer.counters))
+        for key in ("scores", "count", "out", "lse", "counters"):
+            assert np.array_equal(got[key].view(np.uint8), eager[key].view(np.uint8)), (rep, key)
+        assert np.array_equal(got["idx"], eager["idx"]), rep
