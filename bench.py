@@ -32,15 +32,20 @@ METRIC = "decode step tokens/s per layer (rehearse+select+sparse attn) + % HBM p
 
 
 def alg_bytes(spec, c: float) -> dict:
-    """Algorithmic bytes of one layer-step by call (c = mean selected rows per head)."""
+    """Algorithmic bytes of one layer-step by call (c = mean selected rows per head).  Per layer-step:
+    Wq_part D*H*r*s + x B*D*s + Kp B*H*n*r*s + selected K and V B*H*c*2*d*s + q B*H*d*s + o B*H*d*4
+    + idx and counters 2*B*H*c*4; the scores' float32 round trip of the six-call path is an
+    implementation cost, not algorithmic."""
     s = 2 if spec.dtype == "bf16" else 4
     B, H, D, d, r, n = spec.B, spec.H, spec.D, spec.d, spec.r, spec.n
-    return {
+    parts = {
         "rehearse": D * H * r * s + B * D * s + B * H * n * r * s,
-        "select": 0.0,                                   # scores are an implementation round trip
-        "attn": B * H * c * 2 * d * s + B * H * d * s + B * H * d * 4 + B * H * c * 4,
-        "touch": B * H * c * 4,
+        "select": B * H * c * 4,                            # idx written
+        "touch": B * H * c * 4,                             # counters
+        "attn": B * H * c * 2 * d * s + B * H * d * s + B * H * d * 4,
     }
+    parts["speculate"] = parts["rehearse"] + parts["select"] + parts["touch"]
+    return parts
 
 
 def main() -> int:
@@ -50,6 +55,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=32, help="distinct layer buffers per step")
     ap.add_argument("--mode", choices=["topk", "threshold"], default="topk")
+    ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
+                    help="fused: ig_speculate + ig_sparse_decode_attn; unfused: the six-call path")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -80,10 +87,11 @@ def main() -> int:
     print(f"[bench] preparing {wl} x {args.layers} layers", file=sys.stderr, flush=True)
     host = prepare_layer(spec)
     base = DeviceLayer(host, max_out=step_kw["max_out"])
+    base.keep_scores = args.path == "unfused"   # the fused path keeps the scores on chip
     layers = [base] + [base.clone() for _ in range(args.layers - 1)]
     torch.cuda.synchronize()
     footprint = sum(l.nbytes() for l in layers)
-    PARTS = DeviceLayer.PARTS
+    PARTS = DeviceLayer.FUSED if args.path == "fused" else DeviceLayer.PARTS
 
     def run(parts=PARTS):
         # stream=None: torch's current stream, which is the capture stream inside a graph capture
@@ -140,7 +148,7 @@ def main() -> int:
     res = to_host(layers[0].count)
     c_mean = float(res.mean())
     ab = alg_bytes(spec, c_mean)
-    step_bytes = sum(ab.values())
+    step_bytes = sum(ab[p] for p in PARTS)
     t_layer_s = ms_step / 1e3 / args.layers
     dominant = max(per_us, key=per_us.get)
     dom_bytes = ab[dominant]
@@ -160,7 +168,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded OPT-6.7B-shaped draws, no weights or datasets)",
         "config": {"workload": wl, "layers_per_step": args.layers, "footprint_GB": round(footprint / 1e9, 2),
-                   "mean_selected_per_head": round(c_mean, 1)},
+                   "mean_selected_per_head": round(c_mean, 1), "path": args.path,
+                   "calls_per_layer": list(PARTS)},
         "t_layer_us": round(t_layer_s * 1e6, 3),
         "step_alg_bytes_per_layer": int(step_bytes),
         "step_hbm_GBs": round(step_bytes / t_layer_s / 1e9, 1),

@@ -46,7 +46,7 @@ extern "C" {
 enum { IG_OK = 0, IG_EINVAL = 1, IG_EHIP = 2, IG_EUNSUPPORTED = 3 };
 enum { IG_F32 = 0, IG_BF16 = 1 };
 enum { IG_SEL_THRESHOLD = 0, IG_SEL_TOPK = 1, IG_SEL_HEADAVG = 2 };
-enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2 };
+enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3 };
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* ig_last_error(void);
@@ -118,9 +118,17 @@ int ig_partial_weight_index(const void* Wq_s, int D, int H, int d, int r,
 /*
  * Bytes of scratch a call needs (0 if none).  op = IG_OP_REHEARSE: B, H, D,
  * r used.  IG_OP_SELECT: B, H, n, max_out used.  IG_OP_ATTN: B, H, d,
- * max_out used.  Unused arguments are ignored.
+ * max_out used.  IG_OP_SPECULATE: B, H, D, r, n used.  Unused arguments are
+ * ignored.
  */
 size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int max_out);
+
+/*
+ * Zero-fill a workspace on `stream` (a fill kernel, so it may be captured in a
+ * graph).  Required once after allocating the workspace of ig_speculate, whose
+ * calls then leave it zero-filled; harmless for the others.
+ */
+int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Speculation for the next layer (section 3.4, "Decoding Stage", steps 1-2):
@@ -136,6 +144,30 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
                 int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
                 float* q_part, float* scores, int ld,
                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Fused speculation for one layer in one launch: the partial query, speculated
+ * scores, selection and counter update of ig_rehearse + ig_select +
+ * ig_pool_touch (section 3.4, "Decoding Stage" steps 1-3 and 5, and the pool
+ * paragraph), with the scores kept on chip.  Same arguments and results as
+ * those calls; modes IG_SEL_THRESHOLD and IG_SEL_TOPK; n <= 32768 (the scores
+ * of a row live in LDS), otherwise IG_EUNSUPPORTED.
+ * q_part [B][H][r] and scores [B][H][ld] are written only when not NULL.
+ * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
+ * receives the victim.  Two launches: the partial-query projection, then one
+ * workgroup per (b, h) for scores, selection and counters.  The workspace
+ * (IG_OP_SPECULATE bytes, required) holds the projection's partial sums and
+ * one arrival word per sequence; it must have been zero-filled once with
+ * ig_workspace_init, and every call returns the arrival words to zero.  Calls
+ * sharing a workspace must not overlap.  H <= 65535.
+ */
+int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
+                 int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
+                 int mode, float alpha, int k, int max_sel,
+                 int32_t* idx, int32_t* count, int max_out,
+                 uint32_t* counters, uint32_t cmax, int32_t* victim,
+                 float* q_part, float* scores, int ld,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Per-head token selection (section 3.4, "Decoding Stage", steps 3-5).

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libig.so")
 IG_OK, IG_EINVAL, IG_EHIP, IG_EUNSUPPORTED = 0, 1, 2, 3
 IG_F32, IG_BF16 = 0, 1
 IG_SEL_THRESHOLD, IG_SEL_TOPK, IG_SEL_HEADAVG = 0, 1, 2
-IG_OP_REHEARSE, IG_OP_SELECT, IG_OP_ATTN = 0, 1, 2
+IG_OP_REHEARSE, IG_OP_SELECT, IG_OP_ATTN, IG_OP_SPECULATE = 0, 1, 2, 3
 
 _MODES = {"threshold": IG_SEL_THRESHOLD, "topk": IG_SEL_TOPK, "headavg": IG_SEL_HEADAVG}
 
@@ -46,6 +46,9 @@ _SIGS = {
     "ig_store": (_i, [_vp, _i64, _i, _vp]),
     "ig_partial_weight_index": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _i]),
     "ig_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "ig_workspace_init": (_i, [_vp, _sz, _vp]),
+    "ig_speculate": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _i, _i, _vp, _vp, _i,
+                          _vp, _u32, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "ig_rehearse": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp, _sz, _vp]),
     "ig_select": (_i, [_vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "ig_gather_kv": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
@@ -206,6 +209,36 @@ def ig_rehearse(x, Wq_part, Kp, n: int, scale: float, *, bq_part=None, q_part=No
                               float(scale), _ptr(q_part), _ptr(scores), ld, _ptr(ws), wsb, _stream(stream)),
            "ig_rehearse")
     return q_part, scores
+
+
+def ig_workspace_init(ws, *, stream=None):
+    _check(load().ig_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "ig_workspace_init")
+    return ws
+
+
+def ig_speculate(x, Wq_part, Kp, n: int, scale: float, mode: str, max_out: int, *, alpha: float = math.inf,
+                 k: int = 0, max_sel: int = 0, bq_part=None, idx=None, count=None, counters=None, cmax: int = 65535,
+                 victim=None, q_part=None, scores=None, ld=None, ws=None, stream=None):
+    """Fused partial query + scores + selection (+ counter update when ``counters`` is given).
+    ``ws`` (IG_OP_SPECULATE bytes) must have been zero-filled once by ig_workspace_init."""
+    torch = _torch()
+    B, D = x.shape
+    Bk, H, n_cap, r = Kp.shape
+    if idx is None:
+        idx = torch.empty((B, H, max_out), dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty((B, H), dtype=torch.int32, device=x.device)
+    if ld is None:
+        ld = scores.shape[2] if scores is not None else n
+    if ws is None:
+        ws = ig_workspace_init(torch.empty(ig_workspace_size(IG_OP_SPECULATE, B, H, D, 0, r, n, max_out),
+                                           dtype=torch.uint8, device=x.device), stream=stream)
+    wsb = ws.numel() * ws.element_size()
+    _check(load().ig_speculate(_ptr(x), _ptr(Wq_part), _ptr(bq_part), _ptr(Kp), B, D, H, r, n, n_cap, _dtype_of(x),
+                               float(scale), _MODES[mode], float(alpha), int(k), int(max_sel), _ptr(idx), _ptr(count),
+                               max_out, _ptr(counters), int(cmax), _ptr(victim), _ptr(q_part), _ptr(scores), ld,
+                               _ptr(ws), wsb, _stream(stream)), "ig_speculate")
+    return idx, count
 
 
 def ig_select(scores, mode: str, max_out: int, *, n=None, alpha: float = math.inf, k: int = 0, max_sel: int = 0,

@@ -88,6 +88,9 @@ size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int m
         case IG_OP_ATTN:
             if (d < 1 || max_out < 1) return 0;
             return plan_attn(B, H, d, max_out).ws_bytes;
+        case IG_OP_SPECULATE:
+            if (D < 1 || r < 1 || n < 1) return 0;
+            return speculate_ws_bytes(B, H, D, r, n, IG_BF16);
         default:
             return 0;
     }
@@ -110,6 +113,49 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
     return hip_status(launch_rehearse(x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, q_part, scores,
                                       ld, ws, stream),
                       "ig_rehearse");
+}
+
+int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+    IG_REQUIRE(ws || ws_bytes == 0, "ig_workspace_init: NULL workspace");
+    IG_REQUIRE(aligned16(ws), "ig_workspace_init: workspace must be 16-byte aligned");
+    return hip_status(launch_zero(ws, ws_bytes, stream), "ig_workspace_init");
+}
+
+int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H, int r,
+                 int n, int n_cap, int dtype, float scale, int mode, float alpha, int k, int max_sel, int32_t* idx,
+                 int32_t* count, int max_out, uint32_t* counters, uint32_t cmax, int32_t* victim, float* q_part,
+                 float* scores, int ld, void* ws, size_t ws_bytes, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_speculate", dtype);
+    IG_REQUIRE(x && Wq_part && Kp && idx && count, "ig_speculate: NULL required pointer");
+    IG_REQUIRE(B >= 1 && D >= 1 && H >= 1 && r >= 1 && n >= 1 && n <= n_cap && max_out >= 1,
+               "ig_speculate: bad sizes (B=%d D=%d H=%d r=%d n=%d n_cap=%d max_out=%d)", B, D, H, r, n, n_cap,
+               max_out);
+    IG_REQUIRE(r % 8 == 0 && pow2(r / (16 / elem_size(dtype))) && r / (16 / elem_size(dtype)) <= 32,
+               "ig_speculate: r / (16 / element size) must be a power of two <= 32 (got r=%d)", r);
+    IG_REQUIRE(!scores || ld >= n, "ig_speculate: ld must be >= n when scores are written");
+    IG_REQUIRE(std::isfinite(scale), "ig_speculate: scale must be finite");
+    IG_REQUIRE(aligned16(Wq_part) && aligned16(Kp), "ig_speculate: Wq_part and Kp must be 16-byte aligned");
+    if (mode == IG_SEL_THRESHOLD)
+        IG_REQUIRE(alpha >= 0.f && !std::isnan(alpha) && max_sel >= 0, "ig_speculate: alpha must be >= 0");
+    else if (mode == IG_SEL_TOPK)
+        IG_REQUIRE(k >= 1, "ig_speculate: k must be >= 1");
+    else if (mode == IG_SEL_HEADAVG)
+        return fail(IG_EUNSUPPORTED, "ig_speculate: the head-average mode needs every head's count first; "
+                                     "use ig_rehearse + ig_select");
+    else
+        return fail(IG_EINVAL, "ig_speculate: unknown mode %d", mode);
+    if (n > kSpecMaxRows)
+        return fail(IG_EUNSUPPORTED, "ig_speculate: n = %d exceeds %d rows; use ig_rehearse + ig_select", n,
+                    kSpecMaxRows);
+    IG_REQUIRE(!counters || cmax >= 2, "ig_speculate: cmax must be >= 2");
+    IG_REQUIRE(H <= 0xFFFF, "ig_speculate: at most 65535 heads");
+    const size_t need = speculate_ws_bytes(B, H, D, r, n, dtype);
+    IG_REQUIRE(ws && ws_bytes >= need, "ig_speculate: workspace of %zu bytes needed", need);
+    IG_REQUIRE(aligned16(ws), "ig_speculate: workspace must be 16-byte aligned");
+    return hip_status(launch_speculate(x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, mode, alpha, k,
+                                       max_sel, idx, count, max_out, counters, cmax, victim, q_part, scores, ld, ws,
+                                       stream),
+                      "ig_speculate");
 }
 
 int ig_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k, int max_sel,

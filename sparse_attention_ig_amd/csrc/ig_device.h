@@ -29,6 +29,18 @@ __device__ __forceinline__ void load_vec(const uint16_t* __restrict__ p, float (
     v[6] = __uint_as_float(t.w << 16); v[7] = __uint_as_float(t.w & 0xFFFF0000u);
 }
 
+// Widen a raw 16-byte word to floats (8 bf16 or 4 f32).
+__device__ __forceinline__ void unpack_raw(const uint4& t, float (&v)[8]) {
+    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xFFFF0000u);
+    v[4] = __uint_as_float(t.z << 16); v[5] = __uint_as_float(t.z & 0xFFFF0000u);
+    v[6] = __uint_as_float(t.w << 16); v[7] = __uint_as_float(t.w & 0xFFFF0000u);
+}
+__device__ __forceinline__ void unpack_raw(const uint4& t, float (&v)[4]) {
+    v[0] = __uint_as_float(t.x); v[1] = __uint_as_float(t.y);
+    v[2] = __uint_as_float(t.z); v[3] = __uint_as_float(t.w);
+}
+
 // Raw 16-byte copy helpers (no widening).
 __device__ __forceinline__ uint4 load_raw16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void store_raw16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -74,6 +86,36 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 __device__ __forceinline__ float key_score(uint32_t k) {
     uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
     return __uint_as_float(u);
+}
+
+// q[c] = sum over splits of part[s][b][col0 + c] (+ bias[col0 + c]) for c < R, in split order.
+// Every (split, c) load is issued by its own thread at once (a loop of dependent loads would cost
+// one memory round trip per split); s_part holds NT floats.  Ends with a barrier; q (and q_out,
+// when not NULL) then hold the sums.
+template <int NT>
+__device__ __forceinline__ void sum_partials(const float* __restrict__ part, int splits, int B, int N, int b,
+                                             int col0, int R, const float* __restrict__ bias, float* q,
+                                             float* s_part, float* q_out) {
+    const int tid = threadIdx.x;
+    const int per = NT / R;  // splits loaded per pass
+    float a = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += per) {
+        const int s = s0 + tid / R, c = tid % R;
+        float v = 0.f;
+        if (tid < per * R && s < splits) v = part[(static_cast<size_t>(s) * B + b) * N + col0 + c];
+        s_part[tid] = v;
+        __syncthreads();
+        if (tid < R) {
+            for (int k = 0; k < per && s0 + k < splits; ++k) a += s_part[k * R + tid];
+        }
+        __syncthreads();
+    }
+    if (tid < R) {
+        if (bias) a += bias[col0 + tid];
+        q[tid] = a;
+        if (q_out) q_out[tid] = a;
+    }
+    __syncthreads();
 }
 
 // Lanes below this one in the wave, as a 64-bit mask.

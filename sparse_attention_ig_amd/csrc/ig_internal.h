@@ -43,10 +43,16 @@ AttnPlan plan_attn(int B, int H, int d, int max_out);
 
 size_t select_ws_bytes(int B, int H, int n, int max_out);
 
+constexpr int kSpecMaxRows = 32768;   // fused speculation keeps every score of a row in LDS
+size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int dtype);
+size_t speculate_lds_bytes(int n);
+
 // kernel launchers (return hipError_t as int)
 int launch_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
                     int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
                     float* q_part, float* scores, int ld, void* ws, hipStream_t s);
+int launch_proj(const void* x, const void* W, int B, int D, int N, int dtype, const RehearsePlan& p, float* part,
+                hipStream_t s);
 int launch_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k,
                   int max_sel, int32_t* idx, int32_t* count, int max_out, void* ws, hipStream_t s);
 int launch_attn(const void* q, const void* K, const void* V, int ld_rows, const int32_t* idx,
@@ -56,6 +62,11 @@ int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_
                   int d, int n_cap, int max_out, int dtype, void* Kc, void* Vc, hipStream_t s);
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n,
                  int n_cap, int max_out, uint32_t cmax, int32_t* victim, hipStream_t s);
+int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H,
+                     int r, int n, int n_cap, int dtype, float scale, int mode, float alpha, int k, int max_sel,
+                     int32_t* idx, int32_t* count, int max_out, uint32_t* counters, uint32_t cmax, int32_t* victim,
+                     float* q_part, float* scores, int ld, void* ws, hipStream_t s);
+int launch_zero(void* ws, size_t bytes, hipStream_t s);
 int launch_build_partial(const void* K, const int32_t* chan, void* Kp, int B, int H, int d, int r,
                          int n_cap, int row0, int row1, int dtype, hipStream_t s);
 int launch_append(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan,

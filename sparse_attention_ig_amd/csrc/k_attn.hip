@@ -10,10 +10,12 @@
 // and its slice of the weighted V accumulator).  Rows are gathered straight
 // from the cache through the index list (no staging copy in HBM).
 //
-// Split-K: the selected rows of one (b, h) are cut into splits of
-// rows_per_split rows, one workgroup each, so that long selections spread over
-// the chip.  Lane groups of a workgroup are merged through LDS; splits are
-// merged by k_attn_combine with the usual (m, l, acc) rescaling.
+// Each lane group keeps 8 rows of K and V in flight at once and folds them into
+// its running state with one rescale per 8 rows.  Split-K: when there are too
+// few (b, h) units to fill the chip, the selected rows of one (b, h) are cut
+// into splits of at least 128 rows, one workgroup each.  Lane groups of a
+// workgroup are merged through LDS; splits are merged by k_attn_combine with
+// the usual (m, l, acc) rescaling.
 #include <cmath>
 
 #include "ig_device.h"
@@ -22,7 +24,8 @@
 namespace ig {
 
 constexpr int kAttnThreads = 256;
-constexpr int kAttnUnroll = 2;
+constexpr int kAttnUnroll = 8;  // rows per lane group in flight at once (K and V: 16 x 16 bytes per lane)
+
 
 template <typename T, int LPR>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_split(
@@ -31,59 +34,90 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(
     int rows_per_split, int nsplit, float scale, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part) {
     constexpr int VEC = Vec<T>::N;
-    constexpr int G = kAttnThreads / LPR;  // lane groups (rows in flight) per workgroup
+    constexpr int G = kAttnThreads / LPR;  // lane groups (one row each) per workgroup
+    constexpr int U = kAttnUnroll;
     __shared__ float s_m[G], s_l[G];
     __shared__ float s_acc[G * LPR * VEC];
 
     const int bh = blockIdx.y, split = blockIdx.x, tid = threadIdx.x;
     const int li = tid % LPR, gi = tid / LPR;
-    int c = min(count[bh], max_out);
+    // round trip 1: the count, the query slice and the first batch of indices are loaded together
+    // (indices past the count are loaded from the idx row and ignored)
+    const int c_raw = count[bh];
+    const uint4 qraw = load_raw16(q + static_cast<size_t>(bh) * d + li * VEC);
+    const int32_t* irow = idx ? idx + static_cast<size_t>(bh) * max_out : nullptr;
+    const int r0 = split * rows_per_split;
+    const int rcap = min(max_out, r0 + rows_per_split);
+    int ipre[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = r0 + u * G + gi;
+        ipre[u] = (irow && i < rcap) ? irow[i] : i;
+    }
+    int c = min(c_raw, max_out);
     if (!idx) c = min(c, ld_rows);
-    const int r0 = split * rows_per_split, r1 = min(c, r0 + rows_per_split);
+    const int r1 = min(c, rcap);
 
     float qv[VEC];
-    load_vec(q + static_cast<size_t>(bh) * d + li * VEC, qv);
+    unpack_raw(qraw, qv);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) qv[v] *= scale;
 
-    const size_t head = static_cast<size_t>(bh) * ld_rows * d + li * VEC;
-    const int32_t* irow = idx ? idx + static_cast<size_t>(bh) * max_out : nullptr;
+    const T* Kh = K + static_cast<size_t>(bh) * ld_rows * d + li * VEC;
+    const T* Vh = V + static_cast<size_t>(bh) * ld_rows * d + li * VEC;
     float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
-    for (int ib = r0; ib < r1; ib += G * kAttnUnroll) {
-        float kv[kAttnUnroll][VEC], vv[kAttnUnroll][VEC];
-        bool live[kAttnUnroll];
+    for (int ib = r0; ib < r1; ib += G * U) {
+        int rows[U];
 #pragma unroll
-        for (int u = 0; u < kAttnUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int i = ib + u * G + gi;
-            live[u] = i < r1;
-            if (live[u]) {
-                int row = irow ? irow[i] : i;
-                row = min(max(row, 0), ld_rows - 1);
-                const size_t off = head + static_cast<size_t>(row) * d;
-                load_vec(K + off, kv[u]);
-                load_vec(V + off, vv[u]);
+            int row = -1;
+            if (i < r1) row = min(max(ib == r0 ? ipre[u] : (irow ? irow[i] : i), 0), ld_rows - 1);
+            rows[u] = row;
+        }
+        // round trip 2: every K and V row slice of this batch in flight at once
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (rows[u] >= 0) {
+                kr[u] = load_raw16(Kh + static_cast<size_t>(rows[u]) * d);
+                vr[u] = load_raw16(Vh + static_cast<size_t>(rows[u]) * d);
+            } else {
+                kr[u] = make_uint4(0, 0, 0, 0);
+                vr[u] = make_uint4(0, 0, 0, 0);
             }
         }
+        float sc[U];
+        float mb = m;
 #pragma unroll
-        for (int u = 0; u < kAttnUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
+            float kv[VEC];
+            unpack_raw(kr[u], kv);
             float s = 0.f;
-            if (live[u]) {
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) s = fmaf(qv[v], kv[u][v], s);
-            }
+            for (int v = 0; v < VEC; ++v) s = fmaf(qv[v], kv[v], s);
             s = group_sum<LPR>(s);
-            if (live[u]) {
-                const float mn = fmaxf(m, s);
-                const float corr = __expf(m - mn);  // m = -inf on the first row: exp(-inf) = 0
-                const float p = __expf(s - mn);
-                l = l * corr + p;
+            sc[u] = rows[u] >= 0 ? s : -INFINITY;
+            mb = fmaxf(mb, sc[u]);
+        }
+        if (mb != -INFINITY) {  // this lane group has at least one live row (now or before)
+            const float corr = __expf(m - mb);  // m = -inf before the first row: exp(-inf) = 0
+            l *= corr;
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(p, vv[u][v], acc[v] * corr);
-                m = mn;
+            for (int v = 0; v < VEC; ++v) acc[v] *= corr;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float pw = __expf(sc[u] - mb);  // dead rows: exp(-inf) = 0
+                float vv[VEC];
+                unpack_raw(vr[u], vv);
+                l += pw;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(pw, vv[v], acc[v]);
             }
+            m = mb;
         }
     }
     if (li == 0) {
@@ -145,12 +179,18 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 
 AttnPlan plan_attn(int B, int H, int d, int max_out) {
     AttnPlan p{};
-    const int64_t rows = static_cast<int64_t>(max_out) * B * H;
-    int64_t rps = (rows + 1023) / 1024;  // ~1024 workgroups when the selection is long
-    rps = ((rps + 31) / 32) * 32;
-    rps = std::max<int64_t>(32, std::min<int64_t>(1024, rps));
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    // one workgroup per (b, h) when there are enough of them to fill the chip; otherwise split the
+    // selected rows so that about 512 workgroups run, each with at least 128 rows
+    int64_t nsplit = 1;
+    if (bh < 256) {
+        nsplit = (512 + bh - 1) / bh;
+        nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, (max_out + 127) / 128));
+    }
+    int64_t rps = (max_out + nsplit - 1) / nsplit;
+    rps = ((rps + 15) / 16) * 16;
     p.rows_per_split = static_cast<int>(rps);
-    p.nsplit = (max_out + p.rows_per_split - 1) / p.rows_per_split;
+    p.nsplit = static_cast<int>((max_out + rps - 1) / rps);
     p.ws_bytes = p.nsplit > 1 ? static_cast<size_t>(B) * H * p.nsplit * (2 + d) * sizeof(float) : 0;
     return p;
 }

@@ -18,16 +18,13 @@
 // the host link (zero-copy) and the writes land in HBM.
 #include "ig_device.h"
 #include "ig_internal.h"
+#include "ig_pool_dev.h"
 
 namespace ig {
 
 constexpr int kTouchThreads = 1024;
 constexpr int kTouchMaxHeads = 1024;
 constexpr int kGatherThreads = 256;
-
-__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // One workgroup per sequence: every (head, selected slot) of that sequence adds
 // 1 with an integer atomic; an increment that returns cmax - 1 or more means
@@ -46,57 +43,25 @@ __global__ __launch_bounds__(kTouchThreads) void k_touch(uint32_t* __restrict__ 
 
     int sat = 0;
     const int total = H * max_out;
-    for (int e = tid; e < total; e += kTouchThreads) {
-        const int h = e / max_out, i = e - h * max_out;
-        if (i < s_cnt[h]) {
-            const int j = idx[(static_cast<size_t>(b) * H + h) * max_out + i];
-            if (j >= 0 && j < n) {
-                const uint32_t old = atomicAdd(&row[j], 1u);
-                if (old + 1u >= cmax) sat = 1;
-            }
+    constexpr int U = 8;  // index loads, then atomics, 8 per lane at a time, each batch issued together
+    for (int e0 = tid; e0 < total; e0 += kTouchThreads * U) {
+        int jj[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * kTouchThreads;
+            const int h = e / max_out, i = e - h * max_out;
+            jj[u] = (e < total && i < s_cnt[h]) ? idx[(static_cast<size_t>(b) * H + h) * max_out + i] : -1;
         }
+        uint32_t old[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) old[u] = (jj[u] >= 0 && jj[u] < n) ? atomicAdd(&row[jj[u]], 1u) : 0u;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (jj[u] >= 0 && jj[u] < n && old[u] + 1u >= cmax) sat = 1;
     }
     sat = __syncthreads_or(sat);
-    if (sat) {
-        for (int j = tid; j < n; j += kTouchThreads) {
-            const uint32_t v = coherent_load(&row[j]);
-            row[j] = (v < cmax ? v : cmax) >> 1;
-        }
-    }
-    if (!victim) return;
-    // argmin over j < n, lowest index on ties; a thread re-reads only slots it wrote itself
-    uint32_t best = 0xFFFFFFFFu;
-    int bi = n;
-    for (int j = tid; j < n; j += kTouchThreads) {
-        const uint32_t v = coherent_load(&row[j]);
-        if (v < best) {
-            best = v;
-            bi = j;
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const uint32_t ov = __shfl_xor(best, m, kWave);
-        const int oi = __shfl_xor(bi, m, kWave);
-        if (ov < best || (ov == best && oi < bi)) {
-            best = ov;
-            bi = oi;
-        }
-    }
-    const int lane = tid % kWave, wave = tid / kWave;
-    if (lane == 0) {
-        s_val[wave] = best;
-        s_idx[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int w = 1; w < kTouchThreads / kWave; ++w)
-            if (s_val[w] < best || (s_val[w] == best && s_idx[w] < bi)) {
-                best = s_val[w];
-                bi = s_idx[w];
-            }
-        victim[b] = bi;
-    }
+    const int v = pool_finish<kTouchThreads>(row, n, cmax, sat != 0, victim != nullptr, s_val, s_idx);
+    if (victim && tid == 0) victim[b] = v;
 }
 
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n, int n_cap,

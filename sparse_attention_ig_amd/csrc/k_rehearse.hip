@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kProjThreads) void k_rehearse_proj(
     constexpr int VEC = Vec<T>::N;
     constexpr int CPT = 64 / VEC;            // lanes across the 64-column tile
     constexpr int RSUB = kProjThreads / CPT; // rows in flight per workgroup step
-    extern __shared__ float smem[];          // x slice [BB][rows_per_split], later the reduction buffer
+    extern __shared__ __align__(16) float smem[];  // x slice [BB][rows_per_split], later the reduction buffer
 
     const int tid = threadIdx.x;
     const int cg = tid % CPT, rs = tid / CPT;
@@ -38,11 +38,33 @@ __global__ __launch_bounds__(kProjThreads) void k_rehearse_proj(
     const int kn = min(rows_per_split, D - k0);
     const int b0 = blockIdx.z * BB;
 
-    for (int i = tid; i < BB * rows_per_split; i += kProjThreads) {
-        const int bb = i / rows_per_split, kk = i - bb * rows_per_split;
-        float v = 0.f;
-        if (b0 + bb < B && kk < kn) v = to_f32(x[static_cast<size_t>(b0 + bb) * D + k0 + kk]);
-        smem[i] = v;
+    // every weight row of this lane is put in flight before anything waits (one HBM round trip);
+    // rows_per_split <= 256, so a lane owns at most 256 / RSUB rows
+    constexpr int UMAX = 256 / RSUB;
+    uint4 w[UMAX];
+    const bool col_ok = col < N;
+    const T* wp = W + static_cast<size_t>(k0) * N + col;
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) {
+        const int kk = rs + u * RSUB;
+        w[u] = (col_ok && kk < kn) ? load_raw16(wp + static_cast<size_t>(kk) * N) : make_uint4(0, 0, 0, 0);
+    }
+    // x slice [BB][rows_per_split] into LDS; all of a lane's loads are issued before any store
+    {
+        constexpr int UX = (16 * 256 + kProjThreads - 1) / kProjThreads;  // BB <= 16, rows_per_split <= 256
+        float xv[UX];
+#pragma unroll
+        for (int u = 0; u < UX; ++u) {
+            const int i = tid + u * kProjThreads;
+            const int bb = i / rows_per_split, kk = i - bb * rows_per_split;
+            xv[u] = (i < BB * rows_per_split && b0 + bb < B && kk < kn)
+                        ? to_f32(x[static_cast<size_t>(b0 + bb) * D + k0 + kk]) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < UX; ++u) {
+            const int i = tid + u * kProjThreads;
+            if (i < BB * rows_per_split) smem[i] = xv[u];
+        }
     }
     __syncthreads();
 
@@ -51,58 +73,34 @@ __global__ __launch_bounds__(kProjThreads) void k_rehearse_proj(
     for (int bb = 0; bb < BB; ++bb)
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[bb][v] = 0.f;
-
-    if (col < N) {
-        const T* wp = W + static_cast<size_t>(k0) * N + col;
-        int kk = rs;
-        for (; kk + 3 * RSUB < kn; kk += 4 * RSUB) {
-            float w[4][VEC];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) load_vec(wp + static_cast<size_t>(kk + u * RSUB) * N, w[u]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int bb = 0; bb < BB; ++bb) {
-                    const float xv = smem[bb * rows_per_split + kk + u * RSUB];
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) acc[bb][v] = fmaf(xv, w[u][v], acc[bb][v]);
-                }
-        }
-        for (; kk < kn; kk += RSUB) {
-            float w[VEC];
-            load_vec(wp + static_cast<size_t>(kk) * N, w);
+    for (int u = 0; u < UMAX; ++u) {
+        const int kk = rs + u * RSUB;
+        if (kk < kn) {
+            float wv[VEC];
+            unpack_raw(w[u], wv);
 #pragma unroll
             for (int bb = 0; bb < BB; ++bb) {
                 const float xv = smem[bb * rows_per_split + kk];
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[bb][v] = fmaf(xv, w[v], acc[bb][v]);
+                for (int v = 0; v < VEC; ++v) acc[bb][v] = fmaf(xv, wv[v], acc[bb][v]);
             }
         }
     }
-    // lanes of one wave that share a column group differ in the lane bits >= log2(CPT)
+    // reduction over the RSUB row groups through LDS (cross-lane shuffles of 64 values per lane cost
+    // more than the whole weight stream): red[rs][bb][64 columns], then each output sums RSUB terms
+    __syncthreads();  // x slice no longer needed
+    float* red = smem;
 #pragma unroll
     for (int bb = 0; bb < BB; ++bb)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v)
-#pragma unroll
-            for (int m = CPT; m < kWave; m <<= 1) acc[bb][v] += __shfl_xor(acc[bb][v], m, kWave);
-
-    __syncthreads();  // x slice no longer needed
-    const int wave = tid / kWave, lane = tid % kWave;
-    float* red = smem;  // [4 waves][BB][64]
-    if (lane < CPT) {
-#pragma unroll
-        for (int bb = 0; bb < BB; ++bb)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) red[(wave * BB + bb) * 64 + cg * VEC + v] = acc[bb][v];
-    }
+        for (int v = 0; v < VEC; ++v) red[(rs * BB + bb) * 64 + cg * VEC + v] = acc[bb][v];
     __syncthreads();
-    constexpr int NWAVE = kProjThreads / kWave;
     for (int i = tid; i < BB * 64; i += kProjThreads) {
         const int bb = i / 64, c = i % 64;
         float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) s += red[(w * BB + bb) * 64 + c];
+#pragma unroll 8
+        for (int g = 0; g < RSUB; ++g) s += red[(g * BB + bb) * 64 + c];
         const int b = b0 + bb, cc = blockIdx.x * 64 + c;
         if (b < B && cc < N) part[(static_cast<size_t>(blockIdx.y) * B + b) * N + cc] = s;
     }
@@ -116,18 +114,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_rehearse_score(
     constexpr int VEC = Vec<T>::N;
     constexpr int RPI = kScoreThreads / LPR;  // rows per workgroup step
     __shared__ float qs[LPR * VEC];
+    __shared__ float s_part[kScoreThreads];
 
     const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
     const int N = H * r;
     const int tid = threadIdx.x;
-    for (int c = tid; c < r; c += kScoreThreads) {
-        float a = 0.f;
-        for (int s = 0; s < splits; ++s) a += part[(static_cast<size_t>(s) * B + b) * N + h * r + c];
-        if (bias) a += bias[h * r + c];
-        qs[c] = a;
-        if (blockIdx.x == 0) q_part[static_cast<size_t>(bh) * r + c] = a;
-    }
-    __syncthreads();
+    sum_partials<kScoreThreads>(part, splits, B, N, b, h * r, r, bias, qs, s_part,
+                                blockIdx.x == 0 ? q_part + static_cast<size_t>(bh) * r : nullptr);
 
     const int li = tid % LPR, ri = tid / LPR;
     float q[VEC];
@@ -189,19 +182,42 @@ RehearsePlan plan_rehearse(int B, int H, int D, int r, int n, int dtype) {
     return p;
 }
 
+template <typename T, int BB>
+static int launch_proj_bb(dim3 grid, size_t smem, hipStream_t s, const T* x, const T* W, int B, int D, int N, int rps,
+                          float* part) {
+    static bool attr_set = false;  // dynamic LDS above 64 KB needs the per-function limit raised once
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rehearse_proj<T, BB>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_rehearse_proj<T, BB>), grid, dim3(kProjThreads), smem, s, x, W, B, D, N, rps, part);
+    return static_cast<int>(hipGetLastError());
+}
+
 template <typename T>
 static int launch_proj_t(const T* x, const T* W, int B, int D, int N, const RehearsePlan& p, float* part,
                          hipStream_t s) {
     dim3 grid(p.tiles, p.splits, p.bblocks);
-    const size_t smem = static_cast<size_t>(p.bb) * std::max(p.rows_per_split, 256) * sizeof(float);
+    // x slice [bb][rows_per_split], then the reduction buffer [row groups][bb][64]
+    const int rsub = kProjThreads / (64 / Vec<T>::N);
+    const size_t smem = static_cast<size_t>(p.bb) * std::max(p.rows_per_split, rsub * 64) * sizeof(float);
     switch (p.bb) {
-        case 1: hipLaunchKernelGGL((k_rehearse_proj<T, 1>), grid, dim3(kProjThreads), smem, s, x, W, B, D, N, p.rows_per_split, part); break;
-        case 2: hipLaunchKernelGGL((k_rehearse_proj<T, 2>), grid, dim3(kProjThreads), smem, s, x, W, B, D, N, p.rows_per_split, part); break;
-        case 4: hipLaunchKernelGGL((k_rehearse_proj<T, 4>), grid, dim3(kProjThreads), smem, s, x, W, B, D, N, p.rows_per_split, part); break;
-        case 8: hipLaunchKernelGGL((k_rehearse_proj<T, 8>), grid, dim3(kProjThreads), smem, s, x, W, B, D, N, p.rows_per_split, part); break;
-        default: hipLaunchKernelGGL((k_rehearse_proj<T, 16>), grid, dim3(kProjThreads), smem, s, x, W, B, D, N, p.rows_per_split, part); break;
+        case 1: return launch_proj_bb<T, 1>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
+        case 2: return launch_proj_bb<T, 2>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
+        case 4: return launch_proj_bb<T, 4>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
+        case 8: return launch_proj_bb<T, 8>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
+        default: return launch_proj_bb<T, 16>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
     }
     return static_cast<int>(hipGetLastError());
+}
+
+int launch_proj(const void* x, const void* W, int B, int D, int N, int dtype, const RehearsePlan& p, float* part,
+                hipStream_t s) {
+    if (dtype == IG_BF16)
+        return launch_proj_t(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), B, D, N, p, part, s);
+    return launch_proj_t(static_cast<const float*>(x), static_cast<const float*>(W), B, D, N, p, part, s);
 }
 
 template <typename T>

@@ -97,6 +97,7 @@ class DeviceLayer:
         L.ig_build_partial_cache(self.K, self.chan, self.Kp, 0, s.n)
         self.counters = to_device(counters if counters is not None else np.zeros((s.B, s.cap), dtype=np.uint32))
         self.max_out = max_out or s.cap
+        self.keep_scores = True   # the fused path writes the scores to HBM only when asked
         dv = "cuda"
         self.q_part = torch.empty((s.B, s.H, s.r), dtype=torch.float32, device=dv)
         self.scores = torch.empty((s.B, s.H, s.cap), dtype=torch.float32, device=dv)
@@ -109,6 +110,10 @@ class DeviceLayer:
                  L.ig_workspace_size(L.IG_OP_SELECT, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out),
                  L.ig_workspace_size(L.IG_OP_ATTN, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out), 16)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dv)
+        # the fused speculation keeps its arrival words in its own workspace, zero between calls
+        self.ws_spec = L.ig_workspace_init(torch.empty(
+            L.ig_workspace_size(L.IG_OP_SPECULATE, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out),
+            dtype=torch.uint8, device=dv))
 
     def clone(self) -> "DeviceLayer":
         """A copy in distinct HBM buffers (device-to-device copies of every tensor)."""
@@ -122,7 +127,8 @@ class DeviceLayer:
     def nbytes(self) -> int:
         return sum(v.numel() * v.element_size() for v in vars(self).values() if hasattr(v, "is_cuda"))
 
-    PARTS = ("rehearse", "select", "attn", "touch")
+    PARTS = ("rehearse", "select", "attn", "touch")      # the six-call path
+    FUSED = ("speculate", "attn")                        # fused speculation, then attention
 
     def step(self, *, mode: str, alpha: float = math.inf, k: int = 0, max_sel: int = 0,
              max_out: Optional[int] = None, cmax: int = 65535, want_victim: bool = False,
@@ -149,6 +155,14 @@ class DeviceLayer:
             elif part == "attn":
                 L.ig_sparse_decode_attn(self.q, self.K, self.V, idx, self.count, s.softmax_scale, out=self.out,
                                         lse=self.lse, ws=self.ws, stream=stream)
+            elif part == "speculate":
+                if mode == "headavg":
+                    raise ValueError("the fused speculation has no head-average mode")
+                L.ig_speculate(self.x, self.Wq_part, self.Kp, n, s.softmax_scale, mode, max_out, alpha=alpha, k=k,
+                               max_sel=max_sel, idx=idx, count=self.count, counters=self.counters, cmax=cmax,
+                               victim=self.victim if want_victim else None, q_part=self.q_part,
+                               scores=self.scores if self.keep_scores else None, ld=s.cap, ws=self.ws_spec,
+                               stream=stream)
             elif part == "touch":
                 L.ig_pool_touch(self.counters, idx, self.count, n, cmax,
                                 victim=self.victim if want_victim else None, stream=stream)

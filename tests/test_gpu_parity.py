@@ -68,8 +68,8 @@ def _max_out(spec, mode, kw):
     return spec.n
 
 
-def check_step(name, spec, mode, kw, lib_in=None, ora_in=None):
-    say(f"[case {name}] B={spec.B} H={spec.H} d={spec.d} n={spec.n} r={spec.r} {spec.dtype} mode={mode} {kw}")
+def check_step(name, spec, mode, kw, lib_in=None, ora_in=None, path="unfused"):
+    say(f"[case {name}] {path} B={spec.B} H={spec.H} d={spec.d} n={spec.n} r={spec.r} {spec.dtype} mode={mode} {kw}")
     lib_in = lib_in or harness.lib_inputs(spec)
     ora_in = ora_in or harness.oracle_inputs(spec)
     mism = harness.compare_inputs(lib_in, ora_in)
@@ -83,8 +83,15 @@ def check_step(name, spec, mode, kw, lib_in=None, ora_in=None):
     want_victim = bool(kw.get("victim"))
 
     layer = DeviceLayer(lib_in, C0)
+    parts = DeviceLayer.FUSED if path == "fused" else DeviceLayer.PARTS
     g = to_host(layer.step(mode=mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out, cmax=cmax,
-                           want_victim=want_victim))
+                           want_victim=want_victim, parts=parts))
+    if path == "fused":
+        # the arrival words (after the projection partials) are back to zero
+        from sparse_attention_ig_amd import _lib as L
+        part = L.ig_workspace_size(L.IG_OP_REHEARSE, spec.B, spec.H, spec.D, spec.d, spec.r, spec.cap)
+        off = (part + 255) // 256 * 256
+        assert not host(layer.ws_spec)[off:off + 4 * spec.B].any(), "arrival words must return to zero"
     say(f"[case {name}] gpu step done")
     ref = harness.oracle_step(ora_in, mode=mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out, cmax=cmax,
                               counters=C0, want_victim=want_victim)
@@ -136,6 +143,15 @@ def check_step(name, spec, mode, kw, lib_in=None, ora_in=None):
 @pytest.mark.parametrize("name,factory,mode,kw", CASES, ids=[c[0] for c in CASES])
 def test_decode_step_parity(name, factory, mode, kw):
     check_step(name, factory(), mode, kw)
+
+
+FUSED_CASES = [c for c in CASES if c[2] != "headavg"]
+
+
+@pytest.mark.parametrize("name,factory,mode,kw", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_speculation_parity(name, factory, mode, kw):
+    """ig_speculate (partial query, scores, selection and counters in one launch) + attention."""
+    check_step(name, factory(), mode, kw, path="fused")
 
 
 # ---------------------------------------------------------------- per-kernel parity on generator inputs
