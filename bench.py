@@ -57,6 +57,12 @@ def main() -> int:
     ap.add_argument("--mode", choices=["topk", "threshold"], default="topk")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: ig_speculate + ig_sparse_decode_attn; unfused: the six-call path")
+    ap.add_argument("--workload", choices=["opt-6.7b", "llama2-7b-long", "llama2-13b-pipeline", "opt-30b-pool"],
+                    default="opt-6.7b",
+                    help="opt-6.7b: the headline layer; the others are extra measurements")
+    ap.add_argument("--n", type=int, default=0, help="context rows (llama2-7b-long)")
+    ap.add_argument("--batch", type=int, default=0, help="batch (llama2-7b-long)")
+    ap.add_argument("--frac", type=float, default=0.01, help="top-k budget as a fraction of n (llama2-7b-long)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -76,17 +82,28 @@ def main() -> int:
         return 1
     _lib.load()
 
-    spec = gen.opt_6_7b()
+    if args.workload == "llama2-13b-pipeline":
+        return bench_pipeline(args)
+    if args.workload == "opt-30b-pool":
+        return bench_pool(args)
+    if args.workload == "llama2-7b-long":
+        spec = gen.llama2_7b_long(n=args.n or 32768, B=args.batch or 1, frac=args.frac)
+        if args.path == "fused" and spec.n > 32768:
+            args.path = "unfused"   # the fused speculation keeps a row's scores in LDS: n <= 32768
+    else:
+        spec = gen.opt_6_7b()
     if args.mode == "topk":
         step_kw = dict(mode="topk", k=spec.topk, max_out=spec.topk)
-        wl = f"opt-6.7b decode layer B{spec.B} H{spec.H} d{spec.d} D{spec.D} n{spec.n} r{spec.r} bf16 top-{spec.topk}"
+        wl = f"{spec.name} decode layer B{spec.B} H{spec.H} d{spec.d} D{spec.D} n{spec.n} r{spec.r} bf16 top-{spec.topk}"
     else:
         step_kw = dict(mode="threshold", alpha=spec.alpha, max_sel=spec.max_sel, max_out=spec.max_sel)
-        wl = (f"opt-6.7b decode layer B{spec.B} H{spec.H} d{spec.d} D{spec.D} n{spec.n} r{spec.r} bf16 "
+        wl = (f"{spec.name} decode layer B{spec.B} H{spec.H} d{spec.d} D{spec.D} n{spec.n} r{spec.r} bf16 "
               f"alpha={spec.alpha} cap={spec.max_sel}")
-    print(f"[bench] preparing {wl} x {args.layers} layers", file=sys.stderr, flush=True)
+    print(f"[bench] preparing {wl}", file=sys.stderr, flush=True)
     host = prepare_layer(spec)
     base = DeviceLayer(host, max_out=step_kw["max_out"])
+    if args.workload != "opt-6.7b":
+        args.layers = max(2, min(args.layers, int(math.ceil(2e9 / base.nbytes()))))
     base.keep_scores = args.path == "unfused"   # the fused path keeps the scores on chip
     layers = [base] + [base.clone() for _ in range(args.layers - 1)]
     torch.cuda.synchronize()
@@ -166,7 +183,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded OPT-6.7B-shaped draws, no weights or datasets)",
+        "data": f"synthetic (seeded {spec.name}-shaped draws, no weights or datasets)",
         "config": {"workload": wl, "layers_per_step": args.layers, "footprint_GB": round(footprint / 1e9, 2),
                    "mean_selected_per_head": round(c_mean, 1), "path": args.path,
                    "calls_per_layer": list(PARTS)},
@@ -185,6 +202,158 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, step_kw, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_pipeline(args) -> int:
+    """40-layer Llama-2-13B-shaped decode pipeline (speculation for layer l+1 at layer l, layer 0 dense,
+    one appended token per step), measured at the first step (n = 4096) and at the last one
+    (n = 4351) of a 256-token generation.  One layer's draws are cloned into 40 distinct buffers."""
+    import numpy as np
+    import torch
+    from sparse_attention_ig_amd import _lib, gen
+    from sparse_attention_ig_amd.pipeline import DecodePipeline
+    from sparse_attention_ig_amd.runtime import prepare_layer, to_device
+
+    L_ = 40
+    res = {}
+    for n0 in (4096, 4351):
+        spec = gen.llama2_13b(n=n0, B=16, n_cap=4352)
+        print(f"[bench] preparing llama2-13b pipeline n={n0}", file=sys.stderr, flush=True)
+        host = prepare_layer(spec)
+        max_out = int(math.ceil(0.05 * spec.cap))
+        pipe = DecodePipeline([host], max_out=max_out)
+        base = pipe.layers[0]
+        pipe.layers = [base] + [base.clone() for _ in range(L_ - 1)]
+        xs = gen.pipeline_x(spec, L_, 1)
+        xd = [to_device(xs[0, l]) for l in range(L_)]
+        kn, vn = gen.draw_new_rows(spec, 0, 0)
+        knd, vnd = [to_device(kn)] * L_, [to_device(vn)] * L_
+
+        def run():
+            pipe.n = n0
+            pipe.step(xd, knd, vnd)
+
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        for _ in range(args.warmup):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        k = min(max_out, int(math.ceil(0.05 * n0)))
+        s_ = 2
+        per_layer = (spec.D * spec.H * spec.r * s_ + spec.B * spec.D * s_ + spec.B * spec.H * n0 * spec.r * s_
+                     + spec.B * spec.H * k * (2 * spec.d * s_ + 8) + spec.B * spec.H * spec.d * (s_ + 4))
+        res[n0] = {"ms_per_step": round(ms, 4), "tokens_s_layer": round(spec.B * L_ / (ms / 1e3), 1),
+                   "alg_GBs_layers_1_to_39": round(per_layer * (L_ - 1) / (ms / 1e3) / 1e9, 1), "k": k}
+        del pipe, base, g
+        torch.cuda.empty_cache()
+    out = {"metric": METRIC, "value": res[4096]["tokens_s_layer"], "unit": "tokens/s/layer", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res[4096]["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded Llama-2-13B-shaped draws, one layer cloned into 40 buffers)",
+           "config": {"workload": "llama2-13b 40-layer decode pipeline B16 H40 d128 D5120 r32 top-5%, n 4096 and 4351",
+                      "per_step": res}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_pool(args) -> int:
+    """OPT-30B-shaped layers with the full KV cache in a pinned host pool (threshold alpha 5, 20% cap).
+    Per layer: speculation in HBM on the main stream; the selected rows gathered over the host link
+    (zero-copy) on a side stream; attention on the compact rows once the gather is done.  The gather of
+    layer l overlaps the speculation of layer l+1 and the attention of layer l-1."""
+    import numpy as np
+    import torch
+    from sparse_attention_ig_amd import _lib, gen
+    from sparse_attention_ig_amd.runtime import PoolLayer, prepare_layer
+
+    nl = args.layers if args.layers != 32 else 8
+    res = {}
+    for n in (2048, 4096):
+        spec = gen.opt_30b(n=n, B=16, n_cap=4096)
+        print(f"[bench] preparing opt-30b pool n={n} x {nl} host-resident layers", file=sys.stderr, flush=True)
+        host = prepare_layer(spec)
+        layers = [PoolLayer(host, max_out=spec.max_sel) for _ in range(nl)]
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+
+        def step(timing=None):
+            E = [ev() for _ in layers]
+            F = [ev() for _ in layers]
+            G0 = [ev() for _ in layers]
+            for l, lay in enumerate(layers):
+                lay.speculate(alpha=spec.alpha, max_sel=spec.max_sel, stream=main)
+                E[l].record(main)
+                side.wait_event(E[l])
+                G0[l].record(side)
+                lay.gather(stream=side)
+                F[l].record(side)
+                if l > 0:
+                    main.wait_event(F[l - 1])
+                    layers[l - 1].attend(stream=main)
+            main.wait_event(F[-1])
+            layers[-1].attend(stream=main)
+            if timing is not None:
+                timing.append((G0, F))
+
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        gathers = []
+        a.record(main)
+        for _ in range(args.steps):
+            step(gathers)
+        b.record(main)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        g_ms = float(np.mean([s0.elapsed_time(f) for G0, F in gathers for s0, f in zip(G0, F)]))
+        cnt = sum(int(l.count.sum().item()) for l in layers) / nl
+        link_bytes = cnt * spec.d * 2 * 2
+        res[n] = {"ms_per_step": round(ms, 3), "layers": nl, "t_layer_us": round(ms * 1e3 / nl, 1),
+                  "tokens_s_layer": round(spec.B * nl / (ms / 1e3), 1),
+                  "selected_rows_per_layer": int(cnt), "gather_us": round(g_ms * 1e3, 1),
+                  "host_link_GBs": round(link_bytes / (g_ms / 1e3) / 1e9, 2)}
+        del layers
+        torch.cuda.empty_cache()
+    # the pinned host -> device copy ceiling over the same link
+    src = torch.empty(1 << 30, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    h2d = 5 * (1 << 30) / (a.elapsed_time(b) / 1e3) / 1e9
+    out = {"metric": METRIC, "value": res[4096]["tokens_s_layer"], "unit": "tokens/s/layer", "n_gpus": 1,
+           "steps": args.steps, "warmup": 2, "ms_per_step": res[4096]["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded OPT-30B-shaped draws; one layer's pool copied into each pinned buffer)",
+           "config": {"workload": f"opt-30b pinned host KV pool B16 H56 d128 D7168 r32 alpha 5 cap 20%, {nl} layers",
+                      "per_n": res, "pinned_h2d_copy_GBs": round(h2d, 2)}}
     print(json.dumps(out), flush=True)
     return 0
 

@@ -46,11 +46,11 @@ extern "C" {
 enum { IG_OK = 0, IG_EINVAL = 1, IG_EHIP = 2, IG_EUNSUPPORTED = 3 };
 enum { IG_F32 = 0, IG_BF16 = 1 };
 enum { IG_SEL_THRESHOLD = 0, IG_SEL_TOPK = 1, IG_SEL_HEADAVG = 2 };
-enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3 };
+enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3, IG_OP_TOUCH = 4 };
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* ig_last_error(void);
-/* ABI version: bumped on any signature change. */
+/* ABI version: bumped on any signature change (2: ig_pool_touch takes a workspace). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -118,8 +118,8 @@ int ig_partial_weight_index(const void* Wq_s, int D, int H, int d, int r,
 /*
  * Bytes of scratch a call needs (0 if none).  op = IG_OP_REHEARSE: B, H, D,
  * r used.  IG_OP_SELECT: B, H, n, max_out used.  IG_OP_ATTN: B, H, d,
- * max_out used.  IG_OP_SPECULATE: B, H, D, r, n used.  Unused arguments are
- * ignored.
+ * max_out used.  IG_OP_SPECULATE: B, H, D, r, n used.  IG_OP_TOUCH: B, H,
+ * max_out used.  Unused arguments are ignored.
  */
 size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int max_out);
 
@@ -225,12 +225,14 @@ int ig_sparse_decode_attn(const void* q, const void* K, const void* V, int ld_ro
  * lowest index among the minima of C[b][0..n).  counters [B][n_cap] uint32,
  * updated in place; precondition C[b][j] < cmax for j < n.  Indices of one
  * head must be distinct; values outside [0, n) are ignored.  cmax >= 2,
- * H <= 1024.  One workgroup per sequence, so calls for different sequences
- * never touch the same counters.
+ * H <= 1024.  When H * max_out <= 32768 one workgroup per sequence does the
+ * whole update (workspace unused, may be NULL); otherwise three launches
+ * (zero the per-sequence flags, increments over (b, h, chunk) workgroups,
+ * per-sequence finish) with IG_OP_TOUCH workspace bytes.
  */
 int ig_pool_touch(uint32_t* counters, const int32_t* idx, const int32_t* count,
                   int B, int H, int n, int n_cap, int max_out, uint32_t cmax,
-                  int32_t* victim, hipStream_t stream);
+                  int32_t* victim, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Build rows [row0, row1) of the partial key cache from the skewed key cache

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libig.so")
 IG_OK, IG_EINVAL, IG_EHIP, IG_EUNSUPPORTED = 0, 1, 2, 3
 IG_F32, IG_BF16 = 0, 1
 IG_SEL_THRESHOLD, IG_SEL_TOPK, IG_SEL_HEADAVG = 0, 1, 2
-IG_OP_REHEARSE, IG_OP_SELECT, IG_OP_ATTN, IG_OP_SPECULATE = 0, 1, 2, 3
+IG_OP_REHEARSE, IG_OP_SELECT, IG_OP_ATTN, IG_OP_SPECULATE, IG_OP_TOUCH = 0, 1, 2, 3, 4
 
 _MODES = {"threshold": IG_SEL_THRESHOLD, "topk": IG_SEL_TOPK, "headavg": IG_SEL_HEADAVG}
 
@@ -53,7 +53,7 @@ _SIGS = {
     "ig_select": (_i, [_vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "ig_gather_kv": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "ig_sparse_decode_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
-    "ig_pool_touch": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _u32, _vp, _vp]),
+    "ig_pool_touch": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _u32, _vp, _vp, _sz, _vp]),
     "ig_build_partial_cache": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "ig_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
 }
@@ -288,14 +288,15 @@ def ig_sparse_decode_attn(q, K, V, idx, count, scale: float, *, max_out=None, ou
     return out, lse
 
 
-def ig_pool_touch(counters, idx, count, n: int, cmax: int, *, victim=None, want_victim=False, stream=None):
+def ig_pool_touch(counters, idx, count, n: int, cmax: int, *, victim=None, want_victim=False, ws=None, stream=None):
     torch = _torch()
     B, n_cap = counters.shape
     H, max_out = idx.shape[1], idx.shape[2]
     if victim is None and want_victim:
         victim = torch.empty((B,), dtype=torch.int32, device=counters.device)
+    ws, wsb = _ws(ws, ig_workspace_size(IG_OP_TOUCH, B, H, 0, 0, 0, n, max_out), counters.device)
     _check(load().ig_pool_touch(_ptr(counters), _ptr(idx), _ptr(count), B, H, n, n_cap, max_out, int(cmax),
-                                _ptr(victim), _stream(stream)), "ig_pool_touch")
+                                _ptr(victim), _ptr(ws), wsb, _stream(stream)), "ig_pool_touch")
     return counters, victim
 
 

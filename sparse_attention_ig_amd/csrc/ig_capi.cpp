@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 1; }
+int ig_version(void) { return 2; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 
@@ -88,6 +88,9 @@ size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int m
         case IG_OP_ATTN:
             if (d < 1 || max_out < 1) return 0;
             return plan_attn(B, H, d, max_out).ws_bytes;
+        case IG_OP_TOUCH:
+            if (max_out < 1) return 0;
+            return touch_single_kernel(H, max_out) ? 0 : touch_ws_bytes(B);
         case IG_OP_SPECULATE:
             if (D < 1 || r < 1 || n < 1) return 0;
             return speculate_ws_bytes(B, H, D, r, n, IG_BF16);
@@ -206,13 +209,16 @@ int ig_sparse_decode_attn(const void* q, const void* K, const void* V, int ld_ro
 }
 
 int ig_pool_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n, int n_cap,
-                  int max_out, uint32_t cmax, int32_t* victim, hipStream_t stream) {
+                  int max_out, uint32_t cmax, int32_t* victim, void* ws, size_t ws_bytes, hipStream_t stream) {
     IG_REQUIRE(counters && idx && count, "ig_pool_touch: NULL required pointer");
     IG_REQUIRE(B >= 1 && H >= 1 && n >= 1 && n <= n_cap && max_out >= 1,
                "ig_pool_touch: bad sizes (B=%d H=%d n=%d n_cap=%d max_out=%d)", B, H, n, n_cap, max_out);
     IG_REQUIRE(cmax >= 2, "ig_pool_touch: cmax must be >= 2");
     IG_REQUIRE(H <= 1024, "ig_pool_touch: at most 1024 heads");
-    return hip_status(launch_touch(counters, idx, count, B, H, n, n_cap, max_out, cmax, victim, stream),
+    if (!touch_single_kernel(H, max_out))
+        IG_REQUIRE(ws && ws_bytes >= touch_ws_bytes(B) && aligned16(ws),
+                   "ig_pool_touch: workspace of %zu bytes needed (16-byte aligned)", touch_ws_bytes(B));
+    return hip_status(launch_touch(counters, idx, count, B, H, n, n_cap, max_out, cmax, victim, ws, stream),
                       "ig_pool_touch");
 }
 

@@ -61,7 +61,9 @@ int launch_attn(const void* q, const void* K, const void* V, int ld_rows, const 
 int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_t* count, int B, int H,
                   int d, int n_cap, int max_out, int dtype, void* Kc, void* Vc, hipStream_t s);
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n,
-                 int n_cap, int max_out, uint32_t cmax, int32_t* victim, hipStream_t s);
+                 int n_cap, int max_out, uint32_t cmax, int32_t* victim, void* ws, hipStream_t s);
+size_t touch_ws_bytes(int B);
+bool touch_single_kernel(int H, int max_out);
 int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H,
                      int r, int n, int n_cap, int dtype, float scale, int mode, float alpha, int k, int max_sel,
                      int32_t* idx, int32_t* count, int max_out, uint32_t* counters, uint32_t cmax, int32_t* victim,

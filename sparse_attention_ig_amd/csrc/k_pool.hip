@@ -64,10 +64,54 @@ __global__ __launch_bounds__(kTouchThreads) void k_touch(uint32_t* __restrict__ 
     if (victim && tid == 0) victim[b] = v;
 }
 
+// Large selections: the increments spread over (b, h, chunk) workgroups; a slot that saturates sets
+// its sequence's flag (zeroed first); a per-sequence finish halves if flagged and picks the victim.
+__global__ __launch_bounds__(256) void k_touch_inc(uint32_t* __restrict__ C, const int32_t* __restrict__ idx,
+                                                  const int32_t* __restrict__ count, int H, int n, int n_cap,
+                                                  int max_out, uint32_t cmax, uint32_t* __restrict__ flags) {
+    const int bh = blockIdx.y, b = bh / H;
+    const int c = min(count[bh], max_out);
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < c) {
+        const int j = idx[static_cast<size_t>(bh) * max_out + i];
+        if (j >= 0 && j < n) {
+            const uint32_t old = atomicAdd(&C[static_cast<size_t>(b) * n_cap + j], 1u);
+            if (old + 1u >= cmax) flags[b] = 1u;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kTouchThreads) void k_touch_finish(uint32_t* __restrict__ C, int n, int n_cap,
+                                                               uint32_t cmax, const uint32_t* __restrict__ flags,
+                                                               int32_t* __restrict__ victim) {
+    __shared__ uint32_t s_val[kTouchThreads / kWave];
+    __shared__ int s_idx[kTouchThreads / kWave];
+    const int b = blockIdx.x;
+    const bool halve = flags[b] != 0u;
+    const int v = pool_finish<kTouchThreads>(C + static_cast<size_t>(b) * n_cap, n, cmax, halve, victim != nullptr,
+                                              s_val, s_idx);
+    if (victim && threadIdx.x == 0) victim[b] = v;
+}
+
+size_t touch_ws_bytes(int B) { return ((static_cast<size_t>(B) * sizeof(uint32_t) + 255) / 256) * 256; }
+
+bool touch_single_kernel(int H, int max_out) { return static_cast<int64_t>(H) * max_out <= 32768; }
+
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n, int n_cap,
-                 int max_out, uint32_t cmax, int32_t* victim, hipStream_t s) {
-    hipLaunchKernelGGL(k_touch, dim3(B), dim3(kTouchThreads), 0, s, counters, idx, count, H, n, n_cap, max_out, cmax,
-                       victim);
+                 int max_out, uint32_t cmax, int32_t* victim, void* ws, hipStream_t s) {
+    if (touch_single_kernel(H, max_out)) {
+        hipLaunchKernelGGL(k_touch, dim3(B), dim3(kTouchThreads), 0, s, counters, idx, count, H, n, n_cap, max_out,
+                           cmax, victim);
+        return static_cast<int>(hipGetLastError());
+    }
+    uint32_t* flags = static_cast<uint32_t*>(ws);
+    int e = launch_zero(flags, static_cast<size_t>(B) * sizeof(uint32_t), s);
+    if (e) return e;
+    hipLaunchKernelGGL(k_touch_inc, dim3((max_out + 255) / 256, B * H), dim3(256), 0, s, counters, idx, count, H, n,
+                       n_cap, max_out, cmax, flags);
+    e = static_cast<int>(hipGetLastError());
+    if (e) return e;
+    hipLaunchKernelGGL(k_touch_finish, dim3(B), dim3(kTouchThreads), 0, s, counters, n, n_cap, cmax, flags, victim);
     return static_cast<int>(hipGetLastError());
 }
 

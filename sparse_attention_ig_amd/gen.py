@@ -328,3 +328,26 @@ def drift(spec: Spec, x_bits: np.ndarray, layer: int, std: float, purpose_key: i
     g = _rng(spec, layer, _P_DRIFT, purpose_key)
     x = values(x_bits, spec.dtype) + g.standard_normal(x_bits.shape) * std
     return encode(x.astype(np.float32), spec.dtype)
+
+
+# ---------------------------------------------------------------- multi-layer decode pipeline
+PIPE_LAYER_STD = 0.395   # x_{l+1} = x_l + N(0, 0.395^2): cosine ~0.93 between consecutive layer inputs
+PIPE_STEP_STD = 0.14     # x_0(t) = x_0(t-1) + N(0, 0.14^2): cosine ~0.99 between consecutive steps
+
+
+def pipeline_x(spec: Spec, layers: int, steps: int) -> np.ndarray:
+    """Attention inputs x_l(t) [steps][layers][B][D] (stored dtype) of a decode pipeline.
+
+    Stand-in for the residual stream: the first layer's input drifts slowly from step to step and
+    each layer adds an independent perturbation to the previous layer's input, so consecutive layers
+    see similar inputs (the summary's Table 1 reports cosine 0.89-0.97 between consecutive block
+    inputs; 0.395 per layer gives about 0.93 for unit-variance channels)."""
+    out = np.empty((steps, layers, spec.B, spec.D), dtype=np.float32 if spec.dtype == "f32" else np.uint16)
+    x0 = draw_x(spec, 0)
+    for t in range(steps):
+        if t > 0:
+            x0 = drift(spec, x0, 0, PIPE_STEP_STD, purpose_key=100000 + t)
+        out[t, 0] = x0
+        for l in range(1, layers):
+            out[t, l] = drift(spec, out[t, l - 1], l, PIPE_LAYER_STD, purpose_key=t)
+    return out

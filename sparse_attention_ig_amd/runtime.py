@@ -108,7 +108,9 @@ class DeviceLayer:
         self.victim = torch.empty((s.B,), dtype=torch.int32, device=dv)
         nb = max(L.ig_workspace_size(L.IG_OP_REHEARSE, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out),
                  L.ig_workspace_size(L.IG_OP_SELECT, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out),
-                 L.ig_workspace_size(L.IG_OP_ATTN, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out), 16)
+                 L.ig_workspace_size(L.IG_OP_ATTN, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out),
+                 L.ig_workspace_size(L.IG_OP_ATTN, s.B, s.H, s.D, s.d, s.r, s.cap, s.cap),
+                 L.ig_workspace_size(L.IG_OP_TOUCH, s.B, s.H, s.D, s.d, s.r, s.cap, self.max_out), 16)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dv)
         # the fused speculation keeps its arrival words in its own workspace, zero between calls
         self.ws_spec = L.ig_workspace_init(torch.empty(
@@ -165,10 +167,93 @@ class DeviceLayer:
                                stream=stream)
             elif part == "touch":
                 L.ig_pool_touch(self.counters, idx, self.count, n, cmax,
-                                victim=self.victim if want_victim else None, stream=stream)
+                                victim=self.victim if want_victim else None, ws=self.ws, stream=stream)
             else:
                 raise ValueError(part)
             if part in ev:
                 ev[part][1].record(stream)
         return dict(q_part=self.q_part, scores=self.scores, idx=idx, count=self.count, out=self.out, lse=self.lse,
                     counters=self.counters, victim=self.victim if want_victim else None)
+
+
+class MappedHost:
+    """Device-side view of a pinned host tensor: the address kernels must use, from
+    hipHostGetDevicePointer (fails cleanly if the memory is not pinned and mapped), with the shape and
+    dtype the binding reads."""
+
+    _hip = None
+
+    def __init__(self, t):
+        import ctypes
+        if not t.is_pinned():
+            raise ValueError("tensor is not in pinned host memory")
+        if MappedHost._hip is None:
+            MappedHost._hip = ctypes.CDLL("libamdhip64.so")
+        dptr = ctypes.c_void_p()
+        err = MappedHost._hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+        if err != 0 or not dptr.value:
+            raise RuntimeError(f"hipHostGetDevicePointer failed ({err}): host pool not mapped into the device")
+        self._t = t
+        self._dptr = dptr.value
+        self.shape, self.dtype = t.shape, t.dtype
+
+    def data_ptr(self) -> int:
+        return self._dptr
+
+    def is_contiguous(self) -> bool:
+        return self._t.is_contiguous()
+
+
+class PoolLayer:
+    """A layer whose full key / value cache lives in pinned host memory (the KV pool), with the partial
+    key cache, weights, query and counters in HBM.  The selected rows are fetched over the host link by
+    ig_gather_kv (zero-copy reads of the pinned pool) into compact HBM buffers, and the attention runs on
+    those (the summary's section 3.2 Pool Manager and section 3.4 "Decoding Stage" step 5)."""
+
+    def __init__(self, host: HostLayer, max_out: int):
+        import torch
+        from . import _lib as L
+        s = host.spec
+        self.spec = s
+        self.max_out = max_out
+        self.Kh_host = torch.from_numpy(host.K.view(np.int16)).view(torch.bfloat16).pin_memory()
+        self.Vh_host = torch.from_numpy(host.V.view(np.int16)).view(torch.bfloat16).pin_memory()
+        self.Kh, self.Vh = MappedHost(self.Kh_host), MappedHost(self.Vh_host)
+        self.x = to_device(host.x)
+        self.Wq_part = to_device(host.Wq_part)
+        self.chan = to_device(host.chan)
+        self.q = to_device(host.q)
+        dv = "cuda"
+        self.Kp = torch.zeros((s.B, s.H, s.cap, s.r), dtype=torch.bfloat16, device=dv)
+        L.ig_build_partial_cache(self.Kh, self.chan, self.Kp, 0, s.n)   # reads the pinned pool directly
+        self.counters = torch.zeros((s.B, s.cap), dtype=torch.int32, device=dv)
+        self.idx = torch.empty((s.B, s.H, max_out), dtype=torch.int32, device=dv)
+        self.count = torch.empty((s.B, s.H), dtype=torch.int32, device=dv)
+        self.victim = torch.empty((s.B,), dtype=torch.int32, device=dv)
+        self.Kc = torch.empty((s.B, s.H, max_out, s.d), dtype=torch.bfloat16, device=dv)
+        self.Vc = torch.empty_like(self.Kc)
+        self.out = torch.empty((s.B, s.H, s.d), dtype=torch.float32, device=dv)
+        self.lse = torch.empty((s.B, s.H), dtype=torch.float32, device=dv)
+        self.ws_spec = L.ig_workspace_init(torch.empty(
+            L.ig_workspace_size(L.IG_OP_SPECULATE, s.B, s.H, s.D, s.d, s.r, s.cap, max_out),
+            dtype=torch.uint8, device=dv))
+        self.ws = torch.empty(max(L.ig_workspace_size(L.IG_OP_ATTN, s.B, s.H, s.D, s.d, s.r, s.cap, max_out), 16),
+                              dtype=torch.uint8, device=dv)
+
+    def speculate(self, *, alpha: float, max_sel: int, cmax: int = 65535, n: Optional[int] = None,
+                  want_victim: bool = False, stream=None):
+        from . import _lib as L
+        s = self.spec
+        L.ig_speculate(self.x, self.Wq_part, self.Kp, s.n if n is None else n, s.softmax_scale, "threshold",
+                       self.max_out, alpha=alpha, max_sel=max_sel, idx=self.idx, count=self.count,
+                       counters=self.counters, cmax=cmax, victim=self.victim if want_victim else None,
+                       ws=self.ws_spec, stream=stream)
+
+    def gather(self, stream=None):
+        from . import _lib as L
+        L.ig_gather_kv(self.Kh, self.Vh, self.idx, self.count, Kc=self.Kc, Vc=self.Vc, stream=stream)
+
+    def attend(self, stream=None):
+        from . import _lib as L
+        L.ig_sparse_decode_attn(self.q, self.Kc, self.Vc, None, self.count, self.spec.softmax_scale,
+                                max_out=self.max_out, out=self.out, lse=self.lse, ws=self.ws, stream=stream)

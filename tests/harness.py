@@ -146,3 +146,52 @@ def compare_sets(gpu_sel: np.ndarray, ref_sel: np.ndarray, ref_scores: np.ndarra
     band = set(int(v) for v in band_rows(ref_scores, cut))
     ok = (g - band) == (r - band)
     return ok, g == r, band
+
+
+# ---------------------------------------------------------------- multi-layer pipeline
+def pipeline_setup(spec: gen.Spec, layers: int, steps: int, route):
+    """Per-layer inputs through ``route`` (lib_inputs or oracle_inputs) from the shared pipeline draws:
+    x_l(0) drives each layer's own query, x_l(t) drives the speculation for layer l+1."""
+    xs = gen.pipeline_x(spec, layers, steps)
+    ins = [route(spec, l, lay=gen.draw_layer(spec, l, x_bits=xs[0, l], with_wk=False)) for l in range(layers)]
+    new = [[gen.draw_new_rows(spec, l, t) for l in range(layers)] for t in range(steps)]
+    return xs, ins, new
+
+
+def oracle_pipeline(spec: gen.Spec, xs, ins, new, max_out: int, cmax: int = 65535):
+    """The oracle's decode loop: per step, per layer l, attention over idx_l (layer 0 dense), then the
+    speculation for layer l+1 from x_l; after the last layer every layer appends the new token."""
+    from oracle import oracle as O
+    dt = spec.dtype
+    L = len(ins)
+    K = [i.K.copy() for i in ins]
+    V = [i.V.copy() for i in ins]
+    Kp = [O.partial_key_cache(i.K, i.chan) for i in ins]
+    C = [np.zeros((spec.B, spec.cap), np.uint32) for _ in ins]
+    idx = [None] * L
+    cnt = [None] * L
+    n = spec.n
+    trace = []
+    for t in range(xs.shape[0]):
+        rec = {"n": n, "out": [], "idx": [None] * L, "count": [None] * L, "scores": [None] * L}
+        k = min(max_out, int(math.ceil(0.05 * n)))
+        for l in range(L):
+            q = O.decode(ins[l].q, dt)
+            if l == 0:
+                o, _ = O.dense_decode_attn(q, O.decode(K[l], dt), O.decode(V[l], dt), n, spec.softmax_scale)
+            else:
+                o, _ = O.sparse_decode_attn(q, O.decode(K[l], dt), O.decode(V[l], dt), idx[l], cnt[l],
+                                            spec.softmax_scale)
+            rec["out"].append(o)
+            if l + 1 < L:
+                _, sc = O.rehearse(O.decode(xs[t, l], dt), O.decode(ins[l + 1].Wq_part, dt),
+                                   O.decode(Kp[l + 1], dt), n, spec.H, spec.r, spec.softmax_scale)
+                idx[l + 1], cnt[l + 1] = O.select(sc, "topk", k=k, max_out=max_out)
+                C[l + 1], _ = O.pool_touch(C[l + 1], idx[l + 1], cnt[l + 1], n, cmax)
+                rec["idx"][l + 1], rec["count"][l + 1], rec["scores"][l + 1] = idx[l + 1], cnt[l + 1], sc
+        for l in range(L):
+            kn, vn = new[t][l]
+            _, n2 = O.pool_append(K[l], V[l], Kp[l], C[l], ins[l].chan, kn, vn, n)
+        n = n2
+        trace.append(rec)
+    return trace, C

@@ -215,13 +215,14 @@ def test_gather_and_partial_cache_bit_exact():
     assert np.array_equal(host(Kp), O.partial_key_cache(K, chan))
 
 
-@pytest.mark.parametrize("cmax", [15, 65535])
-def test_pool_touch_bit_exact(cmax):
+@pytest.mark.parametrize("cmax,H,max_out", [(15, 8, 400), (65535, 8, 400), (15, 64, 1000), (65535, 64, 1000)])
+def test_pool_touch_bit_exact(cmax, H, max_out):
+    """Single-workgroup path (H * max_out <= 32768) and the three-launch path for large selections."""
     from sparse_attention_ig_amd import _lib as L
-    spec = _spec(gen.opt_6_7b(n=3000, B=3), H=8)
-    say(f"[touch] cmax={cmax}")
+    spec = _spec(gen.opt_6_7b(n=3000, B=3), H=H)
+    say(f"[touch] cmax={cmax} H={H} max_out={max_out}")
     C = gen.draw_counters(spec, cmax)
-    idx, cnt = gen.draw_index_sets(spec, 400)
+    idx, cnt = gen.draw_index_sets(spec, max_out)
     Cd = dev(C)
     rC = C
     for step in range(3):
@@ -355,3 +356,25 @@ def test_graph_replay_matches_eager():
         for key in ("scores", "count", "out", "lse", "counters"):
             assert np.array_equal(got[key].view(np.uint8), eager[key].view(np.uint8)), (rep, key)
         assert np.array_equal(got["idx"], eager["idx"]), rep
+
+
+def test_long_context_32k_fused_sampled():
+    """Llama-2-7B-shaped layer at 32768 rows (the fused path's LDS limit), batch 4, top 4%: sampled
+    heads' selection and attention against the oracle, every head's counters summed."""
+    spec = gen.llama2_7b_long(n=32768, B=4, frac=0.04)
+    say(f"[long 32k fused] n={spec.n} k={spec.topk}")
+    li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
+    assert harness.compare_inputs(li, oi)["chan"] == 0
+    layer = DeviceLayer(li, max_out=spec.topk)
+    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, parts=DeviceLayer.FUSED))
+    say("[long 32k fused] gpu step done")
+    heads = [(0, 0), (1, 17), (3, 31)]
+    ref = harness.oracle_step(oi, mode="topk", k=spec.topk, max_out=spec.topk, heads=heads)
+    for (b, h), r in ref.items():
+        assert harness.score_error(g["scores"][b, h, :spec.n], r["scores"]) <= harness.SCORE_RTOL
+        gs = g["idx"][b, h, :g["count"][b, h]]
+        ok, exact, band = harness.compare_sets(gs, r["idx"], r["scores"], "topk", 0.0)
+        assert ok and g["count"][b, h] == len(r["idx"])
+        if exact:
+            assert np.abs(g["out"][b, h] - r["out"]).max() <= harness.ATTN_TOL["bf16"]
+    assert int(g["counters"].sum()) == spec.B * spec.H * spec.topk

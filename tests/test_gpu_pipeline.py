@@ -1,0 +1,69 @@
+"""GPU parity of the cross-layer decode pipeline (speculation for layer l+1 at layer l, layer 0
+dense, one appended token per step) against the oracle running the same loop on its own inputs."""
+import math
+
+import numpy as np
+import pytest
+
+from sparse_attention_ig_amd import gen
+from tests import harness
+from tests.gpu_util import host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec():
+    base = gen.llama2_13b(n=300, B=2, n_cap=306)
+    return gen.Spec(**{**base.__dict__, "H": 8, "heavy": 6})
+
+
+def test_pipeline_matches_oracle():
+    import torch
+    from sparse_attention_ig_amd.pipeline import DecodePipeline
+    from sparse_attention_ig_amd.runtime import to_device
+    spec = _spec()
+    layers, steps = 3, 5
+    max_out = int(math.ceil(0.05 * spec.cap))
+    say(f"[pipeline] layers={layers} steps={steps} B={spec.B} H={spec.H} n0={spec.n} cap={spec.cap} k<= {max_out}")
+    xs, lib_in, new = harness.pipeline_setup(spec, layers, steps, harness.lib_inputs)
+    _, ora_in, _ = harness.pipeline_setup(spec, layers, steps, harness.oracle_inputs)
+    for a, b in zip(lib_in, ora_in):
+        assert harness.compare_inputs(a, b)["chan"] == 0
+    pipe = DecodePipeline(lib_in, max_out=max_out)
+    trace, C_ref = harness.oracle_pipeline(spec, xs, ora_in, new, max_out)
+    exact_hist = np.ones((layers, spec.B), bool)
+    tol = harness.ATTN_TOL["bf16"]
+    for t in range(steps):
+        xd = [to_device(xs[t, l]) for l in range(layers)]
+        kn = [to_device(new[t][l][0]) for l in range(layers)]
+        vn = [to_device(new[t][l][1]) for l in range(layers)]
+        n = pipe.n
+        assert n == trace[t]["n"]
+        pipe.step(xd, kn, vn)
+        torch.cuda.synchronize()
+        say(f"[pipeline] step {t} n={n} done")
+        for l in range(layers):
+            out = host(pipe.layers[l].out)
+            if l == 0:
+                assert np.abs(out - trace[t]["out"][0]).max() <= tol
+                continue
+            gi, gc = host(pipe.layers[l].idx), host(pipe.layers[l].count)
+            ri, rc = trace[t]["idx"][l], trace[t]["count"][l]
+            for b in range(spec.B):
+                for h in range(spec.H):
+                    gs, rs = gi[b, h, :gc[b, h]], ri[b, h, :rc[b, h]]
+                    ok, exact, band = harness.compare_sets(gs, rs, trace[t]["scores"][l][b, h], "topk", 0.0)
+                    assert ok, (t, l, b, h)
+                    if exact:
+                        assert np.abs(out[b, h] - trace[t]["out"][l][b, h]).max() <= tol, (t, l, b, h)
+                    else:
+                        exact_hist[l, b] = False
+    for l in range(1, layers):
+        C = host(pipe.layers[l].counters).view(np.uint32)
+        for b in range(spec.B):
+            if exact_hist[l, b]:
+                assert np.array_equal(C[b], C_ref[l][b]), (l, b)
+    assert pipe.n == spec.n + steps
+    # the appended rows landed in the caches
+    K = host(pipe.layers[1].K)
+    assert np.array_equal(K[:, :, spec.n], new[0][1][0])

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(L.exported_symbols())
     for name in declared:
         assert hasattr(lib, name)
-    assert L.ig_version() == 1
+    assert L.ig_version() == 2
 
 
 @pytest.mark.parametrize("m,d", [(256, 64), (128, 128), (64, 16)])
@@ -123,8 +123,10 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     assert lib.ig_sparse_decode_attn(ctypes.c_void_p(18), p, p, 8, None, p, 1, 1, 128, 4, L.IG_BF16, f(1.0), p, None,
                                      None, 0, None) == L.IG_EINVAL
     # cmax < 2, n > n_cap
-    assert lib.ig_pool_touch(p, p, p, 1, 1, 4, 4, 4, 1, None, None) == L.IG_EINVAL
-    assert lib.ig_pool_touch(p, p, p, 1, 1, 5, 4, 4, 15, None, None) == L.IG_EINVAL
+    assert lib.ig_pool_touch(p, p, p, 1, 1, 4, 4, 4, 1, None, None, 0, None) == L.IG_EINVAL
+    assert lib.ig_pool_touch(p, p, p, 1, 1, 5, 4, 4, 15, None, None, 0, None) == L.IG_EINVAL
+    # a large selection needs the flag workspace
+    assert lib.ig_pool_touch(p, p, p, 1, 64, 5000, 5000, 1000, 15, None, None, 0, None) == L.IG_EINVAL
     # full pool without a victim
     assert lib.ig_append_kv(p, p, p, p, p, p, p, None, 1, 1, 64, 8, 4, 4, L.IG_BF16, None, None) == L.IG_EINVAL
     # fused speculation: rows beyond the LDS capacity, or the head-average mode, are unsupported
