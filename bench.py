@@ -17,6 +17,7 @@ a bounded sample of the same workload on the host's cores.
 from __future__ import annotations
 
 import argparse
+import faulthandler
 import json
 import math
 import os
@@ -57,6 +58,9 @@ def main() -> int:
     ap.add_argument("--mode", choices=["topk", "threshold"], default="topk")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: ig_speculate + ig_sparse_decode_attn; unfused: the six-call path")
+    ap.add_argument("--schedule", choices=["overlap", "serial"], default="serial",
+                    help="overlap: layer l's attention runs beside the speculation of layer l+1 (two streams, "
+                         "the decode dependencies kept); serial: one stream, call after call")
     ap.add_argument("--workload", choices=["opt-6.7b", "llama2-7b-long", "llama2-13b-pipeline", "opt-30b-pool"],
                     default="opt-6.7b",
                     help="opt-6.7b: the headline layer; the others are extra measurements")
@@ -66,6 +70,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    faulthandler.enable()   # a fatal signal prints the Python stack of every thread
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path has no multi-GPU "
@@ -110,7 +115,40 @@ def main() -> int:
     footprint = sum(l.nbytes() for l in layers)
     PARTS = DeviceLayer.FUSED if args.path == "fused" else DeviceLayer.PARTS
 
+    spec_parts = tuple(p for p in PARTS if p != "attn")
+    s_spec, s_attn = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    ev_spec = [torch.cuda.Event() for _ in layers]
+    ev_attn = [torch.cuda.Event() for _ in layers]
+
+    def run_overlap():
+        """Decode dependencies across layers: the speculation of layer l reads the attention input of
+        layer l-1, which exists once layer l-2's attention is done; layer l's attention needs its own
+        selection and layer l-1's output.  So the speculation of layer l+1 runs beside layer l's
+        attention, on a second stream."""
+        cur = torch.cuda.current_stream()
+        s_spec.wait_stream(cur)
+        s_attn.wait_stream(cur)
+        L = len(layers)
+
+        def spec(i):
+            if i >= 2:
+                s_spec.wait_event(ev_attn[i - 2])
+            layers[i].step(**step_kw, parts=spec_parts, stream=s_spec)
+            ev_spec[i].record(s_spec)
+
+        spec(0)
+        for i in range(L):
+            if i + 1 < L:
+                spec(i + 1)
+            s_attn.wait_event(ev_spec[i])
+            layers[i].step(**step_kw, parts=("attn",), stream=s_attn)
+            ev_attn[i].record(s_attn)
+        cur.wait_stream(s_spec)
+        cur.wait_stream(s_attn)
+
     def run(parts=PARTS):
+        if parts == PARTS and args.schedule == "overlap":
+            return run_overlap()
         # stream=None: torch's current stream, which is the capture stream inside a graph capture
         for l in layers:
             l.step(**step_kw, parts=parts)
@@ -185,7 +223,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": f"synthetic (seeded {spec.name}-shaped draws, no weights or datasets)",
         "config": {"workload": wl, "layers_per_step": args.layers, "footprint_GB": round(footprint / 1e9, 2),
-                   "mean_selected_per_head": round(c_mean, 1), "path": args.path,
+                   "mean_selected_per_head": round(c_mean, 1), "path": args.path, "schedule": args.schedule,
                    "calls_per_layer": list(PARTS)},
         "t_layer_us": round(t_layer_s * 1e6, 3),
         "step_alg_bytes_per_layer": int(step_bytes),

@@ -30,7 +30,8 @@
  *    a power of two <= 32 (r in {8, 16, 32, 64, 128, 256} for bf16,
  *    {8, 16, 32, 64, 128} for f32); d / (16 / sizeof(element)) a power of two
  *    between 4 and 32 (d in {32, 64, 128, 256} for bf16, {16, 32, 64, 128} for
- *    f32); n <= n_cap.
+ *    f32); D a multiple of 16 / sizeof(element) for the speculation calls;
+ *    n <= n_cap.
  */
 #ifndef IG_H_
 #define IG_H_
@@ -50,7 +51,8 @@ enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* ig_last_error(void);
-/* ABI version: bumped on any signature change (2: ig_pool_touch takes a workspace). */
+/* ABI version: bumped on any signature or layout change (2: ig_pool_touch takes a
+ * workspace; 3: Wq_part is stored one row per partial column, [H*r][D]). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -104,10 +106,11 @@ int ig_store(const double* vals, int64_t count, int dtype, void* out);
  * Weight Index Generation", steps 2-3).  Per head h, channel score
  *   score[c] = sum_i |Wq_s[i][h*d+c]| + sum_{b, j<n} |K_s[b][h][j][c]|
  * (float64 sums of the stored values); chan[h] = the r highest-scoring
- * channels (ties: lower channel), ascending.  Wq_part[i][h*r+k] =
- * Wq_s[i][h*d + chan[h][k]] (a copy of the stored elements).
+ * channels (ties: lower channel), ascending.  Wq_part[h*r+k][i] =
+ * Wq_s[i][h*d + chan[h][k]] (a copy of the stored elements, one row of D
+ * inputs per partial column: the transpose of the column selection).
  * Host pointers: Wq_s [D][H*d] dtype; K_s [B][H][n_cap][d] dtype (rows < n
- * used); chan [H][r] int32 out; Wq_part [D][H*r] dtype out.
+ * used); chan [H][r] int32 out; Wq_part [H*r][D] dtype out.
  */
 int ig_partial_weight_index(const void* Wq_s, int D, int H, int d, int r,
                             const void* K_s, int B, int n_cap, int n, int dtype,
@@ -132,10 +135,11 @@ int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Speculation for the next layer (section 3.4, "Decoding Stage", steps 1-2):
- *   q_part[b][h][c]  = sum_i x[b][i] Wq_part[i][h*r+c] (+ bq_part[h*r+c])
+ *   q_part[b][h][c]  = sum_i x[b][i] Wq_part[h*r+c][i] (+ bq_part[h*r+c])
  *   scores[b][h][j]  = scale * sum_c q_part[b][h][c] Kp[b][h][j][c],  j < n
- * x [B][D] dtype (this layer's attention input); Wq_part [D][H*r] dtype (the
- * next layer's partial query weight); bq_part [H*r] float or NULL;
+ * x [B][D] dtype (this layer's attention input); Wq_part [H*r][D] dtype (the
+ * next layer's partial query weight, one row per partial column, as
+ * ig_partial_weight_index writes it); bq_part [H*r] float or NULL;
  * Kp [B][H][n_cap][r] dtype (the next layer's partial key cache);
  * q_part [B][H][r] float out; scores [B][H][ld] float out (ld >= n; columns
  * >= n untouched).  scale: the softmax scale of the attention (e.g. 1/sqrt(d)).

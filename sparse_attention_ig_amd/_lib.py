@@ -187,7 +187,7 @@ def ig_partial_weight_index(Wq_s: np.ndarray, K_s: np.ndarray, r: int, n: int, d
     B, H, n_cap, d = K_s.shape
     D = Wq_s.shape[0]
     chan = np.empty((H, r), dtype=np.int32)
-    Wp = np.empty((D, H * r), dtype=Wq_s.dtype)
+    Wp = np.empty((H * r, D), dtype=Wq_s.dtype)   # one row of D inputs per partial column
     _check(load().ig_partial_weight_index(_ptr(Wq_s), D, H, d, r, _ptr(K_s), B, n_cap, n, _np_dtype(dtype),
                                           _ptr(chan), _ptr(Wp), int(nthreads)), "ig_partial_weight_index")
     return chan, Wp

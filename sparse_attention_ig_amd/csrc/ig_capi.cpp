@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 2; }
+int ig_version(void) { return 3; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 
@@ -109,7 +109,8 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
     IG_REQUIRE(r % 8 == 0 && pow2(r / (16 / elem_size(dtype))) && r / (16 / elem_size(dtype)) <= 32,
                "ig_rehearse: r / (16 / element size) must be a power of two <= 32 (got r=%d)", r);
     IG_REQUIRE(std::isfinite(scale), "ig_rehearse: scale must be finite");
-    IG_REQUIRE(aligned16(Wq_part) && aligned16(Kp), "ig_rehearse: Wq_part and Kp must be 16-byte aligned");
+    IG_REQUIRE(aligned16(x) && aligned16(Wq_part) && aligned16(Kp), "ig_rehearse: x, Wq_part and Kp must be 16-byte aligned");
+    IG_REQUIRE(D % (16 / elem_size(dtype)) == 0, "ig_rehearse: D must be a multiple of 16 / element size (got D=%d)", D);
     const RehearsePlan p = plan_rehearse(B, H, D, r, n, dtype);
     IG_REQUIRE(ws && ws_bytes >= p.ws_bytes, "ig_rehearse: workspace of %zu bytes needed (got %zu)", p.ws_bytes,
                ws ? ws_bytes : static_cast<size_t>(0));
@@ -137,7 +138,8 @@ int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const
                "ig_speculate: r / (16 / element size) must be a power of two <= 32 (got r=%d)", r);
     IG_REQUIRE(!scores || ld >= n, "ig_speculate: ld must be >= n when scores are written");
     IG_REQUIRE(std::isfinite(scale), "ig_speculate: scale must be finite");
-    IG_REQUIRE(aligned16(Wq_part) && aligned16(Kp), "ig_speculate: Wq_part and Kp must be 16-byte aligned");
+    IG_REQUIRE(aligned16(x) && aligned16(Wq_part) && aligned16(Kp), "ig_speculate: x, Wq_part and Kp must be 16-byte aligned");
+    IG_REQUIRE(D % (16 / elem_size(dtype)) == 0, "ig_speculate: D must be a multiple of 16 / element size (got D=%d)", D);
     if (mode == IG_SEL_THRESHOLD)
         IG_REQUIRE(alpha >= 0.f && !std::isnan(alpha) && max_sel >= 0, "ig_speculate: alpha must be >= 0");
     else if (mode == IG_SEL_TOPK)

@@ -48,32 +48,76 @@ __device__ __forceinline__ void store_raw16(void* p, uint4 v) { *reinterpret_cas
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
 
-// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane of
-// the group gets the group total.
+// Cross-lane moves through DPP (data-parallel primitives: a VALU operand modifier, no LDS round
+// trip).  GFX9 control codes: quad permutations, shifts within a 16-lane row, mirrors, and the row
+// broadcasts used by wave scans.  Lanes without a source (or in rows left out by row_mask) read 0.
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15 - i of its row
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7 - i of its half row
+constexpr int kDppRowShr = 0x110;     // + k: lane i <- lane i - k of its row
+constexpr int kDppBcast15 = 0x142;    // row r <- lane 15 of row r - 1
+constexpr int kDppBcast31 = 0x143;    // rows 2, 3 <- lane 31
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+
+// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane of the group gets the
+// group total, the same value in every lane (each step adds two partial sums that the partner lane
+// adds in the other order).
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, kWave);
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group of 1, 2, 4, .., 64 lanes");
+    if constexpr (G >= 2) v += dpp_f32<kDppQuadXor1>(v);
+    if constexpr (G >= 4) v += dpp_f32<kDppQuadXor2>(v);
+    if constexpr (G >= 8) v += dpp_f32<kDppHalfMirror>(v);   // the other quad of the half row
+    if constexpr (G >= 16) v += dpp_f32<kDppRowMirror>(v);   // the other half of the row
+    if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
+    if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+// Inclusive prefix sum over the 64 lanes (lane i gets v_0 + .. + v_i): scans within each 16-lane row
+// by shifts of 1, 2, 4, 8, then the row totals are carried into the rows above by two broadcasts.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += dpp_i32<kDppRowShr + 1>(v);
+    v += dpp_i32<kDppRowShr + 2>(v);
+    v += dpp_i32<kDppRowShr + 4>(v);
+    v += dpp_i32<kDppRowShr + 8>(v);
+    v += dpp_i32<kDppBcast15, 0xA>(v);
+    v += dpp_i32<kDppBcast31, 0xC>(v);
     return v;
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        uint32_t o = __shfl_xor(v, m, kWave);
-        v = o > v ? o : v;
-    }
-    return v;
-}
+
+__device__ __forceinline__ int read_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// Wave-wide reductions with a wave-uniform result: DPP within each 16-lane row, then the four row
+// results read into scalar registers.
 __device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_i32<kDppQuadXor1>(v);
+    v += dpp_i32<kDppQuadXor2>(v);
+    v += dpp_i32<kDppHalfMirror>(v);
+    v += dpp_i32<kDppRowMirror>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max_u32(v, static_cast<uint32_t>(dpp_i32<kDppQuadXor1>(static_cast<int>(v))));
+    v = max_u32(v, static_cast<uint32_t>(dpp_i32<kDppQuadXor2>(static_cast<int>(v))));
+    v = max_u32(v, static_cast<uint32_t>(dpp_i32<kDppHalfMirror>(static_cast<int>(v))));
+    v = max_u32(v, static_cast<uint32_t>(dpp_i32<kDppRowMirror>(static_cast<int>(v))));
+    const int vi = static_cast<int>(v);
+    return max_u32(max_u32(static_cast<uint32_t>(__builtin_amdgcn_readlane(vi, 0)),
+                           static_cast<uint32_t>(__builtin_amdgcn_readlane(vi, 16))),
+                   max_u32(static_cast<uint32_t>(__builtin_amdgcn_readlane(vi, 32)),
+                           static_cast<uint32_t>(__builtin_amdgcn_readlane(vi, 48))));
 }
 
 // Order-preserving map float -> uint32 (larger float -> larger key); -0 maps

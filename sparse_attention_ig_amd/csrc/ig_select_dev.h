@@ -228,3 +228,146 @@ __device__ int ordered_compact(const float* __restrict__ srow, const uint32_t* l
 }
 
 }  // namespace ig
+
+namespace ig {
+
+// ------------------------------------------------------------------ rows held in LDS
+// One 256-bin histogram per radix pass, three of them in rotation: pass p adds into buffer p % 3 and,
+// after its barrier, clears buffer (p + 2) % 3 (last read in pass p - 1), so a pass needs a single
+// barrier and every wave derives the digit on its own.  The histogram words are free after the
+// select and stage the selected indices (kFastStage of them).
+constexpr int kFastStage = 4096;
+
+struct FastSel {
+    uint32_t words[kFastStage];  // hist[3][256] during the select, then staging
+    int wtot[kSelWaves];
+    __device__ uint32_t* hist(int i) { return words + 256 * i; }
+    __device__ uint32_t* stage() { return words; }
+};
+
+// Clears histograms 0 and 1; a barrier must follow before radix_kth_lds.
+__device__ __forceinline__ void fast_sel_init(FastSel& fs) {
+    if (threadIdx.x < 512) fs.words[threadIdx.x] = 0u;
+}
+
+// Exact kk-th largest key T of lk[0..n) (1 <= kk <= n, 1024 threads; fast_sel_init and a barrier
+// before).  Selecting every key above T and the first *need_eq keys equal to T gives the top kk;
+// *eq_total keys equal T.  When a digit's whole bin belongs to the top kk the search stops early: T
+// is then the bin's lowest key value (its low bits zero) and every key >= T is selected
+// (*need_eq == *eq_total).  Ends after a barrier.
+//
+// Per pass: LDS atomics into the histogram (in the first pass, where a row's keys crowd into the few
+// bins of their sign and exponent bits and same-address atomics serialise, the bin of the wave's
+// first active lane is counted with one ballot and a single atomic), one barrier, then every wave
+// finds the digit on its own: lane L holds bins 255-4L .. 252-4L, a DPP prefix sum over the lanes
+// gives the keys above each bin, and the lane holding the bin where the count reaches rem
+// broadcasts it.
+__device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, uint32_t* T_out,
+                                              int* need_eq_out, int* eq_total_out) {
+    const int tid = threadIdx.x, lane = tid % kWave;
+    uint32_t prefix = 0, pmask = 0;
+    int rem = kk, dcount = 0;
+    for (int pass = 0, shift = 24; shift >= 0; ++pass, shift -= 8) {
+        uint32_t* h = fs.hist(pass % 3);
+        for (int j0 = 0; j0 < n; j0 += kSelThreads) {
+            const int j = j0 + tid;
+            const uint32_t key = j < n ? lk[j] : 0u;
+            const uint32_t bin = (key >> shift) & 255u;
+            bool on = j < n && (key & pmask) == prefix;
+            if (pass == 0) {
+                const uint64_t act = __ballot(on);
+                if (act != 0) {
+                    const int leader = __ffsll(static_cast<unsigned long long>(act)) - 1;
+                    const uint32_t b0 = static_cast<uint32_t>(read_lane(static_cast<int>(bin), leader));
+                    const uint64_t m = __ballot(on && bin == b0);
+                    if (lane == leader) atomicAdd(&h[b0], static_cast<uint32_t>(__popcll(m)));
+                    on = on && bin != b0;
+                }
+            }
+            if (on) atomicAdd(&h[bin], 1u);
+        }
+        __syncthreads();
+        if (tid < 256) fs.hist((pass + 2) % 3)[tid] = 0u;
+        const uint4 c4 = *reinterpret_cast<const uint4*>(h + 252 - 4 * lane);
+        const int c[4] = {static_cast<int>(c4.w), static_cast<int>(c4.z), static_cast<int>(c4.y),
+                          static_cast<int>(c4.x)};  // bins 255-4L, 254-4L, 253-4L, 252-4L
+        const int s = c[0] + c[1] + c[2] + c[3];
+        int cum = wave_incl_scan(s) - s;  // keys in the bins above 255-4L
+        int digit = -1, above = 0, cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (digit < 0 && cum < rem && cum + c[q] >= rem) {
+                digit = 255 - 4 * lane - q;
+                above = cum;
+                cnt = c[q];
+            }
+            cum += c[q];
+        }
+        const uint64_t found = __ballot(digit >= 0);
+        const int src = found ? __ffsll(static_cast<unsigned long long>(found)) - 1 : 0;
+        digit = read_lane(digit, src) & 255;
+        above = read_lane(above, src);
+        dcount = read_lane(cnt, src);
+        rem -= above;
+        prefix |= static_cast<uint32_t>(digit) << shift;
+        pmask |= 255u << shift;
+        if (dcount == rem) break;  // the whole bin is taken
+    }
+    *T_out = prefix;
+    *need_eq_out = rem;
+    *eq_total_out = dcount;
+}
+
+// Ordered compaction of lk[0..n): the rows with key > T and the first need_eq rows with key == T (every
+// row >= T when need_eq >= eq_total), ascending.  Each wave owns a contiguous chunk of whole 64-row
+// groups: it counts its rows with ballots, one barrier shares the per-wave counts, and a second pass
+// writes out[pos] = j and calls visit(pos, j).  Returns the number selected (block-uniform).  lk is
+// read by other waves while visit runs, so a visitor must not write lk.
+template <typename Visit>
+__device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, int eq_total,
+                           int32_t* __restrict__ out, int max_out, FastSel& fs, Visit visit) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const bool all_eq = need_eq >= eq_total;
+    const int chunk = (n + kSelThreads - 1) / kSelThreads * kWave;
+    const int lo = min(n, wave * chunk), hi = min(n, lo + chunk);
+    int n_gt = 0, n_eq = 0;
+    for (int j0 = lo; j0 < hi; j0 += kWave) {
+        const int j = j0 + lane;
+        const uint32_t key = j < hi ? lk[j] : 0u;
+        n_gt += __popcll(__ballot(j < hi && key > T));
+        n_eq += __popcll(__ballot(j < hi && key == T));
+    }
+    // per-wave counts packed as gt | eq << 16 (each <= n <= 32768), prefix-summed over the waves
+    if (lane == 0) fs.wtot[wave] = n_gt | (n_eq << 16);
+    __syncthreads();
+    const int incl = wave_incl_scan(lane < kSelWaves ? fs.wtot[lane] : 0);
+    const int before = wave > 0 ? read_lane(incl, wave - 1) : 0;
+    const int total = read_lane(incl, kSelWaves - 1);
+    int eq_before = before >> 16;
+    const int gt_tot = total & 0xFFFF, eq_tot = total >> 16;
+    const int take = all_eq ? eq_tot : min(eq_tot, need_eq);
+    int pos = (before & 0xFFFF) + min(eq_before, take);
+    const uint64_t lt = lanemask_lt();
+    for (int j0 = lo; j0 < hi; j0 += kWave) {
+        const int j = j0 + lane;
+        const uint32_t key = j < hi ? lk[j] : 0u;
+        const bool gt = j < hi && key > T;
+        const bool eq = j < hi && key == T;
+        bool sel = gt || eq;
+        if (!all_eq) {
+            const uint64_t me = __ballot(eq);
+            sel = gt || (eq && eq_before + __popcll(me & lt) < need_eq);
+            eq_before += __popcll(me);
+        }
+        const uint64_t ms = __ballot(sel);
+        const int p = pos + __popcll(ms & lt);
+        if (sel && p < max_out) {
+            out[p] = j;
+            visit(p, j);
+        }
+        pos += __popcll(ms);
+    }
+    return gt_tot + take;
+}
+
+}  // namespace ig

@@ -222,11 +222,14 @@ int partial_weight_index(const void* Wq_s, int D, int H, int d, int r, const voi
     const size_t esz = dtype == IG_F32 ? 4 : 2;
     const char* src = static_cast<const char*>(Wq_s);
     char* dst = static_cast<char*>(Wq_part);
-    const int64_t pcol = static_cast<int64_t>(H) * r;
-    for (int64_t i = 0; i < D; ++i)
-        for (int h = 0; h < H; ++h)
-            for (int k = 0; k < r; ++k)
-                std::memcpy(dst + (i * pcol + h * r + k) * esz, src + (i * ncol + h * d + chan[h * r + k]) * esz, esz);
+    // one row of D inputs per partial column (h, k): the layout the projection's matrix-core operands
+    // read with 16-byte loads along the reduction
+    for (int h = 0; h < H; ++h)
+        for (int k = 0; k < r; ++k) {
+            char* row = dst + (static_cast<int64_t>(h) * r + k) * D * esz;
+            const int64_t c = static_cast<int64_t>(h) * d + chan[h * r + k];
+            for (int64_t i = 0; i < D; ++i) std::memcpy(row + i * esz, src + (i * ncol + c) * esz, esz);
+        }
     return ok();
 }
 

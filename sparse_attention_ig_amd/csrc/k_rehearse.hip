@@ -2,13 +2,12 @@
 // section 3.4 "Decoding Stage", step 1 partial query projection and step 2
 // speculated attention scores).
 //
-// k_rehearse_proj: q_part = x W~_Q^partial.  M = B is tiny, so this is a
-//   bandwidth-bound pass over the [D][H*r] weight: each 256-thread workgroup
-//   owns a 64-column tile and a slice of the D rows; every lane streams 16-byte
-//   rows of its 8 (bf16) or 4 (f32) columns and multiplies them with x from LDS
-//   for up to 16 batch rows at once.  Partial sums of the D slices go to the
-//   workspace in a fixed order (no float atomics), so results are
-//   deterministic.
+// k_rehearse_proj: q_part = x W~_Q^partial, a dense contraction with M = B
+//   batch rows, run on the matrix cores: the partial weight is stored with one
+//   row of D inputs per partial column, so both MFMA operands come straight
+//   from HBM as 16-byte loads along k.  Workgroups split the D reduction;
+//   partial sums go to the workspace in a fixed order (no float atomics), so
+//   results are deterministic.
 // k_rehearse_score: one workgroup per (b, h, row chunk).  It sums the D-slice
 //   partials of its (b, h) (and the bias), then streams its chunk of the
 //   partial key cache Kp[b][h][j][0..r) with coalesced 16-byte loads, LPR lanes
@@ -22,87 +21,69 @@ constexpr int kProjThreads = 256;
 constexpr int kScoreThreads = 256;
 constexpr int kScoreUnroll = 4;
 
-template <typename T, int BB>
-__global__ __launch_bounds__(kProjThreads) void k_rehearse_proj(
-    const T* __restrict__ x, const T* __restrict__ W, int B, int D, int N, int rows_per_split,
-    float* __restrict__ part) {
-    constexpr int VEC = Vec<T>::N;
-    constexpr int CPT = 64 / VEC;            // lanes across the 64-column tile
-    constexpr int RSUB = kProjThreads / CPT; // rows in flight per workgroup step
-    extern __shared__ __align__(16) float smem[];  // x slice [BB][rows_per_split], later the reduction buffer
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-    const int tid = threadIdx.x;
-    const int cg = tid % CPT, rs = tid / CPT;
-    const int col = blockIdx.x * 64 + cg * VEC;
-    const int k0 = blockIdx.y * rows_per_split;
-    const int kn = min(rows_per_split, D - k0);
-    const int b0 = blockIdx.z * BB;
-
-    // every weight row of this lane is put in flight before anything waits (one HBM round trip);
-    // rows_per_split <= 256, so a lane owns at most 256 / RSUB rows
-    constexpr int UMAX = 256 / RSUB;
-    uint4 w[UMAX];
-    const bool col_ok = col < N;
-    const T* wp = W + static_cast<size_t>(k0) * N + col;
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-        const int kk = rs + u * RSUB;
-        w[u] = (col_ok && kk < kn) ? load_raw16(wp + static_cast<size_t>(kk) * N) : make_uint4(0, 0, 0, 0);
+// One 16x16 MFMA step per element type.  Operand lane layout (16x16xK): lane l supplies row l % 16
+// of A (here x: one batch row) and column l % 16 of B (one partial-weight column), each with E
+// consecutive k values of k-group l / 16; the 16x16 float result puts rows 4 (l / 16) .. + 3 of
+// column l % 16 in lane l.  Only the pairing of A's and B's k values matters for the sum, and both
+// operands use the same one.
+template <typename T> struct ProjMma;
+template <> struct ProjMma<uint16_t> {
+    static constexpr int K = 32, E = 8, CHUNK = 8;  // k per step, elements per lane, steps in flight
+    using vec = uint4;
+    static __device__ __forceinline__ vec load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+    static __device__ __forceinline__ vec zero() { return make_uint4(0, 0, 0, 0); }
+    static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     }
-    // x slice [BB][rows_per_split] into LDS; all of a lane's loads are issued before any store
-    {
-        constexpr int UX = (16 * 256 + kProjThreads - 1) / kProjThreads;  // BB <= 16, rows_per_split <= 256
-        float xv[UX];
+};
+template <> struct ProjMma<float> {
+    static constexpr int K = 4, E = 1, CHUNK = 16;
+    using vec = float;
+    static __device__ __forceinline__ vec load(const float* p) { return *p; }
+    static __device__ __forceinline__ vec zero() { return 0.f; }
+    static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// part[s][b][c] = sum over k in split s of x[b][k] * WT[c][k].  Workgroup (64-column tile, D split,
+// 16-row batch block); each wave owns 16 columns.  Every load of a chunk is issued before the first
+// MFMA (one memory round trip per chunk; a split of 256 bf16 rows is one chunk).
+template <typename T>
+__global__ __launch_bounds__(kProjThreads) void k_rehearse_proj(const T* __restrict__ x, const T* __restrict__ WT,
+                                                               int B, int D, int N, int ks,
+                                                               float* __restrict__ part) {
+    using M = ProjMma<T>;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int col = blockIdx.x * 64 + wave * 16 + lane % 16;
+    const int kg = lane / 16;
+    const int b = blockIdx.z * 16 + lane % 16;
+    const int k0 = blockIdx.y * ks, k1 = min(D, k0 + ks);
+    const bool col_ok = col < N, b_ok = b < B;
+    const T* wrow = WT + static_cast<size_t>(col_ok ? col : 0) * D;
+    const T* xrow = x + static_cast<size_t>(b_ok ? b : 0) * D;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kc = k0; kc < k1; kc += M::CHUNK * M::K) {
+        typename M::vec w[M::CHUNK], xv[M::CHUNK];
 #pragma unroll
-        for (int u = 0; u < UX; ++u) {
-            const int i = tid + u * kProjThreads;
-            const int bb = i / rows_per_split, kk = i - bb * rows_per_split;
-            xv[u] = (i < BB * rows_per_split && b0 + bb < B && kk < kn)
-                        ? to_f32(x[static_cast<size_t>(b0 + bb) * D + k0 + kk]) : 0.f;
+        for (int u = 0; u < M::CHUNK; ++u) {
+            const int k = kc + u * M::K + kg * M::E;  // D % E == 0, so a group is wholly in or out
+            const bool in = k < k1;
+            w[u] = (col_ok && in) ? M::load(wrow + k) : M::zero();
+            xv[u] = (b_ok && in) ? M::load(xrow + k) : M::zero();
         }
 #pragma unroll
-        for (int u = 0; u < UX; ++u) {
-            const int i = tid + u * kProjThreads;
-            if (i < BB * rows_per_split) smem[i] = xv[u];
-        }
+        for (int u = 0; u < M::CHUNK; ++u) acc = M::mma(xv[u], w[u], acc);
     }
-    __syncthreads();
-
-    float acc[BB][VEC];
+    if (!col_ok) return;
 #pragma unroll
-    for (int bb = 0; bb < BB; ++bb)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[bb][v] = 0.f;
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-        const int kk = rs + u * RSUB;
-        if (kk < kn) {
-            float wv[VEC];
-            unpack_raw(w[u], wv);
-#pragma unroll
-            for (int bb = 0; bb < BB; ++bb) {
-                const float xv = smem[bb * rows_per_split + kk];
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[bb][v] = fmaf(xv, wv[v], acc[bb][v]);
-            }
-        }
-    }
-    // reduction over the RSUB row groups through LDS (cross-lane shuffles of 64 values per lane cost
-    // more than the whole weight stream): red[rs][bb][64 columns], then each output sums RSUB terms
-    __syncthreads();  // x slice no longer needed
-    float* red = smem;
-#pragma unroll
-    for (int bb = 0; bb < BB; ++bb)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) red[(rs * BB + bb) * 64 + cg * VEC + v] = acc[bb][v];
-    __syncthreads();
-    for (int i = tid; i < BB * 64; i += kProjThreads) {
-        const int bb = i / 64, c = i % 64;
-        float s = 0.f;
-#pragma unroll 8
-        for (int g = 0; g < RSUB; ++g) s += red[(g * BB + bb) * 64 + c];
-        const int b = b0 + bb, cc = blockIdx.x * 64 + c;
-        if (b < B && cc < N) part[(static_cast<size_t>(blockIdx.y) * B + b) * N + cc] = s;
+    for (int q = 0; q < 4; ++q) {
+        const int bb = blockIdx.z * 16 + 4 * kg + q;
+        if (bb < B) part[(static_cast<size_t>(blockIdx.y) * B + bb) * N + col] = acc[q];
     }
 }
 
@@ -155,22 +136,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_rehearse_score(
 }
 
 RehearsePlan plan_rehearse(int B, int H, int D, int r, int n, int dtype) {
-    (void)dtype;
+    (void)dtype;  // the same split for both element types, so the workspace size is dtype-free
     RehearsePlan p{};
     const int N = H * r;
     p.tiles = (N + 63) / 64;
-    int bb = 1;
-    while (bb < B && bb < 16) bb <<= 1;
-    p.bb = bb;
-    p.bblocks = (B + bb - 1) / bb;
-    // aim for ~256 workgroups over the weight; D slices are multiples of 32 rows, at most 256
-    int splits = (256 + p.tiles * p.bblocks - 1) / (p.tiles * p.bblocks);
-    splits = std::max(1, std::min(splits, (D + 31) / 32));
-    int rps = (D + splits - 1) / splits;
-    rps = ((rps + 31) / 32) * 32;
-    if (rps > 256) rps = 256;
-    p.rows_per_split = rps;
-    p.splits = (D + rps - 1) / rps;
+    p.bb = 16;
+    p.bblocks = (B + 15) / 16;
+    // D splits of 256 rows (512 when that leaves more than 1024 workgroups)
+    int ks = 256;
+    if (static_cast<int64_t>(p.tiles) * p.bblocks * ((D + 255) / 256) > 1024) ks = 512;
+    p.rows_per_split = ks;
+    p.splits = (D + ks - 1) / ks;
     p.ws_bytes = static_cast<size_t>(p.splits) * B * N * sizeof(float);
     // score chunks: ~1024 workgroups over B*H*n rows, 256..4096 rows each
     const int64_t rows = static_cast<int64_t>(n) * B * H;
@@ -182,34 +158,11 @@ RehearsePlan plan_rehearse(int B, int H, int D, int r, int n, int dtype) {
     return p;
 }
 
-template <typename T, int BB>
-static int launch_proj_bb(dim3 grid, size_t smem, hipStream_t s, const T* x, const T* W, int B, int D, int N, int rps,
-                          float* part) {
-    static bool attr_set = false;  // dynamic LDS above 64 KB needs the per-function limit raised once
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rehearse_proj<T, BB>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return static_cast<int>(e);
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((k_rehearse_proj<T, BB>), grid, dim3(kProjThreads), smem, s, x, W, B, D, N, rps, part);
-    return static_cast<int>(hipGetLastError());
-}
-
 template <typename T>
 static int launch_proj_t(const T* x, const T* W, int B, int D, int N, const RehearsePlan& p, float* part,
                          hipStream_t s) {
-    dim3 grid(p.tiles, p.splits, p.bblocks);
-    // x slice [bb][rows_per_split], then the reduction buffer [row groups][bb][64]
-    const int rsub = kProjThreads / (64 / Vec<T>::N);
-    const size_t smem = static_cast<size_t>(p.bb) * std::max(p.rows_per_split, rsub * 64) * sizeof(float);
-    switch (p.bb) {
-        case 1: return launch_proj_bb<T, 1>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
-        case 2: return launch_proj_bb<T, 2>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
-        case 4: return launch_proj_bb<T, 4>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
-        case 8: return launch_proj_bb<T, 8>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
-        default: return launch_proj_bb<T, 16>(grid, smem, s, x, W, B, D, N, p.rows_per_split, part);
-    }
+    hipLaunchKernelGGL(k_rehearse_proj<T>, dim3(p.tiles, p.splits, p.bblocks), dim3(kProjThreads), 0, s, x, W, B, D,
+                       N, p.rows_per_split, part);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -14,6 +14,8 @@
 //    exclusive scan of per-thread counts (wave shuffles + per-wave totals in
 //    LDS) gives each selected row its output slot, so idx comes out ascending
 //    without any sort and the result is deterministic.
+#include <type_traits>
+
 #include "ig_internal.h"
 #include "ig_select_dev.h"
 
@@ -25,9 +27,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     int32_t* __restrict__ idx, int32_t* __restrict__ count, int max_out, int32_t* __restrict__ head_counts) {
     __shared__ __align__(16) uint32_t lk[IN_LDS ? kSelLdsKeys : 1];
     __shared__ SelScratch sh;
+    __shared__ std::conditional_t<IN_LDS, FastSel, int> fs;
     const int bh = blockIdx.x, tid = threadIdx.x;
     const float* srow = scores + static_cast<size_t>(bh) * ld;
 
+    if constexpr (IN_LDS) fast_sel_init(fs);  // published by the barriers of block_max_u32
     uint32_t kmax = 0;
     for_each_key<false>(srow, nullptr, n, [&](int j, uint32_t key) {
         if (IN_LDS) lk[j] = key;
@@ -50,9 +54,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         }
         if (max_sel > 0) limit = min(limit, max_sel);
         if (cnt <= limit) {
-            const int w = ordered_compact<IN_LDS>(srow, lk, n, kc, INT_MAX,
-                                                  idx + static_cast<size_t>(bh) * max_out, max_out, sh);
-            if (tid == 0) count[bh] = w;
+            int w;
+            if constexpr (IN_LDS)
+                w = compact_lds(lk, n, kc, INT_MAX, INT_MAX, idx + static_cast<size_t>(bh) * max_out, max_out, fs,
+                                NoVisit());
+            else
+                w = ordered_compact<IN_LDS>(srow, lk, n, kc, INT_MAX, idx + static_cast<size_t>(bh) * max_out,
+                                            max_out, sh);
+            if (tid == 0) count[bh] = min(w, max_out);
             return;
         }
         kk = limit;
@@ -68,11 +77,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         kk = min(k, limit);
     }
     uint32_t T;
-    int need_eq;
-    radix_kth<IN_LDS>(srow, lk, n, kk, sh, &T, &need_eq);
-    const int w = ordered_compact<IN_LDS>(srow, lk, n, T, need_eq, idx + static_cast<size_t>(bh) * max_out,
-                                          max_out, sh);
-    if (tid == 0) count[bh] = w;
+    int need_eq, w;
+    if constexpr (IN_LDS) {
+        int eq_total;
+        radix_kth_lds(lk, n, kk, fs, &T, &need_eq, &eq_total);
+        w = compact_lds(lk, n, T, need_eq, eq_total, idx + static_cast<size_t>(bh) * max_out, max_out, fs,
+                        NoVisit());
+    } else {
+        radix_kth<IN_LDS>(srow, lk, n, kk, sh, &T, &need_eq);
+        w = ordered_compact<IN_LDS>(srow, lk, n, T, need_eq, idx + static_cast<size_t>(bh) * max_out, max_out, sh);
+    }
+    if (tid == 0) count[bh] = min(w, max_out);
 }
 
 size_t select_ws_bytes(int B, int H, int n, int max_out) {

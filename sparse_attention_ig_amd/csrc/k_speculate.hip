@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kSpecThreads) void k_speculate(SpecParams p) {
     constexpr int STEP = RPP * kSpecBatch;     // rows per batch
     extern __shared__ __align__(16) uint32_t keys[];  // n order-preserving score keys
     __shared__ SelScratch sh;
+    __shared__ FastSel fs;
     __shared__ float s_q[R];
     __shared__ int s_last;
 
@@ -77,6 +78,8 @@ __global__ __launch_bounds__(kSpecThreads) void k_speculate(SpecParams p) {
     }
     const int bh = b * p.H + h, n = p.n;
     const T* kp = static_cast<const T*>(p.Kp) + static_cast<size_t>(bh) * p.n_cap * R + li * VEC;
+
+    fast_sel_init(fs);  // the barriers of the partial-query sum below publish the cleared histograms
 
     // 1. partial query of this (b, h): sum of the projection kernel's D-slice partials (fixed order),
     //    then the first partial-key batch goes in flight
@@ -127,10 +130,13 @@ __global__ __launch_bounds__(kSpecThreads) void k_speculate(SpecParams p) {
     }
     const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
 
-    // 3. selection; the compaction leaves the selected indices in keys[0..count)
+    // 3. selection; the compaction also stages the selected indices in LDS (the freed histograms)
     uint32_t* crow = p.counters ? p.counters + static_cast<size_t>(b) * p.n_cap : nullptr;
     const uint32_t cmax = p.cmax;
-    auto keep = [&](int pos, int j) { keys[pos] = static_cast<uint32_t>(j); };
+    uint32_t* stage = fs.stage();
+    auto keep = [&](int pos, int j) {
+        if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(j);
+    };
     int32_t* out = p.idx + static_cast<size_t>(bh) * p.max_out;
     int limit = min(n, p.max_out);
     int written;
@@ -153,17 +159,23 @@ __global__ __launch_bounds__(kSpecThreads) void k_speculate(SpecParams p) {
     } else {
         kk = min(p.k, limit);
     }
-    if (!done) radix_kth<true>(nullptr, keys, n, kk, sh, &kth, &need_eq);
-    written = ordered_compact<true>(nullptr, keys, n, kth, need_eq, out, p.max_out, sh, keep);
-    if (tid == 0) p.count[bh] = written;
+    int eq_total = INT_MAX;
+    if (!done) radix_kth_lds(keys, n, kk, fs, &kth, &need_eq, &eq_total);
+    written = compact_lds(keys, n, kth, need_eq, eq_total, out, p.max_out, fs, keep);
+    if (tid == 0) p.count[bh] = min(written, p.max_out);
 
     // 4. counters: one integer atomic per selected slot, all in flight together; the last workgroup
     //    of sequence b halves (if any slot saturated) and picks the victim
     if (!crow) return;
     __syncthreads();
     int sat = 0;
-    for (int i = tid; i < written; i += kSpecThreads) {
-        const uint32_t old = atomicAdd(&crow[keys[i]], 1u);
+    // (written <= max_out and every staged index is < n by construction; both are re-checked so
+    // that no counter update can land outside the row)
+    const int touched = min(written, p.max_out);
+    for (int i = tid; i < touched; i += kSpecThreads) {
+        const uint32_t j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
+        if (j >= static_cast<uint32_t>(n)) continue;
+        const uint32_t old = atomicAdd(&crow[j], 1u);
         if (old + 1u >= cmax) sat = 1;
     }
     sat = __syncthreads_or(sat);

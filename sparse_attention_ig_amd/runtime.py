@@ -24,7 +24,7 @@ from . import gen
 class HostLayer:
     spec: gen.Spec
     x: np.ndarray          # [B][D] stored
-    Wq_part: np.ndarray    # [D][H*r] stored
+    Wq_part: np.ndarray    # [H*r][D] stored (one row per partial column)
     chan: np.ndarray       # [H][r] int32
     q: np.ndarray          # [B][H][d] stored (skewed full query)
     K: np.ndarray          # [B][H][n_cap][d] stored (skewed keys)

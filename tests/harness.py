@@ -61,7 +61,7 @@ def compare_inputs(a: Inputs, b: Inputs) -> Dict[str, int]:
     """Setup parity: bits of every derived input, and the channel sets."""
     return {
         "chan": int(np.count_nonzero(a.chan != b.chan)),
-        "Wq_part": ulp_mismatch(a.Wq_part, b.Wq_part),
+        "Wq_part": ulp_mismatch(a.Wq_part, np.ascontiguousarray(b.Wq_part.T)),  # library layout: [H*r][D]
         "q": ulp_mismatch(a.q, b.q),
         "K": ulp_mismatch(a.K, b.K),
         "V": ulp_mismatch(a.V, b.V),

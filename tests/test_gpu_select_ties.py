@@ -1,0 +1,120 @@
+"""GPU selection on rows full of equal scores, bit-exact against the oracle.
+
+Decoding stage steps 3-5 of the InfiniGen summary (arXiv 2406.19707, paper-graph-ui, section 3.4)
+pick rows by score; the top-k comparator (section 2, challenge C1) does the same with a fixed
+budget.  Equal scores are where an exact select can go wrong (the k-th value sits inside a run of
+equal keys), so these rows are built from a handful of distinct values:
+  * ig_select on integer-valued scores (exact in float32 and float64, so both sides see the same
+    order and the same threshold cut) for rows held in LDS and rows streamed from HBM;
+  * ig_speculate on a partial key cache whose rows repeat a few distinct vectors, so the score runs
+    are equal in float32 on the device and in float64 in the oracle.
+Index sets and counts must match exactly; no rows are excused.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from sparse_attention_ig_amd import gen
+from tests.gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_ig_amd import _lib as L
+    L.load()
+    yield
+
+
+def _rows(rng, B, H, n, kind):
+    if kind == "few":
+        s = rng.integers(-3, 3, (B, H, n)).astype(np.float32)
+    elif kind == "equal":
+        s = np.full((B, H, n), 2.0, dtype=np.float32)
+    elif kind == "signed-zero":
+        s = rng.choice(np.array([-0.0, 0.0, -1.0, 1.0], dtype=np.float32), (B, H, n))
+    else:  # "wide": many distinct integers, runs of equal ones still common
+        s = rng.integers(-500, 500, (B, H, n)).astype(np.float32)
+    return s
+
+
+SELECT_CASES = [
+    # n, kind, mode, kwargs, max_out
+    (1, "few", "topk", dict(k=1), 1),
+    (63, "few", "topk", dict(k=20), 20),
+    (1000, "few", "topk", dict(k=300), 300),
+    (1000, "equal", "topk", dict(k=77), 77),
+    (5000, "signed-zero", "topk", dict(k=1234), 1234),
+    (8192, "wide", "topk", dict(k=1638), 1638),
+    (8193, "few", "topk", dict(k=900), 900),          # beyond the LDS row limit: keys streamed from HBM
+    (20000, "wide", "topk", dict(k=4000), 4000),
+    (1000, "few", "threshold", dict(alpha=2.0, max_sel=200), 200),      # cap cuts into a run of equal scores
+    (1000, "few", "threshold", dict(alpha=1.0), 1000),                  # no cap: whole runs kept
+    (6000, "wide", "threshold", dict(alpha=40.0, max_sel=150), 150),
+    (12000, "few", "threshold", dict(alpha=0.0, max_sel=2400), 2400),   # alpha 0: the maximum's run only
+]
+
+
+@pytest.mark.parametrize("n,kind,mode,kw,max_out", SELECT_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}" for c in SELECT_CASES])
+def test_select_ties_exact(n, kind, mode, kw, max_out):
+    from sparse_attention_ig_amd import _lib as L
+    rng = np.random.default_rng(n + len(kind))
+    B, H = 2, 3
+    s = _rows(rng, B, H, n, kind)
+    say(f"[select ties] n={n} kind={kind} mode={mode} {kw}")
+    idx, cnt = L.ig_select(dev(s), mode, max_out, **kw)
+    idx, cnt = host(idx), host(cnt)
+    ridx, rcnt = O.select(s, mode, max_out=max_out, **kw)
+    assert np.array_equal(cnt, rcnt)
+    for b in range(B):
+        for h in range(H):
+            c = rcnt[b, h]
+            assert np.array_equal(idx[b, h, :c], ridx[b, h, :c]), (b, h)
+
+
+SPEC_CASES = [
+    # n, distinct rows, mode, kwargs, max_out
+    (2048, 5, "topk", dict(k=128), 128),
+    (2048, 3, "topk", dict(k=700), 700),
+    (3000, 4, "threshold", dict(alpha=1e9, max_sel=600), 600),    # every row passes; the cap decides
+    (9000, 6, "topk", dict(k=90), 90),
+    (32768, 7, "topk", dict(k=1310), 1310),
+]
+
+
+@pytest.mark.parametrize("n,distinct,mode,kw,max_out", SPEC_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}" for c in SPEC_CASES])
+def test_speculate_ties_exact(n, distinct, mode, kw, max_out):
+    from sparse_attention_ig_amd import _lib as L
+    rng = np.random.default_rng(7 * n + distinct)
+    B, H, r, D = 2, 4, 32, 256
+    x = gen.encode(rng.standard_normal((B, D)).astype(np.float32), "bf16")
+    W = gen.encode((rng.standard_normal((D, H * r)) / 16).astype(np.float32), "bf16")
+    base = gen.encode(rng.standard_normal((B, H, distinct, r)).astype(np.float32), "bf16")
+    pick = rng.integers(0, distinct, (B, H, n))
+    Kp = np.take_along_axis(base, pick[..., None].repeat(r, -1), axis=2)
+    Kp = np.ascontiguousarray(Kp)
+    scale = 1.0 / math.sqrt(128)
+    say(f"[speculate ties] n={n} distinct={distinct} mode={mode} {kw}")
+    # the library takes the partial weight one row per partial column
+    idx, cnt = L.ig_speculate(dev(x), dev(np.ascontiguousarray(W.T)), dev(Kp), n, scale, mode, max_out, **kw)
+    idx, cnt = host(idx), host(cnt)
+    _, sc = O.rehearse(O.decode(x, "bf16"), O.decode(W, "bf16"), O.decode(Kp, "bf16"), n, H, r, scale)
+    # the distinct score values of a row must be well apart for float32 and float64 to order them alike
+    for b in range(B):
+        for h in range(H):
+            u = np.unique(sc[b, h])
+            assert len(u) < 2 or np.diff(u).min() > 1e-4 * max(1.0, np.abs(u).max())
+    ridx, rcnt = O.select(sc, mode, max_out=max_out, **kw)
+    assert np.array_equal(cnt, rcnt)
+    for b in range(B):
+        for h in range(H):
+            c = rcnt[b, h]
+            assert np.array_equal(idx[b, h, :c], ridx[b, h, :c]), (b, h)
