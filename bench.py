@@ -46,6 +46,7 @@ def alg_bytes(spec, c: float) -> dict:
         "attn": B * H * c * 2 * d * s + B * H * d * s + B * H * d * 4,
     }
     parts["speculate"] = parts["rehearse"] + parts["select"] + parts["touch"]
+    parts["decode_layer"] = parts["speculate"] + parts["attn"]
     return parts
 
 
@@ -58,9 +59,10 @@ def main() -> int:
     ap.add_argument("--mode", choices=["topk", "threshold"], default="topk")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: ig_speculate + ig_sparse_decode_attn; unfused: the six-call path")
-    ap.add_argument("--schedule", choices=["overlap", "serial"], default="serial",
-                    help="overlap: layer l's attention runs beside the speculation of layer l+1 (two streams, "
-                         "the decode dependencies kept); serial: one stream, call after call")
+    ap.add_argument("--schedule", choices=["layer", "serial", "streams"], default="layer",
+                    help="layer (fused path): ig_decode_layer, layer l's attention beside the speculation for "
+                         "layer l+1 in one launch; serial: call after call on one stream; streams: the same "
+                         "overlap from two streams")
     ap.add_argument("--workload", choices=["opt-6.7b", "llama2-7b-long", "llama2-13b-pipeline", "opt-30b-pool"],
                     default="opt-6.7b",
                     help="opt-6.7b: the headline layer; the others are extra measurements")
@@ -80,7 +82,7 @@ def main() -> int:
     import numpy as np
     import torch
     from sparse_attention_ig_amd import _lib, gen
-    from sparse_attention_ig_amd.runtime import DeviceLayer, prepare_layer, to_host
+    from sparse_attention_ig_amd.runtime import DeviceLayer, decode_layer, prepare_layer, to_host
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
@@ -114,6 +116,8 @@ def main() -> int:
     torch.cuda.synchronize()
     footprint = sum(l.nbytes() for l in layers)
     PARTS = DeviceLayer.FUSED if args.path == "fused" else DeviceLayer.PARTS
+    if args.path != "fused" and args.schedule == "layer":
+        args.schedule = "serial"   # the fused decode layer needs the fused speculation
 
     spec_parts = tuple(p for p in PARTS if p != "attn")
     s_spec, s_attn = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
@@ -146,9 +150,19 @@ def main() -> int:
         cur.wait_stream(s_spec)
         cur.wait_stream(s_attn)
 
+    def run_layer():
+        """One launch per layer after the projection: layer l's attention beside the speculation for
+        layer l+1 (ig_decode_layer); the first layer's speculation and the last layer's attention are
+        the plain calls."""
+        layers[0].step(**step_kw, parts=("speculate",))
+        for i in range(len(layers)):
+            decode_layer(layers[i], layers[i + 1] if i + 1 < len(layers) else None, step_kw)
+
     def run(parts=PARTS):
-        if parts == PARTS and args.schedule == "overlap":
+        if parts == PARTS and args.schedule == "streams":
             return run_overlap()
+        if parts == PARTS and args.schedule == "layer":
+            return run_layer()
         # stream=None: torch's current stream, which is the capture stream inside a graph capture
         for l in layers:
             l.step(**step_kw, parts=parts)
@@ -199,6 +213,23 @@ def main() -> int:
         for _ in range(3):
             gp.replay()
         per_us[part] = 1e3 * timed_ms(gp.replay, args.steps) / (args.steps * args.layers)
+    if args.schedule == "layer":
+        # the fused call alone: attention of layer i beside the speculation for layer i+1, every layer
+        def run_fused_calls():
+            for i in range(len(layers)):
+                decode_layer(layers[i], layers[(i + 1) % len(layers)], step_kw)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_fused_calls()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gl = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gl):
+            run_fused_calls()
+        for _ in range(3):
+            gl.replay()
+        per_us["decode_layer"] = 1e3 * timed_ms(gl.replay, args.steps) / (args.steps * args.layers)
 
     res = to_host(layers[0].count)
     c_mean = float(res.mean())
@@ -224,7 +255,7 @@ def main() -> int:
         "data": f"synthetic (seeded {spec.name}-shaped draws, no weights or datasets)",
         "config": {"workload": wl, "layers_per_step": args.layers, "footprint_GB": round(footprint / 1e9, 2),
                    "mean_selected_per_head": round(c_mean, 1), "path": args.path, "schedule": args.schedule,
-                   "calls_per_layer": list(PARTS)},
+                   "calls_per_layer": ["decode_layer"] if args.schedule == "layer" else list(PARTS)},
         "t_layer_us": round(t_layer_s * 1e6, 3),
         "step_alg_bytes_per_layer": int(step_bytes),
         "step_hbm_GBs": round(step_bytes / t_layer_s / 1e9, 1),

@@ -52,7 +52,8 @@ enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3
 /* Message of the last failing call on this thread ("" if none). */
 const char* ig_last_error(void);
 /* ABI version: bumped on any signature or layout change (2: ig_pool_touch takes a
- * workspace; 3: Wq_part is stored one row per partial column, [H*r][D]). */
+ * workspace; 3: Wq_part is stored one row per partial column, [H*r][D];
+ * 4: ig_decode_layer). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -172,6 +173,64 @@ int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const
                  uint32_t* counters, uint32_t cmax, int32_t* victim,
                  float* q_part, float* scores, int ld,
                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One decode layer (section 3.2, "Big-Picture Architecture": the KV Selection
+ * Controller speculates layer i's tokens from layer i-1's attention input
+ * while layer i-1 computes; section 3.4, "Decoding Stage"): the attention of
+ * layer l over the rows selected for it, and the speculation for layer l+1.
+ * `attn` holds the arguments of ig_sparse_decode_attn for layer l, `spec` those
+ * of ig_speculate for layer l+1 (B, H, dtype shared; d is the attention's head
+ * dim); either may be NULL (then this is that one call).  With both: the
+ * projection of ig_speculate, then one launch in which the speculation's
+ * (b, h) workgroups and the attention's run side by side (no ordering between
+ * the two halves, so spec->idx, count, counters, victim, q_part, scores must not
+ * alias anything attn reads), then the split combine of the attention if it
+ * splits.  Results: those of the two calls (the attention's float sums may
+ * associate differently).  Falls back to the two calls in sequence for shapes
+ * outside the fused set (spec r / (16 / element size) in {2, 4, 8}, attn d /
+ * (16 / element size) in {8, 16, 32}, spec n <= 16384).
+ */
+typedef struct {
+    const void* q;
+    const void* K;
+    const void* V;
+    int ld_rows;
+    const int32_t* idx;
+    const int32_t* count;
+    int max_out;
+    float scale;
+    float* out;
+    float* lse;
+    void* ws;
+    size_t ws_bytes;
+} ig_attn_call;
+
+typedef struct {
+    const void* x;
+    const void* Wq_part;
+    const float* bq_part;
+    const void* Kp;
+    int D, r, n, n_cap;
+    float scale;
+    int mode;
+    float alpha;
+    int k, max_sel;
+    int32_t* idx;
+    int32_t* count;
+    int max_out;
+    uint32_t* counters;
+    uint32_t cmax;
+    int32_t* victim;
+    float* q_part;
+    float* scores;
+    int ld;
+    void* ws;
+    size_t ws_bytes;
+} ig_spec_call;
+
+int ig_decode_layer(int B, int H, int d, int dtype, const ig_attn_call* attn, const ig_spec_call* spec,
+                    hipStream_t stream);
 
 /*
  * Per-head token selection (section 3.4, "Decoding Stage", steps 3-5).

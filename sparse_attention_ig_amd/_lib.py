@@ -38,6 +38,20 @@ class SkewArgs(ctypes.Structure):
                 ("nthreads", _i)]
 
 
+class AttnCall(ctypes.Structure):
+    """ig_attn_call: the attention half of ig_decode_layer."""
+    _fields_ = [("q", _vp), ("K", _vp), ("V", _vp), ("ld_rows", _i), ("idx", _vp), ("count", _vp),
+                ("max_out", _i), ("scale", _f), ("out", _vp), ("lse", _vp), ("ws", _vp), ("ws_bytes", _sz)]
+
+
+class SpecCall(ctypes.Structure):
+    """ig_spec_call: the speculation half of ig_decode_layer."""
+    _fields_ = [("x", _vp), ("Wq_part", _vp), ("bq_part", _vp), ("Kp", _vp), ("D", _i), ("r", _i), ("n", _i),
+                ("n_cap", _i), ("scale", _f), ("mode", _i), ("alpha", _f), ("k", _i), ("max_sel", _i),
+                ("idx", _vp), ("count", _vp), ("max_out", _i), ("counters", _vp), ("cmax", _u32), ("victim", _vp),
+                ("q_part", _vp), ("scores", _vp), ("ld", _i), ("ws", _vp), ("ws_bytes", _sz)]
+
+
 _SIGS = {
     "ig_last_error": (ctypes.c_char_p, []),
     "ig_version": (_i, []),
@@ -54,6 +68,7 @@ _SIGS = {
     "ig_gather_kv": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "ig_sparse_decode_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "ig_pool_touch": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _u32, _vp, _vp, _sz, _vp]),
+    "ig_decode_layer": (_i, [_i, _i, _i, _i, ctypes.POINTER(AttnCall), ctypes.POINTER(SpecCall), _vp]),
     "ig_build_partial_cache": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "ig_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
 }
@@ -286,6 +301,43 @@ def ig_sparse_decode_attn(q, K, V, idx, count, scale: float, *, max_out=None, ou
                                         _dtype_of(q), float(scale), _ptr(out), _ptr(lse), _ptr(ws), wsb,
                                         _stream(stream)), "ig_sparse_decode_attn")
     return out, lse
+
+
+def ig_decode_layer(attn: Optional[dict] = None, spec: Optional[dict] = None, *, stream=None):
+    """Attention of layer l and speculation for layer l+1 in one fused launch (after the projection).
+
+    ``attn``: dict with q, K, V, idx, count, scale, out, and optionally lse, max_out, ws (the arguments
+    of ig_sparse_decode_attn).  ``spec``: dict with x, Wq_part, Kp, n, scale, mode, idx, count, ws and
+    optionally alpha, k, max_sel, bq_part, counters, cmax, victim, q_part, scores, ld (the arguments of
+    ig_speculate; ws zero-filled once).  Output tensors must be preallocated.  Either may be None."""
+    a_ref = s_ref = None
+    if attn is None and spec is None:
+        raise ValueError("nothing to do")
+    ref = attn["K"] if attn is not None else spec["Kp"]
+    B, H = ref.shape[0], ref.shape[1]
+    dtype = _dtype_of(ref)
+    d = attn["K"].shape[3] if attn is not None else 0
+    if attn is not None:
+        K = attn["K"]
+        idx = attn.get("idx")
+        max_out = attn.get("max_out") or (idx.shape[2] if idx is not None else K.shape[2])
+        ws = attn.get("ws")
+        a_ref = AttnCall(_ptr(attn["q"]), _ptr(K), _ptr(attn["V"]), K.shape[2], _ptr(idx), _ptr(attn["count"]),
+                         max_out, float(attn["scale"]), _ptr(attn["out"]), _ptr(attn.get("lse")), _ptr(ws),
+                         ws.numel() * ws.element_size() if ws is not None else 0)
+    if spec is not None:
+        x, Kp, ws = spec["x"], spec["Kp"], spec["ws"]
+        scores = spec.get("scores")
+        ld = spec.get("ld") or (scores.shape[2] if scores is not None else spec["n"])
+        s_ref = SpecCall(_ptr(x), _ptr(spec["Wq_part"]), _ptr(spec.get("bq_part")), _ptr(Kp), x.shape[1], Kp.shape[3],
+                         int(spec["n"]), Kp.shape[2], float(spec["scale"]), _MODES[spec["mode"]],
+                         float(spec.get("alpha", math.inf)), int(spec.get("k", 0)), int(spec.get("max_sel", 0)),
+                         _ptr(spec["idx"]), _ptr(spec["count"]), spec["idx"].shape[2], _ptr(spec.get("counters")),
+                         int(spec.get("cmax", 65535)), _ptr(spec.get("victim")), _ptr(spec.get("q_part")),
+                         _ptr(scores), ld, _ptr(ws), ws.numel() * ws.element_size())
+    _check(load().ig_decode_layer(B, H, d, dtype, ctypes.byref(a_ref) if a_ref is not None else None,
+                                  ctypes.byref(s_ref) if s_ref is not None else None, _stream(stream)),
+           "ig_decode_layer")
 
 
 def ig_pool_touch(counters, idx, count, n: int, cmax: int, *, victim=None, want_victim=False, ws=None, stream=None):

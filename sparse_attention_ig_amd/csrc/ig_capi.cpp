@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 3; }
+int ig_version(void) { return 4; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 
@@ -125,42 +125,47 @@ int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
     return hip_status(launch_zero(ws, ws_bytes, stream), "ig_workspace_init");
 }
 
+// Validation of a speculation call (ig_speculate, and the speculation half of ig_decode_layer).
+static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes) {
+    const int dtype = c.dtype, B = c.B, D = c.D, H = c.H, r = c.r, n = c.n, n_cap = c.n_cap, max_out = c.max_out;
+    IG_REQUIRE(dtype == IG_F32 || dtype == IG_BF16, "%s: unknown dtype %d", fn, dtype);
+    IG_REQUIRE(c.x && c.Wq_part && c.Kp && c.idx && c.count, "%s: NULL required pointer", fn);
+    IG_REQUIRE(B >= 1 && D >= 1 && H >= 1 && r >= 1 && n >= 1 && n <= n_cap && max_out >= 1,
+               "%s: bad sizes (B=%d D=%d H=%d r=%d n=%d n_cap=%d max_out=%d)", fn, B, D, H, r, n, n_cap, max_out);
+    IG_REQUIRE(r % 8 == 0 && pow2(r / (16 / elem_size(dtype))) && r / (16 / elem_size(dtype)) <= 32,
+               "%s: r / (16 / element size) must be a power of two <= 32 (got r=%d)", fn, r);
+    IG_REQUIRE(!c.scores || c.ld >= n, "%s: ld must be >= n when scores are written", fn);
+    IG_REQUIRE(std::isfinite(c.scale), "%s: scale must be finite", fn);
+    IG_REQUIRE(aligned16(c.x) && aligned16(c.Wq_part) && aligned16(c.Kp), "%s: x, Wq_part and Kp must be 16-byte aligned",
+               fn);
+    IG_REQUIRE(D % (16 / elem_size(dtype)) == 0, "%s: D must be a multiple of 16 / element size (got D=%d)", fn, D);
+    if (c.mode == IG_SEL_THRESHOLD)
+        IG_REQUIRE(c.alpha >= 0.f && !std::isnan(c.alpha) && c.max_sel >= 0, "%s: alpha must be >= 0", fn);
+    else if (c.mode == IG_SEL_TOPK)
+        IG_REQUIRE(c.k >= 1, "%s: k must be >= 1", fn);
+    else if (c.mode == IG_SEL_HEADAVG)
+        return fail(IG_EUNSUPPORTED, "%s: the head-average mode needs every head's count first; "
+                                     "use ig_rehearse + ig_select", fn);
+    else
+        return fail(IG_EINVAL, "%s: unknown mode %d", fn, c.mode);
+    if (n > kSpecMaxRows)
+        return fail(IG_EUNSUPPORTED, "%s: n = %d exceeds %d rows; use ig_rehearse + ig_select", fn, n, kSpecMaxRows);
+    IG_REQUIRE(!c.counters || c.cmax >= 2, "%s: cmax must be >= 2", fn);
+    IG_REQUIRE(H <= 0xFFFF, "%s: at most 65535 heads", fn);
+    const size_t need = speculate_ws_bytes(B, H, D, r, n, dtype);
+    IG_REQUIRE(c.ws && ws_bytes >= need, "%s: workspace of %zu bytes needed", fn, need);
+    IG_REQUIRE(aligned16(c.ws), "%s: workspace must be 16-byte aligned", fn);
+    return IG_OK;
+}
+
 int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H, int r,
                  int n, int n_cap, int dtype, float scale, int mode, float alpha, int k, int max_sel, int32_t* idx,
                  int32_t* count, int max_out, uint32_t* counters, uint32_t cmax, int32_t* victim, float* q_part,
                  float* scores, int ld, void* ws, size_t ws_bytes, hipStream_t stream) {
-    IG_REQUIRE_DTYPE("ig_speculate", dtype);
-    IG_REQUIRE(x && Wq_part && Kp && idx && count, "ig_speculate: NULL required pointer");
-    IG_REQUIRE(B >= 1 && D >= 1 && H >= 1 && r >= 1 && n >= 1 && n <= n_cap && max_out >= 1,
-               "ig_speculate: bad sizes (B=%d D=%d H=%d r=%d n=%d n_cap=%d max_out=%d)", B, D, H, r, n, n_cap,
-               max_out);
-    IG_REQUIRE(r % 8 == 0 && pow2(r / (16 / elem_size(dtype))) && r / (16 / elem_size(dtype)) <= 32,
-               "ig_speculate: r / (16 / element size) must be a power of two <= 32 (got r=%d)", r);
-    IG_REQUIRE(!scores || ld >= n, "ig_speculate: ld must be >= n when scores are written");
-    IG_REQUIRE(std::isfinite(scale), "ig_speculate: scale must be finite");
-    IG_REQUIRE(aligned16(x) && aligned16(Wq_part) && aligned16(Kp), "ig_speculate: x, Wq_part and Kp must be 16-byte aligned");
-    IG_REQUIRE(D % (16 / elem_size(dtype)) == 0, "ig_speculate: D must be a multiple of 16 / element size (got D=%d)", D);
-    if (mode == IG_SEL_THRESHOLD)
-        IG_REQUIRE(alpha >= 0.f && !std::isnan(alpha) && max_sel >= 0, "ig_speculate: alpha must be >= 0");
-    else if (mode == IG_SEL_TOPK)
-        IG_REQUIRE(k >= 1, "ig_speculate: k must be >= 1");
-    else if (mode == IG_SEL_HEADAVG)
-        return fail(IG_EUNSUPPORTED, "ig_speculate: the head-average mode needs every head's count first; "
-                                     "use ig_rehearse + ig_select");
-    else
-        return fail(IG_EINVAL, "ig_speculate: unknown mode %d", mode);
-    if (n > kSpecMaxRows)
-        return fail(IG_EUNSUPPORTED, "ig_speculate: n = %d exceeds %d rows; use ig_rehearse + ig_select", n,
-                    kSpecMaxRows);
-    IG_REQUIRE(!counters || cmax >= 2, "ig_speculate: cmax must be >= 2");
-    IG_REQUIRE(H <= 0xFFFF, "ig_speculate: at most 65535 heads");
-    const size_t need = speculate_ws_bytes(B, H, D, r, n, dtype);
-    IG_REQUIRE(ws && ws_bytes >= need, "ig_speculate: workspace of %zu bytes needed", need);
-    IG_REQUIRE(aligned16(ws), "ig_speculate: workspace must be 16-byte aligned");
-    return hip_status(launch_speculate(x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, mode, alpha, k,
-                                       max_sel, idx, count, max_out, counters, cmax, victim, q_part, scores, ld, ws,
-                                       stream),
-                      "ig_speculate");
+    const SpecCall c{x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, mode, alpha, k, max_sel, idx, count,
+                     max_out, counters, cmax, victim, q_part, scores, ld, ws};
+    if (const int e = check_spec("ig_speculate", c, ws_bytes)) return e;
+    return hip_status(launch_decode_layer(nullptr, &c, stream), "ig_speculate");
 }
 
 int ig_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k, int max_sel,
@@ -193,21 +198,55 @@ int ig_gather_kv(const void* K, const void* V, const int32_t* idx, const int32_t
                       "ig_gather_kv");
 }
 
+// Validation of an attention call (ig_sparse_decode_attn, and the attention half of ig_decode_layer).
+static int check_attn(const char* fn, const AttnCall& c, size_t ws_bytes) {
+    const int dtype = c.dtype, B = c.B, H = c.H, d = c.d, max_out = c.max_out;
+    IG_REQUIRE(dtype == IG_F32 || dtype == IG_BF16, "%s: unknown dtype %d", fn, dtype);
+    IG_REQUIRE(c.q && c.K && c.V && c.count && c.out, "%s: NULL required pointer", fn);
+    IG_REQUIRE(B >= 1 && H >= 1 && c.ld_rows >= 1 && max_out >= 1, "%s: bad sizes (B=%d H=%d ld_rows=%d max_out=%d)",
+               fn, B, H, c.ld_rows, max_out);
+    IG_REQUIRE(head_dim_ok(d, dtype), "%s: unsupported head dim %d", fn, d);
+    IG_REQUIRE(std::isfinite(c.scale), "%s: scale must be finite", fn);
+    IG_REQUIRE(aligned16(c.q) && aligned16(c.K) && aligned16(c.V), "%s: q, K, V must be 16-byte aligned", fn);
+    const AttnPlan p = plan_attn(B, H, d, max_out);
+    IG_REQUIRE(p.ws_bytes == 0 || (c.ws && ws_bytes >= p.ws_bytes), "%s: workspace of %zu bytes needed", fn,
+               p.ws_bytes);
+    return IG_OK;
+}
+
 int ig_sparse_decode_attn(const void* q, const void* K, const void* V, int ld_rows, const int32_t* idx,
                           const int32_t* count, int B, int H, int d, int max_out, int dtype, float scale, float* out,
                           float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-    IG_REQUIRE_DTYPE("ig_sparse_decode_attn", dtype);
-    IG_REQUIRE(q && K && V && count && out, "ig_sparse_decode_attn: NULL required pointer");
-    IG_REQUIRE(B >= 1 && H >= 1 && ld_rows >= 1 && max_out >= 1,
-               "ig_sparse_decode_attn: bad sizes (B=%d H=%d ld_rows=%d max_out=%d)", B, H, ld_rows, max_out);
-    IG_REQUIRE(head_dim_ok(d, dtype), "ig_sparse_decode_attn: unsupported head dim %d", d);
-    IG_REQUIRE(std::isfinite(scale), "ig_sparse_decode_attn: scale must be finite");
-    IG_REQUIRE(aligned16(q) && aligned16(K) && aligned16(V), "ig_sparse_decode_attn: q, K, V must be 16-byte aligned");
-    const AttnPlan p = plan_attn(B, H, d, max_out);
-    IG_REQUIRE(p.ws_bytes == 0 || (ws && ws_bytes >= p.ws_bytes),
-               "ig_sparse_decode_attn: workspace of %zu bytes needed", p.ws_bytes);
-    return hip_status(launch_attn(q, K, V, ld_rows, idx, count, B, H, d, max_out, dtype, scale, out, lse, ws, stream),
-                      "ig_sparse_decode_attn");
+    const AttnCall c{q, K, V, ld_rows, idx, count, B, H, d, max_out, dtype, scale, out, lse, ws};
+    if (const int e = check_attn("ig_sparse_decode_attn", c, ws_bytes)) return e;
+    return hip_status(launch_decode_layer(&c, nullptr, stream), "ig_sparse_decode_attn");
+}
+
+int ig_decode_layer(int B, int H, int d, int dtype, const ig_attn_call* attn, const ig_spec_call* spec,
+                    hipStream_t stream) {
+    IG_REQUIRE(attn || spec, "ig_decode_layer: nothing to do (attn and spec both NULL)");
+    AttnCall ac{};
+    SpecCall sc{};
+    if (attn) {
+        ac = AttnCall{attn->q, attn->K, attn->V, attn->ld_rows, attn->idx, attn->count, B, H, d, attn->max_out, dtype,
+                      attn->scale, attn->out, attn->lse, attn->ws};
+        if (const int e = check_attn("ig_decode_layer (attn)", ac, attn->ws_bytes)) return e;
+    }
+    if (spec) {
+        sc = SpecCall{spec->x, spec->Wq_part, spec->bq_part, spec->Kp, B, spec->D, H, spec->r, spec->n, spec->n_cap,
+                      dtype, spec->scale, spec->mode, spec->alpha, spec->k, spec->max_sel, spec->idx, spec->count,
+                      spec->max_out, spec->counters, spec->cmax, spec->victim, spec->q_part, spec->scores, spec->ld,
+                      spec->ws};
+        if (const int e = check_spec("ig_decode_layer (spec)", sc, spec->ws_bytes)) return e;
+    }
+    if (attn && spec) {
+        // the halves run concurrently: what the speculation writes must not be what the attention reads
+        IG_REQUIRE(static_cast<const void*>(sc.idx) != static_cast<const void*>(ac.idx) &&
+                       static_cast<const void*>(sc.count) != static_cast<const void*>(ac.count),
+                   "ig_decode_layer: the speculation's idx/count must not be the attention's");
+        IG_REQUIRE(ac.ws == nullptr || ac.ws != sc.ws, "ig_decode_layer: the two halves need distinct workspaces");
+    }
+    return hip_status(launch_decode_layer(attn ? &ac : nullptr, spec ? &sc : nullptr, stream), "ig_decode_layer");
 }
 
 int ig_pool_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n, int n_cap,

@@ -69,6 +69,47 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
                      int32_t* idx, int32_t* count, int max_out, uint32_t* counters, uint32_t cmax, int32_t* victim,
                      float* q_part, float* scores, int ld, void* ws, hipStream_t s);
 int launch_zero(void* ws, size_t bytes, hipStream_t s);
+int launch_attn_combine(const float* part, int nsplit, int d, int BH, float* out, float* lse, hipStream_t s);
+
+// host-side descriptors of the two halves of a decode layer (the arguments of launch_attn and
+// launch_speculate)
+struct AttnCall {
+    const void* q;
+    const void* K;
+    const void* V;
+    int ld_rows;
+    const int32_t* idx;
+    const int32_t* count;
+    int B, H, d, max_out, dtype;
+    float scale;
+    float* out;
+    float* lse;
+    void* ws;
+};
+struct SpecCall {
+    const void* x;
+    const void* Wq_part;
+    const float* bq_part;
+    const void* Kp;
+    int B, D, H, r, n, n_cap, dtype;
+    float scale;
+    int mode;
+    float alpha;
+    int k, max_sel;
+    int32_t* idx;
+    int32_t* count;
+    int max_out;
+    uint32_t* counters;
+    uint32_t cmax;
+    int32_t* victim;
+    float* q_part;
+    float* scores;
+    int ld;
+    void* ws;
+};
+constexpr int kDecodeMaxRows = 16384;  // rows per (b, h) for the fused decode launch (LDS with two roles)
+bool decode_fusable(const AttnCall& a, const SpecCall& s);
+int launch_decode_layer(const AttnCall* a, const SpecCall* s, hipStream_t st);
 int launch_build_partial(const void* K, const int32_t* chan, void* Kp, int B, int H, int d, int r,
                          int n_cap, int row0, int row1, int dtype, hipStream_t s);
 int launch_append(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan,

@@ -27,6 +27,8 @@ struct SelScratch {
     int bc[4];
 };
 
+// Sum over the first NT threads of the block (the ones still running).
+template <int NT = kSelThreads>
 __device__ __forceinline__ int block_sum(int v, SelScratch& sh) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     v = wave_sum_i32(v);
@@ -34,7 +36,7 @@ __device__ __forceinline__ int block_sum(int v, SelScratch& sh) {
     __syncthreads();
     int t = 0;
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) t += sh.wtot[w];
+    for (int w = 0; w < NT / kWave; ++w) t += sh.wtot[w];
     __syncthreads();
     return t;
 }
@@ -250,8 +252,8 @@ __device__ __forceinline__ void fast_sel_init(FastSel& fs) {
     if (threadIdx.x < 512) fs.words[threadIdx.x] = 0u;
 }
 
-// Exact kk-th largest key T of lk[0..n) (1 <= kk <= n, 1024 threads; fast_sel_init and a barrier
-// before).  Selecting every key above T and the first *need_eq keys equal to T gives the top kk;
+// Exact kk-th largest key T of lk[0..n) (1 <= kk <= n; the first NT threads of the block take part,
+// the others have exited; fast_sel_init and a barrier before).  Selecting every key above T and the first *need_eq keys equal to T gives the top kk;
 // *eq_total keys equal T.  When a digit's whole bin belongs to the top kk the search stops early: T
 // is then the bin's lowest key value (its low bits zero) and every key >= T is selected
 // (*need_eq == *eq_total).  Ends after a barrier.
@@ -262,6 +264,7 @@ __device__ __forceinline__ void fast_sel_init(FastSel& fs) {
 // finds the digit on its own: lane L holds bins 255-4L .. 252-4L, a DPP prefix sum over the lanes
 // gives the keys above each bin, and the lane holding the bin where the count reaches rem
 // broadcasts it.
+template <int NT = kSelThreads>
 __device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, uint32_t* T_out,
                                               int* need_eq_out, int* eq_total_out) {
     const int tid = threadIdx.x, lane = tid % kWave;
@@ -269,7 +272,7 @@ __device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk,
     int rem = kk, dcount = 0;
     for (int pass = 0, shift = 24; shift >= 0; ++pass, shift -= 8) {
         uint32_t* h = fs.hist(pass % 3);
-        for (int j0 = 0; j0 < n; j0 += kSelThreads) {
+        for (int j0 = 0; j0 < n; j0 += NT) {
             const int j = j0 + tid;
             const uint32_t key = j < n ? lk[j] : 0u;
             const uint32_t bin = (key >> shift) & 255u;
@@ -323,12 +326,13 @@ __device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk,
 // groups: it counts its rows with ballots, one barrier shares the per-wave counts, and a second pass
 // writes out[pos] = j and calls visit(pos, j).  Returns the number selected (block-uniform).  lk is
 // read by other waves while visit runs, so a visitor must not write lk.
-template <typename Visit>
+template <int NT = kSelThreads, typename Visit = NoVisit>
 __device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, int eq_total,
                            int32_t* __restrict__ out, int max_out, FastSel& fs, Visit visit) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const bool all_eq = need_eq >= eq_total;
-    const int chunk = (n + kSelThreads - 1) / kSelThreads * kWave;
+    constexpr int NW = NT / kWave;
+    const int chunk = (n + NT - 1) / NT * kWave;
     const int lo = min(n, wave * chunk), hi = min(n, lo + chunk);
     int n_gt = 0, n_eq = 0;
     for (int j0 = lo; j0 < hi; j0 += kWave) {
@@ -340,9 +344,9 @@ __device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, i
     // per-wave counts packed as gt | eq << 16 (each <= n <= 32768), prefix-summed over the waves
     if (lane == 0) fs.wtot[wave] = n_gt | (n_eq << 16);
     __syncthreads();
-    const int incl = wave_incl_scan(lane < kSelWaves ? fs.wtot[lane] : 0);
+    const int incl = wave_incl_scan(lane < NW ? fs.wtot[lane] : 0);
     const int before = wave > 0 ? read_lane(incl, wave - 1) : 0;
-    const int total = read_lane(incl, kSelWaves - 1);
+    const int total = read_lane(incl, NW - 1);
     int eq_before = before >> 16;
     const int gt_tot = total & 0xFFFF, eq_tot = total >> 16;
     const int take = all_eq ? eq_tot : min(eq_tot, need_eq);

@@ -1,0 +1,126 @@
+// One decode layer in one launch (InfiniGen, arXiv 2406.19707, paper-graph-ui
+// summary, section 3.2 "Big-Picture Architecture", KV Selection Controller:
+// the speculation for the next layer runs while the current layer computes,
+// from the current layer's attention input; section 3.4 "Decoding Stage"):
+// the attention of layer l over the rows its speculation selected, beside the
+// speculation for layer l+1 (scores, selection and counters).
+//
+// The partial-query projection for layer l+1 runs first (k_rehearse_proj).
+// Then one grid holds both roles: workgroups [0, B*H) run spec_row for layer
+// l+1, the rest run attention items of layer l (one (b, h, split) each, all
+// 1024 threads of the workgroup on it).  The two roles touch disjoint buffers,
+// so they need no synchronisation; a CU holds one workgroup of each role, and
+// the attention's K/V gathers fill the memory pipeline while the speculation
+// is in its latency-bound selection.  Splits of an attention row are merged by
+// the usual combine kernel afterwards.
+#include "ig_attn_dev.h"
+#include "ig_spec_dev.h"
+
+namespace ig {
+
+constexpr int kDecodeThreads = 1024;
+
+template <int R, int LPR_A, int VEC>
+union DecodeShared {
+    SpecShared<R> spec;
+    AttnShared<kDecodeThreads, LPR_A, VEC> attn;
+};
+
+// Two 1024-thread workgroups per CU (8 waves per SIMD, at most 64 VGPRs each), so that one workgroup
+// of each role fits on a CU at once (the second launch bound is the minimum number of waves per SIMD).
+// Rows in flight per lane that keep the registers there without spills: 4 partial-key rows (double
+// buffered) and 2 K/V rows (64 lane groups x 2 = 128 rows per pass).
+constexpr int kDecodeSpecBatch = 4;
+constexpr int kDecodeAttnRows = 2;
+
+template <typename T, int LPR_S, int LPR_A>
+__global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int n_spec, int bh_attn) {
+    extern __shared__ __align__(16) uint32_t keys[];  // the speculation role's score keys
+    __shared__ DecodeShared<LPR_S * Vec<T>::N, LPR_A, Vec<T>::N> sm;
+    const int wg = blockIdx.x;
+    if (wg < n_spec) {
+        spec_row<T, LPR_S, kDecodeSpecBatch>(p, wg, keys, sm.spec);
+        return;
+    }
+    const int item = wg - n_spec;
+    attn_item<T, LPR_A, kDecodeThreads, kDecodeAttnRows>(a, item % bh_attn, item / bh_attn, sm.attn);
+}
+
+template <typename T, int LPR_S, int LPR_A>
+static int launch_fused(const SpecParams& p, const AttnArgs& a, int bh_attn, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_layer<T, LPR_S, LPR_A>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(speculate_lds_bytes(kDecodeMaxRows)));
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr_set = true;
+    }
+    const int n_spec = p.B * p.H;
+    const int grid = n_spec + a.nsplit * bh_attn;
+    hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A>), dim3(grid), dim3(kDecodeThreads), speculate_lds_bytes(p.n),
+                       s, p, a, n_spec, bh_attn);
+    return static_cast<int>(hipGetLastError());
+}
+
+// lanes per partial-key row (r / elements per 16 bytes) and per K/V row (d / elements per 16 bytes)
+static int lpr_of(int len, int dtype) { return len / (dtype == IG_BF16 ? 8 : 4); }
+
+bool decode_fusable(const AttnCall& a, const SpecCall& s) {
+    const int ls = lpr_of(s.r, s.dtype), la = lpr_of(a.d, a.dtype);
+    return a.dtype == s.dtype && s.n <= kDecodeMaxRows && (ls == 2 || ls == 4 || ls == 8) &&
+           (la == 8 || la == 16 || la == 32);
+}
+
+template <typename T, int LPR_S>
+static int launch_fused_s(const SpecParams& p, const AttnArgs& a, int la, int bh_attn, hipStream_t s) {
+    switch (la) {
+        case 8: return launch_fused<T, LPR_S, 8>(p, a, bh_attn, s);
+        case 16: return launch_fused<T, LPR_S, 16>(p, a, bh_attn, s);
+        case 32: return launch_fused<T, LPR_S, 32>(p, a, bh_attn, s);
+        default: return static_cast<int>(hipErrorInvalidValue);
+    }
+}
+
+template <typename T>
+static int launch_fused_t(const SpecParams& p, const AttnArgs& a, int ls, int la, int bh_attn, hipStream_t s) {
+    switch (ls) {
+        case 2: return launch_fused_s<T, 2>(p, a, la, bh_attn, s);
+        case 4: return launch_fused_s<T, 4>(p, a, la, bh_attn, s);
+        case 8: return launch_fused_s<T, 8>(p, a, la, bh_attn, s);
+        default: return static_cast<int>(hipErrorInvalidValue);
+    }
+}
+
+static int launch_attn_call(const AttnCall& c, hipStream_t s) {
+    return launch_attn(c.q, c.K, c.V, c.ld_rows, c.idx, c.count, c.B, c.H, c.d, c.max_out, c.dtype, c.scale, c.out,
+                       c.lse, c.ws, s);
+}
+
+static int launch_spec_call(const SpecCall& c, hipStream_t s) {
+    return launch_speculate(c.x, c.Wq_part, c.bq_part, c.Kp, c.B, c.D, c.H, c.r, c.n, c.n_cap, c.dtype, c.scale,
+                            c.mode, c.alpha, c.k, c.max_sel, c.idx, c.count, c.max_out, c.counters, c.cmax, c.victim,
+                            c.q_part, c.scores, c.ld, c.ws, s);
+}
+
+int launch_decode_layer(const AttnCall* a, const SpecCall* sc, hipStream_t s) {
+    if (!a) return launch_spec_call(*sc, s);
+    if (!sc) return launch_attn_call(*a, s);
+    if (!decode_fusable(*a, *sc)) {
+        const int e = launch_spec_call(*sc, s);
+        return e ? e : launch_attn_call(*a, s);
+    }
+    SpecParams p;
+    int e = begin_speculate(*sc, &p, s);
+    if (e) return e;
+    const AttnPlan ap = plan_attn(a->B, a->H, a->d, a->max_out);
+    const AttnArgs aa{a->q, a->K, a->V, a->ld_rows, a->idx, a->count, a->d, a->max_out, ap.rows_per_split, ap.nsplit,
+                      a->scale, a->out, a->lse, static_cast<float*>(a->ws)};
+    const int bh = a->B * a->H;
+    e = a->dtype == IG_BF16 ? launch_fused_t<uint16_t>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s)
+                            : launch_fused_t<float>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s);
+    if (e || ap.nsplit == 1) return e;
+    return launch_attn_combine(aa.part, ap.nsplit, a->d, bh, a->out, a->lse, s);
+}
+
+}  // namespace ig

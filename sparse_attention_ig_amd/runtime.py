@@ -176,6 +176,38 @@ class DeviceLayer:
                     counters=self.counters, victim=self.victim if want_victim else None)
 
 
+def attn_call(layer: "DeviceLayer", max_out: Optional[int] = None) -> Dict:
+    """The attention half of ig_decode_layer for ``layer`` (its q, cache and current selection)."""
+    s = layer.spec
+    max_out = layer.max_out if max_out is None else max_out
+    idx = layer.idx if max_out == layer.max_out else layer.idx.view(-1)[:s.B * s.H * max_out].view(s.B, s.H, max_out)
+    return dict(q=layer.q, K=layer.K, V=layer.V, idx=idx, count=layer.count, scale=s.softmax_scale, out=layer.out,
+                lse=layer.lse, ws=layer.ws)
+
+
+def spec_call(layer: "DeviceLayer", *, mode: str, alpha: float = math.inf, k: int = 0, max_sel: int = 0,
+              max_out: Optional[int] = None, cmax: int = 65535, want_victim: bool = False,
+              n: Optional[int] = None, x=None) -> Dict:
+    """The speculation half of ig_decode_layer for ``layer`` (from its own x unless ``x`` is given)."""
+    s = layer.spec
+    max_out = layer.max_out if max_out is None else max_out
+    idx = layer.idx if max_out == layer.max_out else layer.idx.view(-1)[:s.B * s.H * max_out].view(s.B, s.H, max_out)
+    return dict(x=layer.x if x is None else x, Wq_part=layer.Wq_part, Kp=layer.Kp, n=s.n if n is None else n,
+                scale=s.softmax_scale, mode=mode, alpha=alpha, k=k, max_sel=max_sel, idx=idx, count=layer.count,
+                counters=layer.counters, cmax=cmax, victim=layer.victim if want_victim else None,
+                q_part=layer.q_part, scores=layer.scores if layer.keep_scores else None, ld=s.cap, ws=layer.ws_spec)
+
+
+def decode_layer(attn_layer: Optional["DeviceLayer"], spec_layer: Optional["DeviceLayer"], step_kw: Dict,
+                 stream=None):
+    """Layer l's attention (attn_layer) beside the speculation for layer l+1 (spec_layer), one fused launch."""
+    from . import _lib as L
+    kw = {k: v for k, v in step_kw.items() if k in ("mode", "alpha", "k", "max_sel", "max_out", "cmax",
+                                                     "want_victim", "n")}
+    L.ig_decode_layer(attn_call(attn_layer, step_kw.get("max_out")) if attn_layer is not None else None,
+                      spec_call(spec_layer, **kw) if spec_layer is not None else None, stream=stream)
+
+
 class MappedHost:
     """Device-side view of a pinned host tensor: the address kernels must use, from
     hipHostGetDevicePointer (fails cleanly if the memory is not pinned and mapped), with the shape and
