@@ -71,7 +71,16 @@ def main() -> int:
     ap.add_argument("--frac", type=float, default=0.01, help="top-k budget as a fraction of n (llama2-7b-long)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run this many eager steps of the schedule and exit (for hardware-counter passes)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="copy MB megabytes device to device three times and exit (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 counter_collection files of a --profile-steps run and of a "
+                         "--copy-calibration run into the traffic record (no GPU needed)")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(args)
     faulthandler.enable()   # a fatal signal prints the Python stack of every thread
 
     if args.gpus != 1:
@@ -87,6 +96,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        # a plain copy kernel of known size: reads and writes exactly MB megabytes per launch
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {nbytes} bytes x 3", file=sys.stderr, flush=True)
+        return 0
     _lib.load()
 
     if args.workload == "llama2-13b-pipeline":
@@ -190,6 +209,13 @@ def main() -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b)
 
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            run()
+        torch.cuda.synchronize()
+        print(f"[bench] {args.profile_steps} profiled steps done", file=sys.stderr, flush=True)
+        return 0
+
     # eager launches (every call goes through Python and ctypes)
     for _ in range(args.warmup):
         run()
@@ -199,9 +225,18 @@ def main() -> int:
     graph = capture(PARTS)
     for _ in range(args.warmup):
         graph.replay()
+    # one event between consecutive replays: the steps' own durations give the percentiles
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ms_total = timed_ms(graph.replay, args.steps)
+    evs[0].record()
+    for i in range(args.steps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    ms_total = evs[0].elapsed_time(evs[-1])
+    step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     ms_step = ms_total / args.steps
     tok_s_layer = spec.B * args.layers * args.steps / (ms_total / 1e3)
 
@@ -230,6 +265,27 @@ def main() -> int:
         for _ in range(3):
             gl.replay()
         per_us["decode_layer"] = 1e3 * timed_ms(gl.replay, args.steps) / (args.steps * args.layers)
+
+    # dense decode attention over all n rows of the same caches (informative comparison)
+    dense_count = torch.full((spec.B, spec.H), spec.n, dtype=torch.int32, device="cuda")
+
+    def run_dense():
+        for l in layers:
+            _lib.ig_sparse_decode_attn(l.q, l.K, l.V, None, dense_count, spec.softmax_scale, max_out=spec.n,
+                                       out=l.out, lse=l.lse, ws=l.ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_dense()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gd):
+        run_dense()
+    for _ in range(3):
+        gd.replay()
+    dense_us = 1e3 * timed_ms(gd.replay, args.steps) / (args.steps * args.layers)
+    dense_bytes = spec.B * spec.H * spec.n * 2 * spec.d * (2 if spec.dtype == "bf16" else 4)
 
     res = to_host(layers[0].count)
     c_mean = float(res.mean())
@@ -263,9 +319,12 @@ def main() -> int:
         "per_call_us": {k: round(v, 3) for k, v in per_us.items()},
         "eager_ms_per_step": round(ms_eager, 4),
         "eager_tokens_s_layer": round(spec.B * args.layers / (ms_eager / 1e3), 1),
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
+        "dense_attn_us": round(dense_us, 3),
+        "dense_attn_GBs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
         "roofline": {"kernel": f"ig_{dominant}", "bound": "hbm", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "alg_bytes_per_launch": int(dom_bytes)},
+                     "traffic": measured_traffic(args, f"ig_{dominant}"), "alg_bytes_per_launch": int(dom_bytes)},
         "wall_s_timed": round(wall, 3),
     }
 
@@ -427,27 +486,131 @@ def bench_pool(args) -> int:
     return 0
 
 
-def cpu_baseline(spec, step_kw, seconds: float) -> dict:
-    """The CPU oracle (float64 NumPy, one thread) on the same layer-step, repeated for ~seconds."""
+def _oracle_rate(spec, oi, step_kw, seconds: float, threads: int):
     import numpy as np
     from threadpoolctl import threadpool_limits
     from tests import harness
 
-    with threadpool_limits(1):
-        oi = harness.oracle_inputs(spec)
-        kw = dict(step_kw)
+    with threadpool_limits(threads):
         C0 = np.zeros((spec.B, spec.cap), np.uint32)
         reps = 0
         t0 = time.perf_counter()
         while True:
-            harness.oracle_step(oi, counters=C0, **kw)
+            harness.oracle_step(oi, counters=C0, **step_kw)
             reps += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-    return {"value": round(spec.B * reps / el, 2), "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
+    return spec.B * reps / el, reps, el
+
+
+def cpu_baseline(spec, step_kw, seconds: float) -> dict:
+    """The CPU oracle (float64 NumPy) on the same layer-step, repeated for ~seconds: with BLAS on the
+    cores this process may use (its affinity, capped by OMP_NUM_THREADS when set), and with one thread."""
+    from tests import harness
+
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
+    oi = harness.oracle_inputs(spec)
+    rate, reps, el = _oracle_rate(spec, oi, step_kw, seconds, cores)
+    rate1, reps1, el1 = _oracle_rate(spec, oi, step_kw, seconds / 2, 1)
+    return {"value": round(rate, 2), "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
             "sample": f"{reps} full layer-steps of the same workload (1 layer, all {spec.B}x{spec.H} heads), "
-                      f"{el:.1f} s, BLAS limited to 1 thread"}
+                      f"{el:.1f} s, BLAS threads = {cores}",
+            "value_1thread": round(rate1, 2),
+            "sample_1thread": f"{reps1} layer-steps, {el1:.1f} s, BLAS limited to 1 thread"}
+
+
+# ---------------------------------------------------------------- HBM traffic from hardware counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ("ig_attn_dev.h", "ig_device.h", "ig_pool_dev.h", "ig_select_dev.h", "ig_spec_dev.h",
+                  "k_decode.hip", "k_rehearse.hip", "k_speculate.hip", "k_attn.hip", "k_select.hip", "k_pool.hip")
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_attention_ig_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+# the kernels each call launches (rocprofv3 kernel names start with these)
+CALL_KERNELS = {"ig_decode_layer": ("void ig::k_rehearse_proj<", "void ig::k_decode_layer<"),
+                "ig_speculate": ("void ig::k_rehearse_proj<", "void ig::k_speculate<"),
+                "ig_rehearse": ("void ig::k_rehearse_proj<", "void ig::k_rehearse_score<")}
+
+
+def _counter_means(path: str) -> dict:
+    """Mean counter value (KiB) per kernel name of a rocprofv3 counter_collection CSV."""
+    import csv
+    acc = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def record_traffic(args) -> int:
+    """Per-call HBM bytes of the bench's dominant call from FETCH_SIZE and WRITE_SIZE passes, each scaled
+    by what the same counter reads for a plain device copy of --copy-calibration MB (default 512)."""
+    fetch, write, cfetch, cwrite = (_counter_means(p) for p in args.record_traffic)
+    copy_kib = (args.copy_calibration or 512) * 1024.0
+    cname = [k for k in cfetch if "copyBuffer" in k]
+    if not cname:
+        print("no copy kernel in the calibration files", file=sys.stderr)
+        return 1
+    f_fac = copy_kib / cfetch[cname[0]]
+    w_fac = copy_kib / cwrite[cname[0]]
+    call = "ig_decode_layer" if args.schedule == "layer" else "ig_speculate"
+    per_kernel = {}
+    total = 0.0
+    for prefix in CALL_KERNELS[call]:
+        names = [k for k in fetch if k.startswith(prefix)]
+        if len(names) != 1:
+            print(f"expected one kernel named {prefix}*, found {names}", file=sys.stderr)
+            return 1
+        nm = names[0]
+        b = (fetch[nm] * f_fac + write[nm] * w_fac) * 1024.0
+        per_kernel[nm] = {"fetch_KiB": round(fetch[nm], 1), "write_KiB": round(write[nm], 1),
+                          "bytes": int(round(b))}
+        total += b
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec["note"] = ("HBM bytes per call: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the "
+                   "dispatches of a --profile-steps run), each scaled by copy MB / counter reading of a plain "
+                   "device copy; 'sources' is the digest of the kernel sources the counters were taken with")
+    key = f"{args.workload}/{args.mode}/{args.path}/{args.schedule}/{call}"
+    rec.setdefault("entries", {})[key] = {
+        "sources": kernel_sources_digest(), "bytes_per_call": int(round(total)),
+        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "kernels": per_kernel}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec["entries"][key]))
+    return 0
+
+
+def measured_traffic(args, call: str):
+    """HBM bytes per call from the committed FETCH_SIZE / WRITE_SIZE counter passes, scaled by the copy
+    calibration; None when there is no record for this workload and call, or when the kernel sources
+    have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{args.workload}/{args.mode}/{args.path}/{args.schedule}/{call}"
+    entry = rec.get("entries", {}).get(key)
+    if not entry or entry.get("sources") != kernel_sources_digest():
+        return None
+    return entry.get("bytes_per_call")
 
 
 if __name__ == "__main__":

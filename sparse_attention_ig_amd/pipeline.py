@@ -5,9 +5,10 @@ The speculation for layer l+1 runs at layer l from layer l's attention input
 "Decoding Stage"): per decode step and layer l,
 
     attention(l)          over idx_l selected at layer l-1 (layer 0: dense over every row)
-    ig_speculate(l + 1)   from x_l with layer l+1's partial weight and partial key cache
+    speculation(l + 1)    from x_l with layer l+1's partial weight and partial key cache
                           -> idx_{l+1}, counters of layer l+1
 
+both in one ig_decode_layer call (the two run side by side on the GPU),
 and after the last layer every layer appends the new token's key and value (ig_append_kv), which
 also writes the partial-key row and restarts the slot's counter.
 """
@@ -17,7 +18,7 @@ import math
 from typing import List, Optional
 
 from . import _lib as L
-from .runtime import DeviceLayer, HostLayer
+from .runtime import DeviceLayer, HostLayer, attn_call, spec_call
 
 
 class DecodePipeline:
@@ -48,18 +49,15 @@ class DecodePipeline:
         self.dense_count.fill_(n)
         nl = len(self.layers)
         for l, lay in enumerate(self.layers):
+            # attention of layer l (layer 0: dense over every row) beside the speculation for layer l+1
+            attn = attn_call(lay)
             if l == 0:
-                L.ig_sparse_decode_attn(lay.q, lay.K, lay.V, None, self.dense_count, s.softmax_scale,
-                                        max_out=s.cap, out=lay.out, lse=lay.lse, ws=lay.ws, stream=stream)
-            else:
-                L.ig_sparse_decode_attn(lay.q, lay.K, lay.V, lay.idx, lay.count, s.softmax_scale, out=lay.out,
-                                        lse=lay.lse, ws=lay.ws, stream=stream)
+                attn.update(idx=None, count=self.dense_count, max_out=s.cap)
+            spec = None
             if l + 1 < nl:
-                nxt = self.layers[l + 1]
-                L.ig_speculate(x_layers[l], nxt.Wq_part, nxt.Kp, n, s.softmax_scale, mode, self.max_out,
-                               alpha=alpha, k=k, max_sel=max_sel, idx=nxt.idx, count=nxt.count,
-                               counters=nxt.counters, cmax=self.cmax, q_part=nxt.q_part, ws=nxt.ws_spec,
-                               stream=stream)
+                spec = spec_call(self.layers[l + 1], mode=mode, alpha=alpha, k=k, max_sel=max_sel, cmax=self.cmax,
+                                 n=n, x=x_layers[l])
+            L.ig_decode_layer(attn, spec, stream=stream)
         if append:
             for l, lay in enumerate(self.layers):
                 L.ig_append_kv(lay.K, lay.V, lay.Kp, lay.counters, lay.chan, k_new[l], v_new[l], n,
