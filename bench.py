@@ -114,8 +114,6 @@ def main() -> int:
         return bench_pool(args)
     if args.workload == "llama2-7b-long":
         spec = gen.llama2_7b_long(n=args.n or 32768, B=args.batch or 1, frac=args.frac)
-        if args.path == "fused" and spec.n > 32768:
-            args.path = "unfused"   # the fused speculation keeps a row's scores in LDS: n <= 32768
     else:
         spec = gen.opt_6_7b()
     if args.mode == "topk":

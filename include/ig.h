@@ -122,8 +122,8 @@ int ig_partial_weight_index(const void* Wq_s, int D, int H, int d, int r,
 /*
  * Bytes of scratch a call needs (0 if none).  op = IG_OP_REHEARSE: B, H, D,
  * r used.  IG_OP_SELECT: B, H, n, max_out used.  IG_OP_ATTN: B, H, d,
- * max_out used.  IG_OP_SPECULATE: B, H, D, r, n used.  IG_OP_TOUCH: B, H,
- * max_out used.  Unused arguments are ignored.
+ * max_out used.  IG_OP_SPECULATE: B, H, D, r, n, max_out used.  IG_OP_TOUCH:
+ * B, H, max_out used.  Unused arguments are ignored.
  */
 size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int max_out);
 
@@ -155,14 +155,18 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * scores, selection and counter update of ig_rehearse + ig_select +
  * ig_pool_touch (section 3.4, "Decoding Stage" steps 1-3 and 5, and the pool
  * paragraph), with the scores kept on chip.  Same arguments and results as
- * those calls; modes IG_SEL_THRESHOLD and IG_SEL_TOPK; n <= 32768 (the scores
- * of a row live in LDS), otherwise IG_EUNSUPPORTED.
+ * those calls; modes IG_SEL_THRESHOLD and IG_SEL_TOPK.  A row's scores live in
+ * LDS: when there are too few rows to fill the GPU, or n > 32768, each row is
+ * cut into up to 16 slices that select locally, and a merge launch selects
+ * among their candidates; IG_EUNSUPPORTED when the candidates (slices x
+ * min(slice rows, max_out)) would exceed 32768.
  * q_part [B][H][r] and scores [B][H][ld] are written only when not NULL.
  * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
  * receives the victim.  Two launches: the partial-query projection, then one
- * workgroup per (b, h) for scores, selection and counters.  The workspace
- * (IG_OP_SPECULATE bytes, required) holds the projection's partial sums and
- * one arrival word per sequence; it must have been zero-filled once with
+ * workgroup per (b, h) for scores, selection and counters (three with slices:
+ * the slices, then the merges).  The workspace (IG_OP_SPECULATE bytes,
+ * required) holds the projection's partial sums, one arrival word per
+ * sequence and the slices' candidates; it must have been zero-filled once with
  * ig_workspace_init, and every call returns the arrival words to zero.  Calls
  * sharing a workspace must not overlap.  H <= 65535.
  */

@@ -93,7 +93,7 @@ size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int m
             return touch_single_kernel(H, max_out) ? 0 : touch_ws_bytes(B);
         case IG_OP_SPECULATE:
             if (D < 1 || r < 1 || n < 1) return 0;
-            return speculate_ws_bytes(B, H, D, r, n, IG_BF16);
+            return speculate_ws_bytes(B, H, D, r, n, max_out, IG_BF16);
         default:
             return 0;
     }
@@ -148,11 +148,13 @@ static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes) {
                                      "use ig_rehearse + ig_select", fn);
     else
         return fail(IG_EINVAL, "%s: unknown mode %d", fn, c.mode);
-    if (n > kSpecMaxRows)
-        return fail(IG_EUNSUPPORTED, "%s: n = %d exceeds %d rows; use ig_rehearse + ig_select", fn, n, kSpecMaxRows);
+    const SpecPlan plan = plan_speculate(B, H, D, r, n, max_out, dtype);
+    if (!plan.ok)
+        return fail(IG_EUNSUPPORTED, "%s: n = %d with max_out = %d: the candidates of %d slices exceed %d; use "
+                    "ig_rehearse + ig_select", fn, n, max_out, plan.slices, kSpecMaxRows);
     IG_REQUIRE(!c.counters || c.cmax >= 2, "%s: cmax must be >= 2", fn);
     IG_REQUIRE(H <= 0xFFFF, "%s: at most 65535 heads", fn);
-    const size_t need = speculate_ws_bytes(B, H, D, r, n, dtype);
+    const size_t need = plan.ws_bytes;
     IG_REQUIRE(c.ws && ws_bytes >= need, "%s: workspace of %zu bytes needed", fn, need);
     IG_REQUIRE(aligned16(c.ws), "%s: workspace must be 16-byte aligned", fn);
     return IG_OK;

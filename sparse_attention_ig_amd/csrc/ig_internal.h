@@ -43,8 +43,15 @@ AttnPlan plan_attn(int B, int H, int d, int max_out);
 
 size_t select_ws_bytes(int B, int H, int n, int max_out);
 
-constexpr int kSpecMaxRows = 32768;   // fused speculation keeps every score of a row in LDS
-size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int dtype);
+constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
+struct SpecPlan {
+    RehearsePlan rp;
+    int slices, slice_rows, cand_cap;
+    bool ok;                          // false: rows too long for the candidates to fit one merge
+    size_t off_arrive, off_cnt, off_key, off_idx, ws_bytes;
+};
+SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype);
+size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_lds_bytes(int n);
 
 // kernel launchers (return hipError_t as int)
@@ -53,6 +60,9 @@ int launch_rehearse(const void* x, const void* Wq_part, const float* bq_part, co
                     float* q_part, float* scores, int ld, void* ws, hipStream_t s);
 int launch_proj(const void* x, const void* W, int B, int D, int N, int dtype, const RehearsePlan& p, float* part,
                 hipStream_t s);
+int launch_score(const float* part, const float* bias, const void* Kp, int B, int H, int r, int n, int n_cap,
+                 int dtype, float scale, float* q_part, float* scores, int ld, const RehearsePlan& p, hipStream_t s);
+
 int launch_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k,
                   int max_sel, int32_t* idx, int32_t* count, int max_out, void* ws, hipStream_t s);
 int launch_attn(const void* q, const void* K, const void* V, int ld_rows, const int32_t* idx,

@@ -7,6 +7,7 @@
 #pragma once
 
 #include <climits>
+#include <cmath>
 
 #include "ig_device.h"
 
@@ -14,7 +15,7 @@ namespace ig {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kSelLdsKeys = 8192;   // rows per (b, h) held in LDS (32 KB)
+constexpr int kSelLdsKeys = 32768;  // rows per (b, h) held in LDS (up to 128 KB of dynamic LDS)
 constexpr int kSelPerThread = 8;    // consecutive rows per thread in the compaction
 
 // mode values beyond the public ones: count-only pass of the head average
@@ -238,10 +239,13 @@ namespace ig {
 // after its barrier, clears buffer (p + 2) % 3 (last read in pass p - 1), so a pass needs a single
 // barrier and every wave derives the digit on its own.  The histogram words are free after the
 // select and stage the selected indices (kFastStage of them).
-constexpr int kFastStage = 4096;
+constexpr int kFastStage = 6144;
+constexpr int kSampleBase = 1024;             // words[1024, 2048): one sampled key per thread
+constexpr int kCandBase = 2048;               // words[2048, 6144): candidate keys of the sampled select
+constexpr int kMaxCand = kFastStage - kCandBase;
 
-struct FastSel {
-    uint32_t words[kFastStage];  // hist[3][256] during the select, then staging
+struct __align__(16) FastSel {  // 16-byte aligned: the histograms are read 4 bins at a time
+    uint32_t words[kFastStage];  // hist[3][256], samples and candidates during the select, then staging
     int wtot[kSelWaves];
     __device__ uint32_t* hist(int i) { return words + 256 * i; }
     __device__ uint32_t* stage() { return words; }
@@ -252,32 +256,40 @@ __device__ __forceinline__ void fast_sel_init(FastSel& fs) {
     if (threadIdx.x < 512) fs.words[threadIdx.x] = 0u;
 }
 
-// Exact kk-th largest key T of lk[0..n) (1 <= kk <= n; the first NT threads of the block take part,
-// the others have exited; fast_sel_init and a barrier before).  Selecting every key above T and the first *need_eq keys equal to T gives the top kk;
-// *eq_total keys equal T.  When a digit's whole bin belongs to the top kk the search stops early: T
-// is then the bin's lowest key value (its low bits zero) and every key >= T is selected
-// (*need_eq == *eq_total).  Ends after a barrier.
-//
-// Per pass: LDS atomics into the histogram (in the first pass, where a row's keys crowd into the few
-// bins of their sign and exponent bits and same-address atomics serialise, the bin of the wave's
-// first active lane is counted with one ballot and a single atomic), one barrier, then every wave
-// finds the digit on its own: lane L holds bins 255-4L .. 252-4L, a DPP prefix sum over the lanes
-// gives the keys above each bin, and the lane holding the bin where the count reaches rem
-// broadcasts it.
-template <int NT = kSelThreads>
-__device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, uint32_t* T_out,
-                                              int* need_eq_out, int* eq_total_out) {
-    const int tid = threadIdx.x, lane = tid % kWave;
-    uint32_t prefix = 0, pmask = 0;
-    int rem = kk, dcount = 0;
-    for (int pass = 0, shift = 24; shift >= 0; ++pass, shift -= 8) {
-        uint32_t* h = fs.hist(pass % 3);
-        for (int j0 = 0; j0 < n; j0 += NT) {
-            const int j = j0 + tid;
-            const uint32_t key = j < n ? lk[j] : 0u;
-            const uint32_t bin = (key >> shift) & 255u;
-            bool on = j < n && (key & pmask) == prefix;
-            if (pass == 0) {
+// E consecutive keys of lk from j (j % E == 0, lk 16-byte aligned); positions at or past `end` read 0.
+template <int E>
+__device__ __forceinline__ void load_keys(const uint32_t* lk, int j, int end, uint32_t (&k)[E]) {
+    if constexpr (E == 4) {
+        if (j + 3 < end) {
+            const uint4 v = *reinterpret_cast<const uint4*>(lk + j);
+            k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
+            return;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) k[e] = j + e < end ? lk[j + e] : 0u;
+}
+
+// Keys per lane per step: 4 (one 16-byte LDS read) once every thread has at least 4 keys, else 1.
+template <int NT>
+__device__ __forceinline__ bool wide_rows(int n) { return n >= 4 * NT; }
+
+// One radix pass: hist[digit] counts of the keys whose bits above `shift + 8` equal `prefix`.
+template <int NT, int E>
+__device__ __forceinline__ void radix_hist(const uint32_t* lk, int n, uint32_t* h, int shift, uint32_t prefix,
+                                           uint32_t pmask, bool first) {
+    const int lane = threadIdx.x % kWave;
+    for (int j0 = E * static_cast<int>(threadIdx.x); j0 < n; j0 += E * NT) {
+        uint32_t k[E];
+        load_keys<E>(lk, j0, n, k);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t bin = (k[e] >> shift) & 255u;
+            bool on = j0 + e < n && (k[e] & pmask) == prefix;
+            if (first) {
+                // the first pass's keys crowd into the few bins of their sign and exponent bits, and
+                // LDS atomics to one address serialise: the bin of the first active lane is counted
+                // with one ballot and a single atomic
                 const uint64_t act = __ballot(on);
                 if (act != 0) {
                     const int leader = __ffsll(static_cast<unsigned long long>(act)) - 1;
@@ -289,6 +301,31 @@ __device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk,
             }
             if (on) atomicAdd(&h[bin], 1u);
         }
+    }
+}
+
+// Exact kk-th largest key T of lk[0..n) (1 <= kk <= n; the first NT threads of the block take part,
+// the others have exited; fast_sel_init and a barrier before).  Selecting every key above T and the
+// first *need_eq keys equal to T gives the top kk; *eq_total keys equal T.  When a digit's whole bin
+// belongs to the top kk the search stops early: T is then the bin's lowest key value (its low bits
+// zero) and every key >= T is selected (*need_eq == *eq_total).  Ends after a barrier.
+//
+// Per pass: LDS atomics into that pass's histogram, one barrier, then every wave finds the digit on
+// its own: lane L holds bins 255-4L .. 252-4L, a DPP prefix sum over the lanes gives the keys above
+// each bin, and the lane holding the bin where the count reaches rem broadcasts it.
+template <int NT = kSelThreads>
+__device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, uint32_t* T_out,
+                                              int* need_eq_out, int* eq_total_out) {
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const bool wide = wide_rows<NT>(n);
+    uint32_t prefix = 0, pmask = 0;
+    int rem = kk, dcount = 0;
+    for (int pass = 0, shift = 24; shift >= 0; ++pass, shift -= 8) {
+        uint32_t* h = fs.hist(pass % 3);
+        if (wide)
+            radix_hist<NT, 4>(lk, n, h, shift, prefix, pmask, pass == 0);
+        else
+            radix_hist<NT, 1>(lk, n, h, shift, prefix, pmask, pass == 0);
         __syncthreads();
         if (tid < 256) fs.hist((pass + 2) % 3)[tid] = 0u;
         const uint4 c4 = *reinterpret_cast<const uint4*>(h + 252 - 4 * lane);
@@ -321,28 +358,50 @@ __device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk,
     *eq_total_out = dcount;
 }
 
+// Keys >= kc among lk[0..n), summed over the first NT threads (ends after barriers).
+template <int NT = kSelThreads>
+__device__ __forceinline__ int count_ge_lds(const uint32_t* lk, int n, uint32_t kc, SelScratch& sh) {
+    int c = 0;
+    if (wide_rows<NT>(n)) {
+        for (int j0 = 4 * static_cast<int>(threadIdx.x); j0 < n; j0 += 4 * NT) {
+            uint32_t k[4];
+            load_keys<4>(lk, j0, n, k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c += (j0 + e < n && k[e] >= kc) ? 1 : 0;
+        }
+    } else {
+        for (int j = threadIdx.x; j < n; j += NT) c += lk[j] >= kc ? 1 : 0;
+    }
+    return block_sum<NT>(c, sh);
+}
+
 // Ordered compaction of lk[0..n): the rows with key > T and the first need_eq rows with key == T (every
-// row >= T when need_eq >= eq_total), ascending.  Each wave owns a contiguous chunk of whole 64-row
-// groups: it counts its rows with ballots, one barrier shares the per-wave counts, and a second pass
-// writes out[pos] = j and calls visit(pos, j).  Returns the number selected (block-uniform).  lk is
+// row >= T when need_eq >= eq_total), ascending.  Each wave owns a contiguous chunk of whole groups of
+// 64*E keys (E consecutive keys per lane): it counts its rows in registers, one barrier shares the
+// per-wave counts, and a second pass places each group with DPP prefix sums over the lanes' counts,
+// writing out[pos] = j and calling visit(pos, j).  Returns the number selected (block-uniform).  lk is
 // read by other waves while visit runs, so a visitor must not write lk.
-template <int NT = kSelThreads, typename Visit = NoVisit>
-__device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, int eq_total,
-                           int32_t* __restrict__ out, int max_out, FastSel& fs, Visit visit) {
+template <int NT, int E, typename Visit>
+__device__ int compact_lds_e(const uint32_t* lk, int n, uint32_t T, int need_eq, int eq_total,
+                             int32_t* __restrict__ out, int max_out, FastSel& fs, Visit visit) {
+    constexpr int NW = NT / kWave, G = kWave * E;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const bool all_eq = need_eq >= eq_total;
-    constexpr int NW = NT / kWave;
-    const int chunk = (n + NT - 1) / NT * kWave;
+    const int chunk = (n + NW * G - 1) / (NW * G) * G;
     const int lo = min(n, wave * chunk), hi = min(n, lo + chunk);
-    int n_gt = 0, n_eq = 0;
-    for (int j0 = lo; j0 < hi; j0 += kWave) {
-        const int j = j0 + lane;
-        const uint32_t key = j < hi ? lk[j] : 0u;
-        n_gt += __popcll(__ballot(j < hi && key > T));
-        n_eq += __popcll(__ballot(j < hi && key == T));
+    int c_gt = 0, c_eq = 0;
+    for (int j0 = lo + lane * E; j0 < hi; j0 += G) {
+        uint32_t k[E];
+        load_keys<E>(lk, j0, hi, k);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            c_gt += (j0 + e < hi && k[e] > T) ? 1 : 0;
+            c_eq += (j0 + e < hi && k[e] == T) ? 1 : 0;
+        }
     }
     // per-wave counts packed as gt | eq << 16 (each <= n <= 32768), prefix-summed over the waves
-    if (lane == 0) fs.wtot[wave] = n_gt | (n_eq << 16);
+    const int packed = wave_sum_i32(c_gt | (c_eq << 16));
+    if (lane == 0) fs.wtot[wave] = packed;
     __syncthreads();
     const int incl = wave_incl_scan(lane < NW ? fs.wtot[lane] : 0);
     const int before = wave > 0 ? read_lane(incl, wave - 1) : 0;
@@ -351,27 +410,98 @@ __device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, i
     const int gt_tot = total & 0xFFFF, eq_tot = total >> 16;
     const int take = all_eq ? eq_tot : min(eq_tot, need_eq);
     int pos = (before & 0xFFFF) + min(eq_before, take);
-    const uint64_t lt = lanemask_lt();
-    for (int j0 = lo; j0 < hi; j0 += kWave) {
-        const int j = j0 + lane;
-        const uint32_t key = j < hi ? lk[j] : 0u;
-        const bool gt = j < hi && key > T;
-        const bool eq = j < hi && key == T;
-        bool sel = gt || eq;
-        if (!all_eq) {
-            const uint64_t me = __ballot(eq);
-            sel = gt || (eq && eq_before + __popcll(me & lt) < need_eq);
-            eq_before += __popcll(me);
+    for (int g0 = lo; g0 < hi; g0 += G) {  // whole wave in step: the DPP scans need every lane
+        const int j0 = g0 + lane * E;
+        uint32_t k[E];
+        load_keys<E>(lk, j0, hi, k);
+        bool sel[E];
+        int cs = 0;
+        if (all_eq) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                sel[e] = j0 + e < hi && k[e] >= T;
+                cs += sel[e] ? 1 : 0;
+            }
+        } else {
+            int ce = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) ce += (j0 + e < hi && k[e] == T) ? 1 : 0;
+            const int ie = wave_incl_scan(ce);
+            int er = eq_before + ie - ce;  // rank among the equal keys of this lane's first equal key
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool valid = j0 + e < hi;
+                const bool eq = valid && k[e] == T;
+                sel[e] = (valid && k[e] > T) || (eq && er < need_eq);
+                er += eq ? 1 : 0;
+                cs += sel[e] ? 1 : 0;
+            }
+            eq_before += read_lane(ie, kWave - 1);
         }
-        const uint64_t ms = __ballot(sel);
-        const int p = pos + __popcll(ms & lt);
-        if (sel && p < max_out) {
-            out[p] = j;
-            visit(p, j);
+        if (__ballot(cs != 0) == 0) continue;  // nothing selected in this group (uniform)
+        const int is = wave_incl_scan(cs);
+        int p = pos + is - cs;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (sel[e]) {
+                if (p < max_out) {
+                    if (out) out[p] = j0 + e;
+                    visit(p, j0 + e);
+                }
+                ++p;
+            }
         }
-        pos += __popcll(ms);
+        pos += read_lane(is, kWave - 1);
     }
     return gt_tot + take;
+}
+
+template <int NT = kSelThreads, typename Visit = NoVisit>
+__device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, int eq_total,
+                           int32_t* __restrict__ out, int max_out, FastSel& fs, Visit visit) {
+    if (wide_rows<NT>(n)) return compact_lds_e<NT, 4>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
+    return compact_lds_e<NT, 1>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
+}
+
+// Top-kk cut of a long row through a sampled bound.  One key per thread at a fixed stride gives a
+// sample; its r-th largest key L (r = the expected sample count above the cut, plus 2.5 standard
+// deviations and 4) bounds the cut from below when at least kk keys are >= L.  The keys >= L (at
+// most kMaxCand) are copied to LDS and the exact radix select runs on them: every key >= the kk-th
+// largest is among them, so the result is the one the full row would give.  Returns false (nothing
+// decided; run the full radix) when the bound fails either way.  The selection is then every key
+// above *T plus the first *need_eq keys equal to *T, *eq_total keys being equal to it.
+template <int NT = kSelThreads>
+__device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, SelScratch& sh, uint32_t* T_out,
+                                int* need_eq_out, int* eq_total_out) {
+    const int tid = threadIdx.x;
+    if (n < 8 * NT) return false;
+    const double expect = static_cast<double>(kk) * NT / n;
+    const int r = static_cast<int>(expect + 2.5 * sqrt(expect) + 4.0);
+    if (r >= NT) return false;
+    uint32_t* sample = fs.words + kSampleBase;
+    uint32_t* cand = fs.words + kCandBase;
+    sample[tid] = lk[static_cast<int64_t>(tid) * n / NT];
+    __syncthreads();
+    uint32_t L;
+    int ne, et;
+    radix_kth_lds<NT>(sample, NT, r, fs, &L, &ne, &et);  // (an early exit gives a lower L: still a bound)
+    const int c = count_ge_lds<NT>(lk, n, L, sh);
+    if (c < kk || c > kMaxCand) {                        // uniform: c comes from a block sum
+        // the sample's passes left counts in the histograms: the full radix starts from clean ones
+        fast_sel_init(fs);
+        __syncthreads();
+        return false;
+    }
+    fast_sel_init(fs);                                   // fresh histograms for the candidate select
+    auto copy_key = [&](int p, int j) { cand[p] = lk[j]; };
+    compact_lds<NT>(lk, n, L, INT_MAX, INT_MAX, nullptr, kMaxCand, fs, copy_key);
+    __syncthreads();
+    uint32_t T;
+    radix_kth_lds<NT>(cand, c, kk, fs, &T, need_eq_out, eq_total_out);
+    // an early exit leaves T at its bin's lowest value, which may lie below L: every candidate at or
+    // above it is selected, and those are exactly the row's keys >= max(T, L)
+    *T_out = T < L ? L : T;
+    return true;
 }
 
 }  // namespace ig

@@ -52,50 +52,157 @@ struct SpecParams {
     int32_t* victim;
     uint32_t* arrive;  // [B] words: (arrivals << 16) + saturated workgroups; zero between calls
     int xcd_heads;
+    // sliced rows (few rows, or rows longer than one workgroup's LDS): workgroup (slice, row) selects
+    // within rows [slice * slice_rows, +slice_rows) and leaves its candidates; a merge workgroup per
+    // row selects among them.  slices == 1: the row's own workgroup does everything.
+    int slices, slice_rows, cand_cap;
+    uint32_t* cand_key;      // [B*H][slices][cand_cap]
+    int32_t* cand_idx;       // [B*H][slices][cand_cap] row indices
+    int32_t* cand_cnt;       // [B*H][slices]
 };
 
 // Launches the partial-query projection of a speculation call and fills the row kernel's parameters.
 int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s);
 
+constexpr int kSpecMaxSlices = 16;
+
 template <int R>
 struct SpecShared {
     SelScratch sh;
     FastSel fs;
-    float q[R];
+    float q[R < kSpecMaxSlices + 1 ? kSpecMaxSlices + 1 : R];  // partial query; slice offsets in a merge
     int last;
 };
 
+// (b, h) of a row workgroup index: with xcd_heads, groups of adjacent heads go to one XCD with all
+// their batch rows (workgroups are dealt to the 8 XCDs round robin)
+__device__ __forceinline__ void spec_bh(const SpecParams& p, int row_wg, int* b, int* h) {
+    if (p.xcd_heads) {
+        const int G = p.xcd_heads;
+        const int xcd = row_wg % 8, slot = row_wg / 8;
+        const int grp = xcd + 8 * (slot / (p.B * G));
+        const int rem = slot % (p.B * G);
+        *h = grp * G + rem % G;
+        *b = rem / G;
+    } else {
+        *b = row_wg / p.H;
+        *h = row_wg - *b * p.H;
+    }
+}
+
+// Selection over keys[0..m) and its results.  `rows`: the row count the limit refers to (the slice's
+// length in a slice workgroup, n otherwise); gidx(j): the row index of key j.  TO_CANDS: write the
+// selected keys and row indices as this slice's candidates; otherwise write idx / count and update the
+// counters (one integer atomic per selected slot, all in flight together; the last workgroup of
+// sequence b halves if any slot saturated and picks the victim).
+template <bool TO_CANDS, typename GIdx>
+__device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, int slice, int m, int rows,
+                                            uint32_t kmax_all, uint32_t* keys, SelScratch& sh, FastSel& fs,
+                                            int& s_last, GIdx gidx) {
+    const int tid = threadIdx.x;
+    int limit = min(rows, p.max_out);
+    bool done = false;
+    int kk = 0;
+    uint32_t kth = 0;
+    int need_eq = INT_MAX, eq_total = INT_MAX;
+    if (p.mode == IG_SEL_THRESHOLD) {
+        const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
+        const int cnt = count_ge_lds<kSpecThreads>(keys, m, kc, sh);
+        if (p.max_sel > 0) limit = min(limit, p.max_sel);
+        if (cnt <= limit) {
+            kth = kc;
+            done = true;
+        } else {
+            kk = limit;
+        }
+    } else {
+        kk = min(p.k, limit);
+    }
+    if (!done && !sampled_kth_lds(keys, m, kk, fs, sh, &kth, &need_eq, &eq_total))
+        radix_kth_lds(keys, m, kk, fs, &kth, &need_eq, &eq_total);
+
+    if constexpr (TO_CANDS) {
+        const size_t base = (static_cast<size_t>(bh) * p.slices + slice) * p.cand_cap;
+        uint32_t* ck = p.cand_key + base;
+        int32_t* ci = p.cand_idx + base;
+        auto put = [&](int pos, int j) {
+            ck[pos] = keys[j];
+            ci[pos] = gidx(j);
+        };
+        const int written = compact_lds(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put);
+        if (tid == 0) p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = min(written, p.cand_cap);
+        return;
+    } else {
+        const int n = p.n;
+        uint32_t* crow = p.counters ? p.counters + static_cast<size_t>(b) * p.n_cap : nullptr;
+        const uint32_t cmax = p.cmax;
+        uint32_t* stage = fs.stage();  // the select's scratch words are free by now
+        int32_t* out = p.idx + static_cast<size_t>(bh) * p.max_out;
+        auto keep = [&](int pos, int j) {
+            const int g = gidx(j);
+            out[pos] = g;
+            if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(g);
+        };
+        const int written = compact_lds(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
+        if (tid == 0) p.count[bh] = min(written, p.max_out);
+        if (!crow) return;
+        __syncthreads();
+        int sat = 0;
+        // (written <= max_out and every staged index is < n by construction; both are re-checked so
+        // that no counter update can land outside the row)
+        const int touched = min(written, p.max_out);
+        for (int i = tid; i < touched; i += kSpecThreads) {
+            const uint32_t j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
+            if (j >= static_cast<uint32_t>(n)) continue;
+            const uint32_t old = atomicAdd(&crow[j], 1u);
+            if (old + 1u >= cmax) sat = 1;
+        }
+        sat = __syncthreads_or(sat);
+        // Every counter atomic of this workgroup has returned (its value was used) before the barrier,
+        // so it is performed before thread 0's arrival atomic below; atomics are coherent across XCDs,
+        // so no fence (an agent-scope fence writes back the XCD's whole L2) is needed.  One word per
+        // sequence carries the arrivals (high half) and the workgroups that saw a saturation (low half).
+        if (tid == 0) {
+            const uint32_t old = atomicAdd(&p.arrive[b], 0x10000u + (sat ? 1u : 0u));
+            const bool last = (old >> 16) == static_cast<uint32_t>(p.H - 1);
+            s_last = last ? (1 + (((old & 0xFFFFu) + (sat ? 1u : 0u)) != 0u ? 1 : 0)) : 0;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        const bool halve = s_last == 2;
+        // reuse the key storage for the argmin scratch
+        const int v = pool_finish<kSpecThreads>(crow, n, cmax, halve, p.victim != nullptr, keys, &sh.wtot[0]);
+        if (tid == 0) {
+            if (p.victim) p.victim[b] = v;
+            __hip_atomic_store(&p.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Workgroup wg of the speculation launch: one (b, h) row, or (slices > 1) one slice of one row
+// (wg = slice * B*H + row).  Partial query from the projection's split partials, the slice's scores
+// as LDS keys from its partial-key rows, then the selection.
 template <typename T, int LPR, int BATCH = kSpecBatch>
 __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* keys, SpecShared<LPR * Vec<T>::N>& sm) {
     constexpr int VEC = Vec<T>::N;
     constexpr int R = LPR * VEC;               // partial channels per head
     constexpr int RPP = kSpecThreads / LPR;    // rows per pass
-    constexpr int STEP = RPP * BATCH;     // rows per batch
+    constexpr int STEP = RPP * BATCH;          // rows per batch
     SelScratch& sh = sm.sh;
     FastSel& fs = sm.fs;
     float* s_q = sm.q;
-    int& s_last = sm.last;
 
     const int tid = threadIdx.x, li = tid % LPR, ri = tid / LPR;
-    const int lane = tid % kWave, wave = tid / kWave;
+    const int nrow = p.B * p.H;
+    const int slice = p.slices > 1 ? wg / nrow : 0;
     int b, h;
-    if (p.xcd_heads) {
-        // groups of G adjacent heads (G = xcd_heads) go to one XCD with all their batch rows, so the
-        // weight lines those heads share are fetched into a single L2
-        const int G = p.xcd_heads;
-        const int xcd = wg % 8, slot = wg / 8;
-        const int grp = xcd + 8 * (slot / (p.B * G));
-        const int rem = slot % (p.B * G);
-        h = grp * G + rem % G;
-        b = rem / G;
-    } else {
-        b = wg / p.H;
-        h = wg - b * p.H;
-    }
-    const int bh = b * p.H + h, n = p.n;
-    const T* kp = static_cast<const T*>(p.Kp) + static_cast<size_t>(bh) * p.n_cap * R + li * VEC;
+    spec_bh(p, p.slices > 1 ? wg - slice * nrow : wg, &b, &h);
+    const int bh = b * p.H + h;
+    const int r0 = slice * p.slice_rows;
+    const int n = p.slices > 1 ? min(p.n - r0, p.slice_rows) : p.n;  // this workgroup's rows
+    const T* kp = static_cast<const T*>(p.Kp) + (static_cast<size_t>(bh) * p.n_cap + r0) * R + li * VEC;
 
-    fast_sel_init(fs);  // the barriers of the partial-query sum below publish the cleared histograms
+    fast_sel_init(fs);  // the barriers of the partial-query sum publish the cleared histograms
 
     // 1. partial query of this (b, h): sum of the projection kernel's D-slice partials (fixed order),
     //    then the first partial-key batch goes in flight
@@ -106,13 +213,13 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
         cur[u] = j < n ? load_raw16(kp + static_cast<size_t>(j) * R) : make_uint4(0, 0, 0, 0);
     }
     sum_partials<kSpecThreads>(p.part, p.splits, p.B, p.H * R, b, h * R, R, p.bias, s_q, reinterpret_cast<float*>(keys),
-                               p.q_part ? p.q_part + static_cast<size_t>(bh) * R : nullptr);
+                               (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr);
     float q[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) q[v] = s_q[li * VEC + v] * p.scale;
 
     // 2. scores -> LDS keys, double-buffered row batches (the first batch is already in flight)
-    float* srow = p.scores ? p.scores + static_cast<size_t>(bh) * p.ld : nullptr;
+    float* srow = p.scores ? p.scores + static_cast<size_t>(bh) * p.ld + r0 : nullptr;
     uint32_t kmax = 0;
     for (int jb = 0; jb < n; jb += STEP) {
         const bool more = jb + STEP < n;
@@ -146,73 +253,55 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
     }
     const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
 
-    // 3. selection; the compaction also stages the selected indices in LDS (the freed histograms)
-    uint32_t* crow = p.counters ? p.counters + static_cast<size_t>(b) * p.n_cap : nullptr;
-    const uint32_t cmax = p.cmax;
-    uint32_t* stage = fs.stage();
-    auto keep = [&](int pos, int j) {
-        if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(j);
-    };
-    int32_t* out = p.idx + static_cast<size_t>(bh) * p.max_out;
-    int limit = min(n, p.max_out);
-    int written;
-    bool done = false;
-    int kk = 0;
-    uint32_t kth = 0;
-    int need_eq = INT_MAX;
-    if (p.mode == IG_SEL_THRESHOLD) {
-        const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
-        int c = 0;
-        for (int j = tid; j < n; j += kSpecThreads) c += keys[j] >= kc ? 1 : 0;
-        const int cnt = block_sum(c, sh);
-        if (p.max_sel > 0) limit = min(limit, p.max_sel);
-        if (cnt <= limit) {
-            kth = kc;
-            done = true;
-        } else {
-            kk = limit;
-        }
-    } else {
-        kk = min(p.k, limit);
-    }
-    int eq_total = INT_MAX;
-    if (!done) radix_kth_lds(keys, n, kk, fs, &kth, &need_eq, &eq_total);
-    written = compact_lds(keys, n, kth, need_eq, eq_total, out, p.max_out, fs, keep);
-    if (tid == 0) p.count[bh] = min(written, p.max_out);
+    // 3. selection (and, for a whole row, counters)
+    if (p.slices > 1)
+        spec_select<true>(p, b, bh, slice, n, n, kmax_all, keys, sh, fs, sm.last, [&](int j) { return r0 + j; });
+    else
+        spec_select<false>(p, b, bh, 0, n, n, kmax_all, keys, sh, fs, sm.last, [](int j) { return j; });
+}
 
-    // 4. counters: one integer atomic per selected slot, all in flight together; the last workgroup
-    //    of sequence b halves (if any slot saturated) and picks the victim
-    if (!crow) return;
-    __syncthreads();
-    int sat = 0;
-    // (written <= max_out and every staged index is < n by construction; both are re-checked so
-    // that no counter update can land outside the row)
-    const int touched = min(written, p.max_out);
-    for (int i = tid; i < touched; i += kSpecThreads) {
-        const uint32_t j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
-        if (j >= static_cast<uint32_t>(n)) continue;
-        const uint32_t old = atomicAdd(&crow[j], 1u);
-        if (old + 1u >= cmax) sat = 1;
-    }
-    sat = __syncthreads_or(sat);
-    // Every counter atomic of this workgroup has returned (its value was used) before the barrier, so
-    // it is performed before thread 0's arrival atomic below; atomics are coherent across XCDs, so no
-    // fence (an agent-scope fence writes back the XCD's whole L2) is needed.  One word per sequence
-    // carries the arrivals (high half) and the number of workgroups that saw a saturation (low half).
+// Merge workgroup of a sliced row: the row's candidates (every slice's local selection, which together
+// hold the row's selection: a key among the row's top c is among its slice's top c) go to LDS in slice
+// order, which is row order, and the selection runs again over them with the row's rules.
+template <int R>
+__device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t* keys, SpecShared<R>& sm) {
+    SelScratch& sh = sm.sh;
+    FastSel& fs = sm.fs;
+    int* s_off = reinterpret_cast<int*>(sm.q);  // slice offsets (slices + 1 <= R words)
+    const int tid = threadIdx.x;
+    int b, h;
+    spec_bh(p, wg, &b, &h);
+    const int bh = b * p.H + h, S = p.slices;
+    fast_sel_init(fs);
     if (tid == 0) {
-        const uint32_t old = atomicAdd(&p.arrive[b], 0x10000u + (sat ? 1u : 0u));
-        const bool last = (old >> 16) == static_cast<uint32_t>(p.H - 1);
-        s_last = last ? (1 + (((old & 0xFFFFu) + (sat ? 1u : 0u)) != 0u ? 1 : 0)) : 0;
+        int o = 0;
+        for (int sl = 0; sl < S; ++sl) {
+            s_off[sl] = o;
+            o += p.cand_cnt[static_cast<size_t>(bh) * S + sl];
+        }
+        s_off[S] = o;
     }
     __syncthreads();
-    if (!s_last) return;
-    const bool halve = s_last == 2;
-    // reuse the key storage for the argmin scratch
-    const int v = pool_finish<kSpecThreads>(crow, n, cmax, halve, p.victim != nullptr, keys, &sh.wtot[0]);
-    if (tid == 0) {
-        if (p.victim) p.victim[b] = v;
-        __hip_atomic_store(&p.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int m = s_off[S];
+    const size_t base = static_cast<size_t>(bh) * S * p.cand_cap;
+    uint32_t kmax = 0;
+    for (int sl = 0; sl < S; ++sl) {
+        const int o = s_off[sl], c = s_off[sl + 1] - o;
+        const uint32_t* ck = p.cand_key + base + static_cast<size_t>(sl) * p.cand_cap;
+        for (int i = tid; i < c; i += kSpecThreads) {
+            const uint32_t key = ck[i];
+            keys[o + i] = key;
+            kmax = key > kmax ? key : kmax;
+        }
     }
+    const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
+    const int32_t* ci = p.cand_idx + base;
+    auto gidx = [&](int j) {
+        int sl = 0;
+        while (sl + 1 < S && s_off[sl + 1] <= j) ++sl;
+        return static_cast<int>(ci[static_cast<size_t>(sl) * p.cand_cap + (j - s_off[sl])]);
+    };
+    spec_select<false>(p, b, bh, 0, m, p.n, kmax_all, keys, sh, fs, sm.last, gidx);
 }
 
 }  // namespace ig

@@ -68,8 +68,9 @@ static int lpr_of(int len, int dtype) { return len / (dtype == IG_BF16 ? 8 : 4);
 
 bool decode_fusable(const AttnCall& a, const SpecCall& s) {
     const int ls = lpr_of(s.r, s.dtype), la = lpr_of(a.d, a.dtype);
-    return a.dtype == s.dtype && s.n <= kDecodeMaxRows && (ls == 2 || ls == 4 || ls == 8) &&
-           (la == 8 || la == 16 || la == 32);
+    return a.dtype == s.dtype && s.n <= kDecodeMaxRows &&
+           plan_speculate(s.B, s.H, s.D, s.r, s.n, s.max_out, s.dtype).slices == 1 &&
+           (ls == 2 || ls == 4 || ls == 8) && (la == 8 || la == 16 || la == 32);
 }
 
 template <typename T, int LPR_S>

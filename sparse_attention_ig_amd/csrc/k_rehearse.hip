@@ -19,7 +19,7 @@ namespace ig {
 
 constexpr int kProjThreads = 256;
 constexpr int kScoreThreads = 256;
-constexpr int kScoreUnroll = 4;
+constexpr int kScoreUnroll = 8;  // partial-key rows per lane group per batch
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -100,37 +100,48 @@ __global__ __launch_bounds__(kScoreThreads) void k_rehearse_score(
     const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
     const int N = H * r;
     const int tid = threadIdx.x;
-    sum_partials<kScoreThreads>(part, splits, B, N, b, h * r, r, bias, qs, s_part,
-                                blockIdx.x == 0 ? q_part + static_cast<size_t>(bh) * r : nullptr);
-
     const int li = tid % LPR, ri = tid / LPR;
+    const T* base = Kp + static_cast<size_t>(bh) * n_cap * r + li * VEC;
+    float* srow = scores + static_cast<size_t>(bh) * ld;
+    const int j0 = blockIdx.x * chunk, j1 = min(n, j0 + chunk);
+    // kScoreUnroll rows per lane group per batch, two batches in flight (double buffering); the first
+    // batch goes out before the partial sums are read
+    constexpr int STEP = RPI * kScoreUnroll;
+    uint4 cur[kScoreUnroll], nxt[kScoreUnroll];
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+        const int j = j0 + u * RPI + ri;
+        cur[u] = j < j1 ? load_raw16(base + static_cast<size_t>(j) * r) : make_uint4(0, 0, 0, 0);
+    }
+    sum_partials<kScoreThreads>(part, splits, B, N, b, h * r, r, bias, qs, s_part,
+                                (blockIdx.x == 0 && q_part) ? q_part + static_cast<size_t>(bh) * r : nullptr);
     float q[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) q[v] = qs[li * VEC + v] * scale;
 
-    const T* base = Kp + static_cast<size_t>(bh) * n_cap * r + li * VEC;
-    float* srow = scores + static_cast<size_t>(bh) * ld;
-    const int j0 = blockIdx.x * chunk, j1 = min(n, j0 + chunk);
-    for (int jb = j0; jb < j1; jb += RPI * kScoreUnroll) {
-        float kv[kScoreUnroll][VEC];
+    for (int jb = j0; jb < j1; jb += STEP) {
+        const bool more = jb + STEP < j1;
+        if (more) {
 #pragma unroll
-        for (int u = 0; u < kScoreUnroll; ++u) {
-            const int j = jb + u * RPI + ri;
-            if (j < j1) {
-                load_vec(base + static_cast<size_t>(j) * r, kv[u]);
-            } else {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) kv[u][v] = 0.f;
+            for (int u = 0; u < kScoreUnroll; ++u) {
+                const int j = jb + STEP + u * RPI + ri;
+                nxt[u] = j < j1 ? load_raw16(base + static_cast<size_t>(j) * r) : make_uint4(0, 0, 0, 0);
             }
         }
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
-            float s = 0.f;
+            float kv[VEC];
+            unpack_raw(cur[u], kv);
+            float sc = 0.f;
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) s = fmaf(q[v], kv[u][v], s);
-            s = group_sum<LPR>(s);
+            for (int v = 0; v < VEC; ++v) sc = fmaf(q[v], kv[v], sc);
+            sc = group_sum<LPR>(sc);
             const int j = jb + u * RPI + ri;
-            if (li == 0 && j < j1) srow[j] = s;
+            if (li == 0 && j < j1) srow[j] = sc;
+        }
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < kScoreUnroll; ++u) cur[u] = nxt[u];
         }
     }
 }
@@ -196,6 +207,15 @@ static int launch_score_t(const float* part, const float* bias, const T* Kp, int
     }
 #undef IG_SCORE_CASE
     return static_cast<int>(hipGetLastError());
+}
+
+int launch_score(const float* part, const float* bias, const void* Kp, int B, int H, int r, int n, int n_cap,
+                 int dtype, float scale, float* q_part, float* scores, int ld, const RehearsePlan& p, hipStream_t s) {
+    if (dtype == IG_BF16)
+        return launch_score_t(part, bias, static_cast<const uint16_t*>(Kp), B, H, r, n, n_cap, scale, q_part, scores,
+                              ld, p, s);
+    return launch_score_t(part, bias, static_cast<const float*>(Kp), B, H, r, n, n_cap, scale, q_part, scores, ld, p,
+                          s);
 }
 
 int launch_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D,

@@ -25,7 +25,7 @@ template <bool IN_LDS>
 __global__ __launch_bounds__(kSelThreads) void k_select(
     const float* __restrict__ scores, int H, int n, int ld, int mode, float alpha, int k, int max_sel,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, int max_out, int32_t* __restrict__ head_counts) {
-    __shared__ __align__(16) uint32_t lk[IN_LDS ? kSelLdsKeys : 1];
+    extern __shared__ __align__(16) uint32_t lk[];  // IN_LDS: the row's n keys (dynamic, n <= 32768)
     __shared__ SelScratch sh;
     __shared__ std::conditional_t<IN_LDS, FastSel, int> fs;
     const int bh = blockIdx.x, tid = threadIdx.x;
@@ -45,9 +45,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     if (mode == IG_SEL_THRESHOLD || mode == kSelCountOnly) {
         const float cut = key_score(kmax_all) - alpha;
         const uint32_t kc = score_key(cut);
-        int c = 0;
-        for_each_key<IN_LDS>(srow, lk, n, [&](int, uint32_t key) { c += key >= kc ? 1 : 0; });
-        const int cnt = block_sum(c, sh);
+        int cnt;
+        if constexpr (IN_LDS) {
+            cnt = count_ge_lds(lk, n, kc, sh);
+        } else {
+            int c = 0;
+            for_each_key<IN_LDS>(srow, lk, n, [&](int, uint32_t key) { c += key >= kc ? 1 : 0; });
+            cnt = block_sum(c, sh);
+        }
         if (mode == kSelCountOnly) {
             if (tid == 0) head_counts[bh] = cnt;
             return;
@@ -80,7 +85,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     int need_eq, w;
     if constexpr (IN_LDS) {
         int eq_total;
-        radix_kth_lds(lk, n, kk, fs, &T, &need_eq, &eq_total);
+        if (!sampled_kth_lds(lk, n, kk, fs, sh, &T, &need_eq, &eq_total))
+            radix_kth_lds(lk, n, kk, fs, &T, &need_eq, &eq_total);
         w = compact_lds(lk, n, T, need_eq, eq_total, idx + static_cast<size_t>(bh) * max_out, max_out, fs,
                         NoVisit());
     } else {
@@ -101,23 +107,27 @@ int launch_select(const float* scores, int B, int H, int n, int ld, int mode, fl
     const dim3 grid(B * H), block(kSelThreads);
     int32_t* hc = static_cast<int32_t*>(ws);
     const bool lds = n <= kSelLdsKeys;
-    if (mode == IG_SEL_HEADAVG) {
+    static bool attr_set = false;  // dynamic LDS above 64 KB needs the per-function limit raised once
+    if (lds && !attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<true>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(kSelLdsKeys * sizeof(uint32_t)));
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr_set = true;
+    }
+    const size_t dyn = lds ? static_cast<size_t>(n) * sizeof(uint32_t) : 0;
+    for (int pass = mode == IG_SEL_HEADAVG ? 0 : 1; pass < 2; ++pass) {
+        const int m = pass == 0 ? kSelCountOnly : mode;  // the head average counts every head first
         if (lds)
-            hipLaunchKernelGGL((k_select<true>), grid, block, 0, s, scores, H, n, ld, kSelCountOnly, alpha, k,
-                               max_sel, idx, count, max_out, hc);
+            hipLaunchKernelGGL((k_select<true>), grid, block, dyn, s, scores, H, n, ld, m, alpha, k, max_sel, idx,
+                               count, max_out, hc);
         else
-            hipLaunchKernelGGL((k_select<false>), grid, block, 0, s, scores, H, n, ld, kSelCountOnly, alpha, k,
-                               max_sel, idx, count, max_out, hc);
+            hipLaunchKernelGGL((k_select<false>), grid, block, 0, s, scores, H, n, ld, m, alpha, k, max_sel, idx,
+                               count, max_out, hc);
         const int e = static_cast<int>(hipGetLastError());
         if (e) return e;
     }
-    if (lds)
-        hipLaunchKernelGGL((k_select<true>), grid, block, 0, s, scores, H, n, ld, mode, alpha, k, max_sel, idx,
-                           count, max_out, hc);
-    else
-        hipLaunchKernelGGL((k_select<false>), grid, block, 0, s, scores, H, n, ld, mode, alpha, k, max_sel, idx,
-                           count, max_out, hc);
-    return static_cast<int>(hipGetLastError());
+    return 0;
 }
 
 }  // namespace ig

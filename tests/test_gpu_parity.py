@@ -300,15 +300,18 @@ def test_determinism():
             assert np.array_equal(runs[0]["idx"][b, h, :c], runs[1]["idx"][b, h, :c])
 
 
-def test_long_context_full_size_sampled():
+@pytest.mark.parametrize("path", ["unfused", "fused"])
+def test_long_context_full_size_sampled(path):
     """Llama-2-7B-shaped layer at 131072 rows, top 1%: every head's scores and the sampled heads'
-    selection and attention against the oracle."""
+    selection and attention against the oracle.  The fused speculation cuts each row into slices
+    (one workgroup each, candidates merged per row)."""
     spec = gen.llama2_7b_long(n=131072, B=1, frac=0.01)
-    say(f"[long full] n={spec.n} k={spec.topk}")
+    say(f"[long full {path}] n={spec.n} k={spec.topk}")
     li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
     assert harness.compare_inputs(li, oi)["chan"] == 0
-    layer = DeviceLayer(li)
-    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk))
+    layer = DeviceLayer(li, max_out=spec.topk)
+    parts = DeviceLayer.FUSED if path == "fused" else DeviceLayer.PARTS
+    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, parts=parts))
     say("[long full] gpu step done")
     heads = [(0, 0), (0, 13), (0, 31)]
     ref = harness.oracle_step(oi, mode="topk", k=spec.topk, max_out=spec.topk, heads=heads)
