@@ -23,6 +23,7 @@
 #pragma once
 
 #include <climits>
+#include <type_traits>
 
 #include "ig_internal.h"
 #include "ig_pool_dev.h"
@@ -90,6 +91,11 @@ __device__ __forceinline__ void spec_bh(const SpecParams& p, int row_wg, int* b,
     }
 }
 
+// Row index of key j for a whole row (the key's own position).
+struct IdentityIdx {
+    __device__ __forceinline__ int operator()(int j) const { return j; }
+};
+
 // Selection over keys[0..m) and its results.  `rows`: the row count the limit refers to (the slice's
 // length in a slice workgroup, n otherwise); gidx(j): the row index of key j.  TO_CANDS: write the
 // selected keys and row indices as this slice's candidates; otherwise write idx / count and update the
@@ -138,24 +144,67 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
         const uint32_t cmax = p.cmax;
         uint32_t* stage = fs.stage();  // the select's scratch words are free by now
         int32_t* out = p.idx + static_cast<size_t>(bh) * p.max_out;
-        auto keep = [&](int pos, int j) {
-            const int g = gidx(j);
-            out[pos] = g;
-            if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(g);
-        };
-        const int written = compact_lds(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
+        int written;
+        if constexpr (std::is_same<GIdx, IdentityIdx>::value) {
+            auto keep = [&](int pos, int j) {
+                out[pos] = j;
+                if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(j);
+            };
+            written = compact_lds(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
+        } else {
+            // key positions first, then every position mapped to its row index with batched loads
+            written = compact_lds(keys, m, kth, need_eq, eq_total, out, p.max_out, fs, NoVisit());
+            __syncthreads();
+            const int w = min(written, p.max_out);
+            constexpr int U = 8;
+            for (int i0 = tid; i0 < w; i0 += kSpecThreads * U) {
+                int pos[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) pos[u] = i0 + u * kSpecThreads < w ? out[i0 + u * kSpecThreads] : 0;
+                int g[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) g[u] = i0 + u * kSpecThreads < w ? gidx(pos[u]) : 0;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = i0 + u * kSpecThreads;
+                    if (i < w) {
+                        out[i] = g[u];
+                        if (i < kFastStage) stage[i] = static_cast<uint32_t>(g[u]);
+                    }
+                }
+            }
+        }
         if (tid == 0) p.count[bh] = min(written, p.max_out);
         if (!crow) return;
         __syncthreads();
         int sat = 0;
         // (written <= max_out and every staged index is < n by construction; both are re-checked so
         // that no counter update can land outside the row)
+        // at most one atomic per lane when the selection is small, else 8 per lane in flight at a time,
+        // their returns checked afterwards
         const int touched = min(written, p.max_out);
-        for (int i = tid; i < touched; i += kSpecThreads) {
-            const uint32_t j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
-            if (j >= static_cast<uint32_t>(n)) continue;
-            const uint32_t old = atomicAdd(&crow[j], 1u);
-            if (old + 1u >= cmax) sat = 1;
+        if (touched <= kSpecThreads) {
+            if (tid < touched) {
+                const uint32_t j = tid < kFastStage ? stage[tid] : static_cast<uint32_t>(out[tid]);
+                if (j < static_cast<uint32_t>(n) && atomicAdd(&crow[j], 1u) + 1u >= cmax) sat = 1;
+            }
+        } else {
+        constexpr int U = 8;
+        for (int i0 = tid; i0 < touched; i0 += kSpecThreads * U) {
+            uint32_t old[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * kSpecThreads;
+                uint32_t j = 0xFFFFFFFFu;
+                if (i < touched) j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
+                old[u] = j < static_cast<uint32_t>(n) ? atomicAdd(&crow[j], 1u) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * kSpecThreads;
+                if (i < touched && old[u] + 1u >= cmax) sat = 1;
+            }
+        }
         }
         sat = __syncthreads_or(sat);
         // Every counter atomic of this workgroup has returned (its value was used) before the barrier,
@@ -257,7 +306,7 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
     if (p.slices > 1)
         spec_select<true>(p, b, bh, slice, n, n, kmax_all, keys, sh, fs, sm.last, [&](int j) { return r0 + j; });
     else
-        spec_select<false>(p, b, bh, 0, n, n, kmax_all, keys, sh, fs, sm.last, [](int j) { return j; });
+        spec_select<false>(p, b, bh, 0, n, n, kmax_all, keys, sh, fs, sm.last, IdentityIdx());
 }
 
 // Merge workgroup of a sliced row: the row's candidates (every slice's local selection, which together
@@ -288,10 +337,18 @@ __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t
     for (int sl = 0; sl < S; ++sl) {
         const int o = s_off[sl], c = s_off[sl + 1] - o;
         const uint32_t* ck = p.cand_key + base + static_cast<size_t>(sl) * p.cand_cap;
-        for (int i = tid; i < c; i += kSpecThreads) {
-            const uint32_t key = ck[i];
-            keys[o + i] = key;
-            kmax = key > kmax ? key : kmax;
+        constexpr int U = 8;  // 8 loads per lane in flight
+        for (int i0 = tid; i0 < c; i0 += kSpecThreads * U) {
+            uint32_t v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < c ? ck[i0 + u * kSpecThreads] : 0u;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (i0 + u * kSpecThreads < c) {
+                    keys[o + i0 + u * kSpecThreads] = v[u];
+                    kmax = v[u] > kmax ? v[u] : kmax;
+                }
+            }
         }
     }
     const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
