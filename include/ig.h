@@ -47,13 +47,14 @@ extern "C" {
 enum { IG_OK = 0, IG_EINVAL = 1, IG_EHIP = 2, IG_EUNSUPPORTED = 3 };
 enum { IG_F32 = 0, IG_BF16 = 1 };
 enum { IG_SEL_THRESHOLD = 0, IG_SEL_TOPK = 1, IG_SEL_HEADAVG = 2 };
-enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3, IG_OP_TOUCH = 4 };
+enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3, IG_OP_TOUCH = 4,
+       IG_OP_SETUP = 5 };
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* ig_last_error(void);
 /* ABI version: bumped on any signature or layout change (2: ig_pool_touch takes a
  * workspace; 3: Wq_part is stored one row per partial column, [H*r][D];
- * 4: ig_decode_layer). */
+ * 4: ig_decode_layer; 5: ig_partial_weight_index_dev). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -118,6 +119,22 @@ int ig_partial_weight_index(const void* Wq_s, int D, int H, int d, int r,
                             int32_t* chan, void* Wq_part, int nthreads);
 
 /* ------------------------------------------------------------------ device calls */
+
+/*
+ * ig_partial_weight_index on the GPU (section 3.4, "Prefill Stage: Partial
+ * Weight Index Generation", steps 2-3), so that the prefill setup and the
+ * cache growth (ig_build_partial_cache, ig_append_kv) never leave the device.
+ * Same definition and outputs: per head, score[c] = sum_i |Wq_s[i][h*d+c]| +
+ * sum_{b, j<n} |K_s[b][h][j][c]| in float64 (partial sums over fixed slices,
+ * added in a fixed order, so the result is deterministic; it can differ from
+ * the host routine only where two channel scores agree to rounding), the r
+ * largest (ties: lower channel) in ascending order to chan [H][r], and
+ * Wq_part [H*r][D] = the chosen columns, one row per channel.  Device
+ * pointers; workspace IG_OP_SETUP bytes (B, H, D, d, n used).
+ */
+int ig_partial_weight_index_dev(const void* Wq_s, int D, int H, int d, int r, const void* K_s, int B, int n_cap,
+                                int n, int dtype, int32_t* chan, void* Wq_part, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /*
  * Bytes of scratch a call needs (0 if none).  op = IG_OP_REHEARSE: B, H, D,

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libig.so")
 IG_OK, IG_EINVAL, IG_EHIP, IG_EUNSUPPORTED = 0, 1, 2, 3
 IG_F32, IG_BF16 = 0, 1
 IG_SEL_THRESHOLD, IG_SEL_TOPK, IG_SEL_HEADAVG = 0, 1, 2
-IG_OP_REHEARSE, IG_OP_SELECT, IG_OP_ATTN, IG_OP_SPECULATE, IG_OP_TOUCH = 0, 1, 2, 3, 4
+IG_OP_REHEARSE, IG_OP_SELECT, IG_OP_ATTN, IG_OP_SPECULATE, IG_OP_TOUCH, IG_OP_SETUP = 0, 1, 2, 3, 4, 5
 
 _MODES = {"threshold": IG_SEL_THRESHOLD, "topk": IG_SEL_TOPK, "headavg": IG_SEL_HEADAVG}
 
@@ -69,6 +69,7 @@ _SIGS = {
     "ig_sparse_decode_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "ig_pool_touch": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _u32, _vp, _vp, _sz, _vp]),
     "ig_decode_layer": (_i, [_i, _i, _i, _i, ctypes.POINTER(AttnCall), ctypes.POINTER(SpecCall), _vp]),
+    "ig_partial_weight_index_dev": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "ig_build_partial_cache": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "ig_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
 }
@@ -301,6 +302,23 @@ def ig_sparse_decode_attn(q, K, V, idx, count, scale: float, *, max_out=None, ou
                                         _dtype_of(q), float(scale), _ptr(out), _ptr(lse), _ptr(ws), wsb,
                                         _stream(stream)), "ig_sparse_decode_attn")
     return out, lse
+
+
+def ig_partial_weight_index_dev(Wq_s, K_s, r: int, n: int, *, chan=None, Wq_part=None, ws=None, stream=None):
+    """Device tensors: Wq_s [D][H*d], K_s [B][H][n_cap][d]; returns chan [H][r] int32 and
+    Wq_part [H*r][D] (device)."""
+    torch = _torch()
+    D = Wq_s.shape[0]
+    B, H, n_cap, d = K_s.shape
+    if chan is None:
+        chan = torch.empty((H, r), dtype=torch.int32, device=Wq_s.device)
+    if Wq_part is None:
+        Wq_part = torch.empty((H * r, D), dtype=Wq_s.dtype, device=Wq_s.device)
+    ws, wsb = _ws(ws, ig_workspace_size(IG_OP_SETUP, B, H, D, d, r, n, 0), Wq_s.device)
+    _check(load().ig_partial_weight_index_dev(_ptr(Wq_s), D, H, d, r, _ptr(K_s), B, n_cap, int(n), _dtype_of(Wq_s),
+                                              _ptr(chan), _ptr(Wq_part), _ptr(ws), wsb, _stream(stream)),
+           "ig_partial_weight_index_dev")
+    return chan, Wq_part
 
 
 def ig_decode_layer(attn: Optional[dict] = None, spec: Optional[dict] = None, *, stream=None):

@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 4; }
+int ig_version(void) { return 5; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 
@@ -94,6 +94,9 @@ size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int m
         case IG_OP_SPECULATE:
             if (D < 1 || r < 1 || n < 1) return 0;
             return speculate_ws_bytes(B, H, D, r, n, max_out, IG_BF16);
+        case IG_OP_SETUP:
+            if (D < 1 || d < 1 || n < 1) return 0;
+            return plan_setup(B, H, d, D, n).ws_bytes;
         default:
             return 0;
     }
@@ -222,6 +225,22 @@ int ig_sparse_decode_attn(const void* q, const void* K, const void* V, int ld_ro
     const AttnCall c{q, K, V, ld_rows, idx, count, B, H, d, max_out, dtype, scale, out, lse, ws};
     if (const int e = check_attn("ig_sparse_decode_attn", c, ws_bytes)) return e;
     return hip_status(launch_decode_layer(&c, nullptr, stream), "ig_sparse_decode_attn");
+}
+
+int ig_partial_weight_index_dev(const void* Wq_s, int D, int H, int d, int r, const void* K_s, int B, int n_cap,
+                                int n, int dtype, int32_t* chan, void* Wq_part, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_partial_weight_index_dev", dtype);
+    IG_REQUIRE(Wq_s && K_s && chan && Wq_part, "ig_partial_weight_index_dev: NULL required pointer");
+    IG_REQUIRE(D >= 1 && H >= 1 && B >= 1 && r >= 1 && r <= d && n >= 1 && n <= n_cap,
+               "ig_partial_weight_index_dev: bad sizes (D=%d H=%d d=%d r=%d B=%d n=%d n_cap=%d)", D, H, d, r, B, n,
+               n_cap);
+    IG_REQUIRE(head_dim_ok(d, dtype), "ig_partial_weight_index_dev: unsupported head dim %d", d);
+    const size_t need = plan_setup(B, H, d, D, n).ws_bytes;
+    IG_REQUIRE(ws && ws_bytes >= need && aligned16(ws),
+               "ig_partial_weight_index_dev: workspace of %zu bytes needed (16-byte aligned)", need);
+    return hip_status(launch_setup(Wq_s, D, H, d, r, K_s, B, n_cap, n, dtype, chan, Wq_part, ws, stream),
+                      "ig_partial_weight_index_dev");
 }
 
 int ig_decode_layer(int B, int H, int d, int dtype, const ig_attn_call* attn, const ig_spec_call* spec,

@@ -81,6 +81,16 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
 int launch_zero(void* ws, size_t bytes, hipStream_t s);
 int launch_attn_combine(const float* part, int nsplit, int d, int BH, float* out, float* lse, hipStream_t s);
 
+// device-side partial weight index: float64 column-sum partials of |W~_Q| ([wslices][H*d]) and |K~|
+// ([B*kchunks][H][d]) in the workspace
+struct SetupPlan {
+    int wslices, kchunks;
+    size_t off_k, ws_bytes;
+};
+SetupPlan plan_setup(int B, int H, int d, int D, int n);
+int launch_setup(const void* Wq_s, int D, int H, int d, int r, const void* K_s, int B, int n_cap, int n, int dtype,
+                 int32_t* chan, void* Wq_part, void* ws, hipStream_t s);
+
 // host-side descriptors of the two halves of a decode layer (the arguments of launch_attn and
 // launch_speculate)
 struct AttnCall {
