@@ -59,7 +59,12 @@ class DecodePipeline:
                                  n=n, x=x_layers[l])
             L.ig_decode_layer(attn, spec, stream=stream)
         if append:
-            for l, lay in enumerate(self.layers):
-                L.ig_append_kv(lay.K, lay.V, lay.Kp, lay.counters, lay.chan, k_new[l], v_new[l], n,
-                               slot_out=self.slot, stream=stream)
-            self.n = min(n + 1, s.cap)
+            self.append(k_new, v_new, stream=stream)
+
+    def append(self, k_new, v_new, *, stream=None):
+        """Every layer appends the new token's key and value rows (slot n, or the victim when full)."""
+        n = self.n
+        for l, lay in enumerate(self.layers):
+            L.ig_append_kv(lay.K, lay.V, lay.Kp, lay.counters, lay.chan, k_new[l], v_new[l], n,
+                           slot_out=self.slot, stream=stream)
+        self.n = min(n + 1, self.spec.cap)

@@ -48,7 +48,7 @@ def oracle_inputs(spec: gen.Spec, layer: int = 0, lay: Optional[gen.Layer] = Non
     chan = O.partial_weight_index(Wq_s, K, H, d, r, spec.n, dtype=spec.dtype)
     Wq_part = O.pack_partial_weight(Wq_s, chan, d)
     return Inputs(spec, lay.x, Wq_part, chan, q.reshape(B, H, d), K, V,
-                  extra={"A": A, "heavy": heavy, "Kp": O.partial_key_cache(K, chan)})
+                  extra={"A": A, "heavy": heavy, "Kp": O.partial_key_cache(K, chan), "Wq_s": Wq_s})
 
 
 def ulp_mismatch(a: np.ndarray, b: np.ndarray) -> int:
