@@ -54,7 +54,8 @@ enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3
 const char* ig_last_error(void);
 /* ABI version: bumped on any signature or layout change (2: ig_pool_touch takes a
  * workspace; 3: Wq_part is stored one row per partial column, [H*r][D];
- * 4: ig_decode_layer; 5: ig_partial_weight_index_dev). */
+ * 4: ig_decode_layer; 5: ig_partial_weight_index_dev; 6: the speculation
+ * workspace starts with its arrival words). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -179,11 +180,12 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * min(slice rows, max_out)) would exceed 32768.
  * q_part [B][H][r] and scores [B][H][ld] are written only when not NULL.
  * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
- * receives the victim.  Two launches: the partial-query projection, then one
- * workgroup per (b, h) for scores, selection and counters (three with slices:
- * the slices, then the merges).  The workspace (IG_OP_SPECULATE bytes,
- * required) holds the projection's partial sums, one arrival word per
- * sequence and the slices' candidates; it must have been zero-filled once with
+ * receives the victim.  One launch of one workgroup per (b, h), which projects
+ * its own partial query and then scores, selects and updates the counters (two
+ * launches with slices: the slices, then the merges).  D * element size must
+ * not exceed 131072 bytes.  The workspace (IG_OP_SPECULATE bytes, required)
+ * starts with one uint32 arrival word per sequence ([B] at offset 0), followed
+ * by the slices' candidates; it must have been zero-filled once with
  * ig_workspace_init, and every call returns the arrival words to zero.  Calls
  * sharing a workspace must not overlap.  H <= 65535.
  */
@@ -202,15 +204,16 @@ int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const
  * layer l over the rows selected for it, and the speculation for layer l+1.
  * `attn` holds the arguments of ig_sparse_decode_attn for layer l, `spec` those
  * of ig_speculate for layer l+1 (B, H, dtype shared; d is the attention's head
- * dim); either may be NULL (then this is that one call).  With both: the
- * projection of ig_speculate, then one launch in which the speculation's
- * (b, h) workgroups and the attention's run side by side (no ordering between
+ * dim); either may be NULL (then this is that one call).  With both: one
+ * launch in which the speculation's (b, h) workgroups and the attention's run
+ * side by side (no ordering between
  * the two halves, so spec->idx, count, counters, victim, q_part, scores must not
  * alias anything attn reads), then the split combine of the attention if it
  * splits.  Results: those of the two calls (the attention's float sums may
  * associate differently).  Falls back to the two calls in sequence for shapes
  * outside the fused set (spec r / (16 / element size) in {2, 4, 8}, attn d /
- * (16 / element size) in {8, 16, 32}, spec n <= 16384).
+ * (16 / element size) in {8, 16, 32}, spec n <= 16384 without slices, spec
+ * D * element size <= 65536 bytes).
  */
 typedef struct {
     const void* q;

@@ -45,14 +45,13 @@ size_t select_ws_bytes(int B, int H, int n, int max_out);
 
 constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
 struct SpecPlan {
-    RehearsePlan rp;
     int slices, slice_rows, cand_cap;
     bool ok;                          // false: rows too long for the candidates to fit one merge
     size_t off_arrive, off_cnt, off_key, off_idx, ws_bytes;
 };
 SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);
-size_t speculate_lds_bytes(int n);
+size_t speculate_lds_bytes(int n, int x_bytes);
 
 // kernel launchers (return hipError_t as int)
 int launch_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,

@@ -4,9 +4,9 @@
 // scores, threshold or top-k selection, and the access-counter update.
 //
 // One 1024-thread workgroup per (b, h); scores never leave the chip.
-//  0. A projection kernel (k_rehearse_proj, shared with ig_rehearse) reads the
-//     partial query weight once and leaves fixed-order split partials.
-//  1. The workgroup sums its (b, h) partials into the partial query.
+//  1. The workgroup projects its own partial query: x[b] staged in LDS, the
+//     head's r rows of the partial weight read along D by groups of lanes
+//     (the batch rows of a head share those rows through the L2 cache).
 //  2. Scores of every cached row go to LDS as order-preserving keys (and to
 //     HBM only if the caller asks for them), streaming the partial-key rows in
 //     double-buffered batches of 8 rows x 16 bytes per lane.
@@ -19,7 +19,7 @@
 //
 // The workgroup index `wg` of the row is passed in (the fused decode kernel
 // runs rows after other roles' workgroups); the caller provides the LDS:
-// `keys` holds max(n, 1024) words, `sm` the fixed scratch.
+// `keys` holds max(n, 1024, D * element size / 4) words, `sm` the fixed scratch.
 #pragma once
 
 #include <climits>
@@ -35,8 +35,9 @@ constexpr int kSpecThreads = 1024;
 constexpr int kSpecBatch = 8;  // default partial-key rows per lane per batch
 
 struct SpecParams {
-    const float* part;   // [splits][B][H*r] partial sums of the projection kernel
-    int splits;
+    const void* x;       // [B][D] attention input
+    const void* W;       // [H*r][D] partial query weight (one row per partial column)
+    int D;
     const float* bias;
     const void* Kp;
     int B, H, r, n, n_cap, ld;
@@ -62,8 +63,8 @@ struct SpecParams {
     int32_t* cand_cnt;       // [B*H][slices]
 };
 
-// Launches the partial-query projection of a speculation call and fills the row kernel's parameters.
-int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s);
+// Fills the row kernel's parameters of a speculation call.
+void begin_speculate(const SpecCall& c, SpecParams* p);
 
 constexpr int kSpecMaxSlices = 16;
 
@@ -74,6 +75,55 @@ struct SpecShared {
     float q[R < kSpecMaxSlices + 1 ? kSpecMaxSlices + 1 : R];  // partial query; slice offsets in a merge
     int last;
 };
+
+// Partial query of one (b, h) inside its workgroup (summary section 3.4 "Decoding Stage" step 1):
+// q[c] = x . W[c] (+ bias[c]) for c < R, W the head's R rows of D inputs.  x is staged in LDS (xs, D
+// elements); row c is read by a group of G = min(64, NT / R) lanes, 16 bytes per lane per step along D
+// with U steps in flight, and the group's partial sums are added by DPP in a fixed order.  Ends with a
+// barrier; q (and q_out, when not NULL) then hold the sums.
+template <typename T, int NT, int R, int U>
+__device__ __forceinline__ void project_partial(const T* __restrict__ x, const T* __restrict__ W, int D,
+                                                const float* __restrict__ bias, uint4* xs, float* q, float* q_out) {
+    constexpr int VEC = Vec<T>::N;
+    constexpr int G = NT / R < 64 ? NT / R : 64;
+    static_assert(G >= 1, "at most one partial channel per thread");
+    const int tid = threadIdx.x;
+    const int nv = D / VEC;  // D is a multiple of VEC and both operands are 16-byte aligned
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    for (int i = tid; i < nv; i += NT) xs[i] = xv[i];
+    __syncthreads();
+    const int c = tid / G, g = tid % G;
+    float acc = 0.f;
+    if (c < R) {
+        const uint4* wv = reinterpret_cast<const uint4*>(W + static_cast<size_t>(c) * D);
+        for (int i0 = g; i0 < nv; i0 += G * U) {
+            uint4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * G;
+                w[u] = i < nv ? wv[i] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * G;
+                if (i < nv) {
+                    float a[VEC], xe[VEC];
+                    unpack_raw(w[u], a);
+                    unpack_raw(xs[i], xe);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc = fmaf(xe[v], a[v], acc);
+                }
+            }
+        }
+    }
+    acc = group_sum<G>(acc);  // whole groups: threads past R * G hold zeros in groups of their own
+    if (c < R && g == 0) {
+        const float v = bias ? acc + bias[c] : acc;
+        q[c] = v;
+        if (q_out) q_out[c] = v;
+    }
+    __syncthreads();
+}
 
 // (b, h) of a row workgroup index: with xcd_heads, groups of adjacent heads go to one XCD with all
 // their batch rows (workgroups are dealt to the 8 XCDs round robin)
@@ -229,9 +279,11 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
 }
 
 // Workgroup wg of the speculation launch: one (b, h) row, or (slices > 1) one slice of one row
-// (wg = slice * B*H + row).  Partial query from the projection's split partials, the slice's scores
-// as LDS keys from its partial-key rows, then the selection.
-template <typename T, int LPR, int BATCH = kSpecBatch>
+// (wg = slice * B*H + row).  The partial query projected in the workgroup, the slice's scores as LDS
+// keys from its partial-key rows, then the selection.
+// PU: partial-weight loads per lane in flight during the projection; PRE: the first partial-key batch
+// is issued before the projection (it then holds registers through it).
+template <typename T, int LPR, int BATCH = kSpecBatch, int PU = BATCH, bool PRE = true>
 __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* keys, SpecShared<LPR * Vec<T>::N>& sm) {
     constexpr int VEC = Vec<T>::N;
     constexpr int R = LPR * VEC;               // partial channels per head
@@ -253,16 +305,26 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
 
     fast_sel_init(fs);  // the barriers of the partial-query sum publish the cleared histograms
 
-    // 1. partial query of this (b, h): sum of the projection kernel's D-slice partials (fixed order),
-    //    then the first partial-key batch goes in flight
+    // 1. the partial query of this (b, h), with the first partial-key batch in flight (PRE) or after
     uint4 cur[BATCH], nxt[BATCH];
+    if constexpr (PRE) {
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-        const int j = u * RPP + ri;
-        cur[u] = j < n ? load_raw16(kp + static_cast<size_t>(j) * R) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < BATCH; ++u) {
+            const int j = u * RPP + ri;
+            cur[u] = j < n ? load_raw16(kp + static_cast<size_t>(j) * R) : make_uint4(0, 0, 0, 0);
+        }
     }
-    sum_partials<kSpecThreads>(p.part, p.splits, p.B, p.H * R, b, h * R, R, p.bias, s_q, reinterpret_cast<float*>(keys),
-                               (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr);
+    project_partial<T, kSpecThreads, R, PU>(static_cast<const T*>(p.x) + static_cast<size_t>(b) * p.D,
+                                               static_cast<const T*>(p.W) + static_cast<size_t>(h) * R * p.D, p.D,
+                                               p.bias ? p.bias + h * R : nullptr, reinterpret_cast<uint4*>(keys), s_q,
+                                               (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr);
+    if constexpr (!PRE) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int j = u * RPP + ri;
+            cur[u] = j < n ? load_raw16(kp + static_cast<size_t>(j) * R) : make_uint4(0, 0, 0, 0);
+        }
+    }
     float q[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) q[v] = s_q[li * VEC + v] * p.scale;

@@ -5,9 +5,8 @@
 // the attention of layer l over the rows its speculation selected, beside the
 // speculation for layer l+1 (scores, selection and counters).
 //
-// The partial-query projection for layer l+1 runs first (k_rehearse_proj).
-// Then one grid holds both roles: workgroups [0, B*H) run spec_row for layer
-// l+1, the rest run attention items of layer l (one (b, h, split) each, all
+// One grid holds both roles: workgroups [0, B*H) run spec_row for layer l+1
+// (its own partial-query projection included), the rest run attention items of layer l (one (b, h, split) each, all
 // 1024 threads of the workgroup on it).  The two roles touch disjoint buffers,
 // so they need no synchronisation; a CU holds one workgroup of each role, and
 // the attention's K/V gathers fill the memory pipeline while the speculation
@@ -32,6 +31,8 @@ union DecodeShared {
 // buffered) and 2 K/V rows (64 lane groups x 2 = 128 rows per pass).
 constexpr int kDecodeSpecBatch = 4;
 constexpr int kDecodeAttnRows = 2;
+// partial-weight loads per lane in flight in the projection (the partial-key rows are issued after it)
+constexpr int kDecodeProjLoads = 6;
 
 template <typename T, int LPR_S, int LPR_A>
 __global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int n_spec, int bh_attn) {
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p
     __shared__ DecodeShared<LPR_S * Vec<T>::N, LPR_A, Vec<T>::N> sm;
     const int wg = blockIdx.x;
     if (wg < n_spec) {
-        spec_row<T, LPR_S, kDecodeSpecBatch>(p, wg, keys, sm.spec);
+        spec_row<T, LPR_S, kDecodeSpecBatch, kDecodeProjLoads, false>(p, wg, keys, sm.spec);
         return;
     }
     const int item = wg - n_spec;
@@ -52,13 +53,13 @@ static int launch_fused(const SpecParams& p, const AttnArgs& a, int bh_attn, hip
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_layer<T, LPR_S, LPR_A>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(speculate_lds_bytes(kDecodeMaxRows)));
+                                                 static_cast<int>(speculate_lds_bytes(kDecodeMaxRows, 0)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
     const int n_spec = p.B * p.H;
     const int grid = n_spec + a.nsplit * bh_attn;
-    hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A>), dim3(grid), dim3(kDecodeThreads), speculate_lds_bytes(p.n),
+    hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A>), dim3(grid), dim3(kDecodeThreads), speculate_lds_bytes(p.n, p.D * static_cast<int>(sizeof(T))),
                        s, p, a, n_spec, bh_attn);
     return static_cast<int>(hipGetLastError());
 }
@@ -68,7 +69,7 @@ static int lpr_of(int len, int dtype) { return len / (dtype == IG_BF16 ? 8 : 4);
 
 bool decode_fusable(const AttnCall& a, const SpecCall& s) {
     const int ls = lpr_of(s.r, s.dtype), la = lpr_of(a.d, a.dtype);
-    return a.dtype == s.dtype && s.n <= kDecodeMaxRows &&
+    return a.dtype == s.dtype && s.n <= kDecodeMaxRows && s.D * (s.dtype == IG_BF16 ? 2 : 4) <= 4 * kDecodeMaxRows &&
            plan_speculate(s.B, s.H, s.D, s.r, s.n, s.max_out, s.dtype).slices == 1 &&
            (ls == 2 || ls == 4 || ls == 8) && (la == 8 || la == 16 || la == 32);
 }
@@ -112,13 +113,12 @@ int launch_decode_layer(const AttnCall* a, const SpecCall* sc, hipStream_t s) {
         return e ? e : launch_attn_call(*a, s);
     }
     SpecParams p;
-    int e = begin_speculate(*sc, &p, s);
-    if (e) return e;
+    begin_speculate(*sc, &p);
     const AttnPlan ap = plan_attn(a->B, a->H, a->d, a->max_out);
     const AttnArgs aa{a->q, a->K, a->V, a->ld_rows, a->idx, a->count, a->d, a->max_out, ap.rows_per_split, ap.nsplit,
                       a->scale, a->out, a->lse, static_cast<float*>(a->ws)};
     const int bh = a->B * a->H;
-    e = a->dtype == IG_BF16 ? launch_fused_t<uint16_t>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s)
+    const int e = a->dtype == IG_BF16 ? launch_fused_t<uint16_t>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s)
                             : launch_fused_t<float>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s);
     if (e || ap.nsplit == 1) return e;
     return launch_attn_combine(aa.part, ap.nsplit, a->d, bh, a->out, a->lse, s);

@@ -1,19 +1,21 @@
-// Fused speculation entry point: the partial-query projection kernel, then one
-// 1024-thread workgroup per (b, h) running spec_row (scores, selection and
-// counters with the scores kept on chip).  Few rows, or rows longer than one
+// Fused speculation entry point: one 1024-thread workgroup per (b, h) running
+// spec_row (partial query, scores, selection and counters with the scores kept
+// on chip).  Few rows, or rows longer than one
 // workgroup's LDS: each row is cut into slices, one workgroup each, that leave
 // their local selection as candidates, and a merge workgroup per row selects
 // among them.  InfiniGen, arXiv 2406.19707, paper-graph-ui summary, section
 // 3.4 "Decoding Stage" steps 1-3 and 5.
+#include <algorithm>
+
 #include "ig_spec_dev.h"
 
 namespace ig {
 
 template <typename T, int LPR>
 __global__ __launch_bounds__(kSpecThreads) void k_speculate(SpecParams p) {
-    extern __shared__ __align__(16) uint32_t keys[];  // max(rows, 1024) order-preserving score keys
+    extern __shared__ __align__(16) uint32_t keys[];  // staged x, then the slice's order-preserving score keys
     __shared__ SpecShared<LPR * Vec<T>::N> sm;
-    spec_row<T, LPR>(p, blockIdx.x, keys, sm);
+    spec_row<T, LPR, kSpecBatch, 16>(p, blockIdx.x, keys, sm);
 }
 
 __global__ __launch_bounds__(kSpecThreads) void k_spec_merge(SpecParams p) {
@@ -26,7 +28,6 @@ static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype) {
     SpecPlan sp{};
-    sp.rp = plan_rehearse(B, H, D, r, n, dtype);
     const int64_t rows = static_cast<int64_t>(B) * H;
     // slices per row: enough for every row to fit in LDS, more (up to 16, at least 2048 rows each) when
     // there are too few rows to fill the chip, fewer if the candidates would not fit the merge's LDS
@@ -47,7 +48,7 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     sp.slice_rows = S > 1 ? slice_rows : n;
     sp.cand_cap = S > 1 ? cap : 0;
     const size_t cands = static_cast<size_t>(rows) * S * sp.cand_cap;
-    sp.off_arrive = align256(sp.rp.ws_bytes);
+    sp.off_arrive = 0;
     sp.off_cnt = sp.off_arrive + align256(static_cast<size_t>(B) * sizeof(uint32_t));
     sp.off_key = sp.off_cnt + (S > 1 ? align256(static_cast<size_t>(rows) * S * sizeof(int32_t)) : 0);
     sp.off_idx = sp.off_key + (S > 1 ? align256(cands * sizeof(uint32_t)) : 0);
@@ -59,9 +60,12 @@ size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dt
     return plan_speculate(B, H, D, r, n, max_out, dtype).ws_bytes;
 }
 
-// keys for the rows of a workgroup; at least one word per thread (the same storage first holds the
-// split-partial staging of the partial query, and last the argmin scratch of the pool finish)
-size_t speculate_lds_bytes(int n) { return static_cast<size_t>(n < kSpecThreads ? kSpecThreads : n) * sizeof(uint32_t); }
+// keys for the rows of a workgroup; at least one word per thread (the argmin scratch of the pool
+// finish) and the attention input x (staged there first for the partial-query projection)
+size_t speculate_lds_bytes(int n, int x_bytes) {
+    const size_t w = static_cast<size_t>(std::max({n, kSpecThreads, (x_bytes + 3) / 4}));
+    return w * sizeof(uint32_t);
+}
 
 template <typename T, int L>
 static int launch_spec_tl(const SpecParams& p, hipStream_t s) {
@@ -69,12 +73,12 @@ static int launch_spec_tl(const SpecParams& p, hipStream_t s) {
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_speculate<T, L>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows)));
+                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows, 0)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
     hipLaunchKernelGGL((k_speculate<T, L>), dim3(p.B * p.H * p.slices), dim3(kSpecThreads),
-                       speculate_lds_bytes(p.slice_rows), s, p);
+                       speculate_lds_bytes(p.slice_rows, p.D * static_cast<int>(sizeof(T))), s, p);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -96,28 +100,25 @@ static int launch_merge(const SpecParams& p, hipStream_t s) {
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_spec_merge),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows)));
+                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows, 0)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
     hipLaunchKernelGGL(k_spec_merge, dim3(p.B * p.H), dim3(kSpecThreads),
-                       speculate_lds_bytes(p.slices * p.cand_cap), s, p);
+                       speculate_lds_bytes(p.slices * p.cand_cap, 0), s, p);
     return static_cast<int>(hipGetLastError());
 }
 
-int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s) {
+void begin_speculate(const SpecCall& c, SpecParams* p) {
     const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
     char* ws = static_cast<char*>(c.ws);
-    float* part = reinterpret_cast<float*>(ws);
-    const int e = launch_proj(c.x, c.Wq_part, c.B, c.D, c.H * c.r, c.dtype, sp.rp, part, s);
-    if (e) return e;
-    // all batch rows of a head on one XCD when the heads split evenly over the 8 XCDs
-    *p = SpecParams{part, sp.rp.splits, c.bq_part, c.Kp, c.B, c.H, c.r, c.n, c.n_cap, c.ld, c.scale, c.mode, c.alpha,
+    // all batch rows of a head on one XCD when the heads split evenly over the 8 XCDs (they share the
+    // head's partial weight rows through that XCD's L2)
+    *p = SpecParams{c.x, c.Wq_part, c.D, c.bq_part, c.Kp, c.B, c.H, c.r, c.n, c.n_cap, c.ld, c.scale, c.mode, c.alpha,
                     c.k, c.max_sel, c.max_out, c.idx, c.count, c.q_part, c.scores, c.counters, c.cmax, c.victim,
                     reinterpret_cast<uint32_t*>(ws + sp.off_arrive), c.H % 8 == 0 ? 1 : 0, sp.slices, sp.slice_rows,
                     sp.cand_cap, reinterpret_cast<uint32_t*>(ws + sp.off_key), reinterpret_cast<int32_t*>(ws + sp.off_idx),
                     reinterpret_cast<int32_t*>(ws + sp.off_cnt)};
-    return 0;
 }
 
 int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H,
@@ -127,9 +128,8 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     const SpecCall c{x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, mode, alpha, k, max_sel, idx, count,
                      max_out, counters, cmax, victim, q_part, scores, ld, ws};
     SpecParams p;
-    int e = begin_speculate(c, &p, s);
-    if (e) return e;
-    e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
+    begin_speculate(c, &p);
+    const int e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
     if (e || p.slices == 1) return e;
     return launch_merge(p, s);
 }
