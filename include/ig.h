@@ -181,11 +181,12 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * q_part [B][H][r] and scores [B][H][ld] are written only when not NULL.
  * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
  * receives the victim.  One launch of one workgroup per (b, h), which projects
- * its own partial query and then scores, selects and updates the counters (two
- * launches with slices: the slices, then the merges).  D * element size must
- * not exceed 131072 bytes.  The workspace (IG_OP_SPECULATE bytes, required)
- * starts with one uint32 arrival word per sequence ([B] at offset 0), followed
- * by the slices' candidates; it must have been zero-filled once with
+ * its own partial query and then scores, selects and updates the counters
+ * (with slices: the partial-query projection, the slices, then the merges).
+ * D * element size must not exceed 131072 bytes.  The workspace
+ * (IG_OP_SPECULATE bytes, required) starts with one uint32 arrival word per
+ * sequence ([B] at offset 0), followed by the projection's partial sums and
+ * the slices' candidates when there are slices; it must have been zero-filled once with
  * ig_workspace_init, and every call returns the arrival words to zero.  Calls
  * sharing a workspace must not overlap.  H <= 65535.
  */

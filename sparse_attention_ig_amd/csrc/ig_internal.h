@@ -45,9 +45,10 @@ size_t select_ws_bytes(int B, int H, int n, int max_out);
 
 constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
 struct SpecPlan {
+    RehearsePlan rp;                  // the projection kernel of sliced rows
     int slices, slice_rows, cand_cap;
     bool ok;                          // false: rows too long for the candidates to fit one merge
-    size_t off_arrive, off_cnt, off_key, off_idx, ws_bytes;
+    size_t off_arrive, off_part, off_cnt, off_key, off_idx, ws_bytes;
 };
 SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);

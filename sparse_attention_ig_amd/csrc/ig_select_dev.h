@@ -463,44 +463,83 @@ __device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, i
     return compact_lds_e<NT, 1>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
 }
 
-// Top-kk cut of a long row through a sampled bound.  One key per thread at a fixed stride gives a
-// sample; its r-th largest key L (r = the expected sample count above the cut, plus 2.5 standard
-// deviations and 4) bounds the cut from below when at least kk keys are >= L.  The keys >= L (at
-// most kMaxCand) are copied to LDS and the exact radix select runs on them: every key >= the kk-th
-// largest is among them, so the result is the one the full row would give.  Returns false (nothing
-// decided; run the full radix) when the bound fails either way.  The selection is then every key
-// above *T plus the first *need_eq keys equal to *T, *eq_total keys being equal to it.
+// Top-kk cut of a long row through a sampled bracket.  One key per thread at a fixed stride gives a
+// sample of NT keys; with e the expected sample count above the cut and m = 2.5 sqrt(e) + 4, the
+// sample's (e + m)-th largest key L bounds the cut from below and, when e - m >= 1, its (e - m)-th
+// largest key U bounds it from above (taken only when the keys >= L would not fit).  One pass over the row counts the keys >= U (c_hi) and copies the
+// keys in [L, U) (the band) to LDS in any order.  When c_hi < kk <= c_hi + |band| and the band holds at
+// most kMaxCand keys, the row's kk-th largest key is the band's (kk - c_hi)-th largest, found by the
+// exact radix select on the band, and keys equal to it all lie in the band, so the counts it returns
+// are the row's.  Without an upper bound the band is every key >= L.  Returns false (nothing decided;
+// run the full radix) when a bound fails.  The selection is then every key above *T plus the first
+// *need_eq keys equal to *T, *eq_total keys being equal to it.  Ends after a barrier.
 template <int NT = kSelThreads>
 __device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, SelScratch& sh, uint32_t* T_out,
                                 int* need_eq_out, int* eq_total_out) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid % kWave;
     if (n < 8 * NT) return false;
     const double expect = static_cast<double>(kk) * NT / n;
-    const int r = static_cast<int>(expect + 2.5 * sqrt(expect) + 4.0);
-    if (r >= NT) return false;
+    const double margin = 2.5 * sqrt(expect) + 4.0;
+    const int r_lo = static_cast<int>(expect + margin);
+    const int r_hi = static_cast<int>(expect - margin);
+    if (r_lo >= NT) return false;
     uint32_t* sample = fs.words + kSampleBase;
     uint32_t* cand = fs.words + kCandBase;
     sample[tid] = lk[static_cast<int64_t>(tid) * n / NT];
     __syncthreads();
-    uint32_t L;
+    uint32_t L, U = 0;
     int ne, et;
-    radix_kth_lds<NT>(sample, NT, r, fs, &L, &ne, &et);  // (an early exit gives a lower L: still a bound)
-    const int c = count_ge_lds<NT>(lk, n, L, sh);
-    if (c < kk || c > kMaxCand) {                        // uniform: c comes from a block sum
+    // (an early exit gives a lower value: L is still a lower bound, and U is checked by the count)
+    radix_kth_lds<NT>(sample, NT, r_lo, fs, &L, &ne, &et);
+    // the upper bound only when the keys >= L are expected to overflow the candidate space
+    const bool want_hi = r_hi >= 1 && static_cast<double>(r_lo) * n / NT > 0.75 * kMaxCand;
+    if (want_hi) {
+        __syncthreads();  // every wave has read the last histogram before it is cleared
+        fast_sel_init(fs);
+        __syncthreads();
+        radix_kth_lds<NT>(sample, NT, r_hi, fs, &U, &ne, &et);
+    }
+    const bool has_hi = want_hi && U > L;
+    if (tid == 0) fs.wtot[0] = 0;  // band keys placed so far
+    __syncthreads();
+    int c_hi = 0;
+    for (int j0 = 4 * tid; j0 < n; j0 += 4 * NT) {  // n >= 8 NT: four keys per lane
+        uint32_t k[4];
+        load_keys<4>(lk, j0, n, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool valid = j0 + e < n;
+            const bool hi = valid && has_hi && k[e] >= U;
+            const bool in = valid && !hi && k[e] >= L;
+            c_hi += hi ? 1 : 0;
+            // lane 0 holds the wave's lowest j0, so it is active whenever any lane is
+            const uint64_t m = __ballot(in);
+            if (m != 0) {
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&fs.wtot[0], __popcll(m));
+                base = read_lane(base, 0);
+                const int pos = base + __popcll(m & lanemask_lt());
+                if (in && pos < kMaxCand) cand[pos] = k[e];
+            }
+        }
+    }
+    __syncthreads();
+    const int c_band = fs.wtot[0];
+    c_hi = block_sum<NT>(c_hi, sh);
+    if (c_hi >= kk || c_hi + c_band < kk || c_band > kMaxCand) {  // uniform: block-wide counts
         // the sample's passes left counts in the histograms: the full radix starts from clean ones
         fast_sel_init(fs);
         __syncthreads();
         return false;
     }
-    fast_sel_init(fs);                                   // fresh histograms for the candidate select
-    auto copy_key = [&](int p, int j) { cand[p] = lk[j]; };
-    compact_lds<NT>(lk, n, L, INT_MAX, INT_MAX, nullptr, kMaxCand, fs, copy_key);
+    fast_sel_init(fs);  // fresh histograms for the band select
     __syncthreads();
     uint32_t T;
-    radix_kth_lds<NT>(cand, c, kk, fs, &T, need_eq_out, eq_total_out);
-    // an early exit leaves T at its bin's lowest value, which may lie below L: every candidate at or
-    // above it is selected, and those are exactly the row's keys >= max(T, L)
+    radix_kth_lds<NT>(cand, c_band, kk - c_hi, fs, &T, need_eq_out, eq_total_out);
+    // an early exit leaves T at its bin's lowest value, which may lie below L: every band key at or
+    // above it is selected, and those with the keys >= U are exactly the row's keys >= max(T, L)
     *T_out = T < L ? L : T;
+    __syncthreads();
     return true;
 }
 

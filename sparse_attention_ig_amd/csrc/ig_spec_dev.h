@@ -6,7 +6,9 @@
 // One 1024-thread workgroup per (b, h); scores never leave the chip.
 //  1. The workgroup projects its own partial query: x[b] staged in LDS, the
 //     head's r rows of the partial weight read along D by groups of lanes
-//     (the batch rows of a head share those rows through the L2 cache).
+//     (the batch rows of a head share those rows through the L2 cache).  Sliced
+//     rows instead add the split partials of one projection kernel
+//     (k_rehearse_proj, shared with ig_rehearse).
 //  2. Scores of every cached row go to LDS as order-preserving keys (and to
 //     HBM only if the caller asks for them), streaming the partial-key rows in
 //     double-buffered batches of 8 rows x 16 bytes per lane.
@@ -38,6 +40,8 @@ struct SpecParams {
     const void* x;       // [B][D] attention input
     const void* W;       // [H*r][D] partial query weight (one row per partial column)
     int D;
+    const float* part;   // NULL: each workgroup projects its partial query from x and W; else the
+    int splits;          //   projection kernel's partial sums [splits][B][H*r], added in fixed order
     const float* bias;
     const void* Kp;
     int B, H, r, n, n_cap, ld;
@@ -63,8 +67,9 @@ struct SpecParams {
     int32_t* cand_cnt;       // [B*H][slices]
 };
 
-// Fills the row kernel's parameters of a speculation call.
-void begin_speculate(const SpecCall& c, SpecParams* p);
+// Fills the row kernel's parameters of a speculation call; with sliced rows, first launches the
+// partial-query projection kernel (every slice of a row would otherwise project the same query).
+int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s);
 
 constexpr int kSpecMaxSlices = 16;
 
@@ -314,10 +319,15 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
             cur[u] = j < n ? load_raw16(kp + static_cast<size_t>(j) * R) : make_uint4(0, 0, 0, 0);
         }
     }
-    project_partial<T, kSpecThreads, R, PU>(static_cast<const T*>(p.x) + static_cast<size_t>(b) * p.D,
-                                               static_cast<const T*>(p.W) + static_cast<size_t>(h) * R * p.D, p.D,
-                                               p.bias ? p.bias + h * R : nullptr, reinterpret_cast<uint4*>(keys), s_q,
-                                               (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr);
+    float* q_out = (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr;
+    if (p.part)
+        sum_partials<kSpecThreads>(p.part, p.splits, p.B, p.H * R, b, h * R, R, p.bias, s_q,
+                                   reinterpret_cast<float*>(keys), q_out);
+    else
+        project_partial<T, kSpecThreads, R, PU>(static_cast<const T*>(p.x) + static_cast<size_t>(b) * p.D,
+                                                static_cast<const T*>(p.W) + static_cast<size_t>(h) * R * p.D, p.D,
+                                                p.bias ? p.bias + h * R : nullptr, reinterpret_cast<uint4*>(keys), s_q,
+                                                q_out);
     if constexpr (!PRE) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {

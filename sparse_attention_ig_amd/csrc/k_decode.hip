@@ -113,12 +113,13 @@ int launch_decode_layer(const AttnCall* a, const SpecCall* sc, hipStream_t s) {
         return e ? e : launch_attn_call(*a, s);
     }
     SpecParams p;
-    begin_speculate(*sc, &p);
+    int e = begin_speculate(*sc, &p, s);  // (no launch: the fused set has no slices)
+    if (e) return e;
     const AttnPlan ap = plan_attn(a->B, a->H, a->d, a->max_out);
     const AttnArgs aa{a->q, a->K, a->V, a->ld_rows, a->idx, a->count, a->d, a->max_out, ap.rows_per_split, ap.nsplit,
                       a->scale, a->out, a->lse, static_cast<float*>(a->ws)};
     const int bh = a->B * a->H;
-    const int e = a->dtype == IG_BF16 ? launch_fused_t<uint16_t>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s)
+    e = a->dtype == IG_BF16 ? launch_fused_t<uint16_t>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s)
                             : launch_fused_t<float>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s);
     if (e || ap.nsplit == 1) return e;
     return launch_attn_combine(aa.part, ap.nsplit, a->d, bh, a->out, a->lse, s);

@@ -1,6 +1,6 @@
 // Fused speculation entry point: one 1024-thread workgroup per (b, h) running
 // spec_row (partial query, scores, selection and counters with the scores kept
-// on chip).  Few rows, or rows longer than one
+// on chip).  Sliced rows: the partial-query projection kernel first.  Few rows, or rows longer than one
 // workgroup's LDS: each row is cut into slices, one workgroup each, that leave
 // their local selection as candidates, and a merge workgroup per row selects
 // among them.  InfiniGen, arXiv 2406.19707, paper-graph-ui summary, section
@@ -49,7 +49,9 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     sp.cand_cap = S > 1 ? cap : 0;
     const size_t cands = static_cast<size_t>(rows) * S * sp.cand_cap;
     sp.off_arrive = 0;
-    sp.off_cnt = sp.off_arrive + align256(static_cast<size_t>(B) * sizeof(uint32_t));
+    sp.rp = plan_rehearse(B, H, D, r, n, dtype);
+    sp.off_part = align256(static_cast<size_t>(B) * sizeof(uint32_t));
+    sp.off_cnt = sp.off_part + (S > 1 ? align256(sp.rp.ws_bytes) : 0);
     sp.off_key = sp.off_cnt + (S > 1 ? align256(static_cast<size_t>(rows) * S * sizeof(int32_t)) : 0);
     sp.off_idx = sp.off_key + (S > 1 ? align256(cands * sizeof(uint32_t)) : 0);
     sp.ws_bytes = sp.off_idx + (S > 1 ? align256(cands * sizeof(int32_t)) : 0);
@@ -109,16 +111,23 @@ static int launch_merge(const SpecParams& p, hipStream_t s) {
     return static_cast<int>(hipGetLastError());
 }
 
-void begin_speculate(const SpecCall& c, SpecParams* p) {
+int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s) {
     const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
     char* ws = static_cast<char*>(c.ws);
+    float* part = nullptr;
+    if (sp.slices > 1) {
+        part = reinterpret_cast<float*>(ws + sp.off_part);
+        const int e = launch_proj(c.x, c.Wq_part, c.B, c.D, c.H * c.r, c.dtype, sp.rp, part, s);
+        if (e) return e;
+    }
     // all batch rows of a head on one XCD when the heads split evenly over the 8 XCDs (they share the
     // head's partial weight rows through that XCD's L2)
-    *p = SpecParams{c.x, c.Wq_part, c.D, c.bq_part, c.Kp, c.B, c.H, c.r, c.n, c.n_cap, c.ld, c.scale, c.mode, c.alpha,
+    *p = SpecParams{c.x, c.Wq_part, c.D, part, sp.rp.splits, c.bq_part, c.Kp, c.B, c.H, c.r, c.n, c.n_cap, c.ld, c.scale, c.mode, c.alpha,
                     c.k, c.max_sel, c.max_out, c.idx, c.count, c.q_part, c.scores, c.counters, c.cmax, c.victim,
                     reinterpret_cast<uint32_t*>(ws + sp.off_arrive), c.H % 8 == 0 ? 1 : 0, sp.slices, sp.slice_rows,
                     sp.cand_cap, reinterpret_cast<uint32_t*>(ws + sp.off_key), reinterpret_cast<int32_t*>(ws + sp.off_idx),
                     reinterpret_cast<int32_t*>(ws + sp.off_cnt)};
+    return 0;
 }
 
 int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H,
@@ -128,8 +137,9 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     const SpecCall c{x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, mode, alpha, k, max_sel, idx, count,
                      max_out, counters, cmax, victim, q_part, scores, ld, ws};
     SpecParams p;
-    begin_speculate(c, &p);
-    const int e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
+    int e = begin_speculate(c, &p, s);
+    if (e) return e;
+    e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
     if (e || p.slices == 1) return e;
     return launch_merge(p, s);
 }

@@ -39,6 +39,8 @@ def _rows(rng, B, H, n, kind):
         s = np.full((B, H, n), 2.0, dtype=np.float32)
     elif kind == "signed-zero":
         s = rng.choice(np.array([-0.0, 0.0, -1.0, 1.0], dtype=np.float32), (B, H, n))
+    elif kind == "dense":  # float32 draws: ties are rare
+        s = rng.standard_normal((B, H, n)).astype(np.float32)
     else:  # "wide": many distinct integers, runs of equal ones still common
         s = rng.integers(-500, 500, (B, H, n)).astype(np.float32)
     return s
@@ -58,6 +60,11 @@ SELECT_CASES = [
     (1000, "few", "threshold", dict(alpha=1.0), 1000),                  # no cap: whole runs kept
     (6000, "wide", "threshold", dict(alpha=40.0, max_sel=150), 150),
     (12000, "few", "threshold", dict(alpha=0.0, max_sel=2400), 2400),   # alpha 0: the maximum's run only
+    # large selections of long rows: the sampled bracket (band of keys between two sampled bounds)
+    (32768, "dense", "topk", dict(k=5243), 5243),
+    (30000, "wide", "topk", dict(k=6000), 6000),
+    (32000, "dense", "threshold", dict(alpha=1.5, max_sel=6400), 6400),
+    (24576, "few", "topk", dict(k=5000), 5000),                         # bounds on equal keys: full radix
 ]
 
 
@@ -112,6 +119,41 @@ def test_speculate_ties_exact(n, distinct, mode, kw, max_out):
         for h in range(H):
             u = np.unique(sc[b, h])
             assert len(u) < 2 or np.diff(u).min() > 1e-4 * max(1.0, np.abs(u).max())
+    ridx, rcnt = O.select(sc, mode, max_out=max_out, **kw)
+    assert np.array_equal(cnt, rcnt)
+    for b in range(B):
+        for h in range(H):
+            c = rcnt[b, h]
+            assert np.array_equal(idx[b, h, :c], ridx[b, h, :c]), (b, h)
+
+
+INT_CASES = [
+    # n, mode, kwargs, max_out
+    (65536, "topk", dict(k=6000), 6000),                        # five slices, a merge of 30000 candidates
+    (40000, "threshold", dict(alpha=1e9, max_sel=7000), 7000),  # every row passes; the cap decides
+    (32768, "topk", dict(k=5243), 5243),
+]
+
+
+@pytest.mark.parametrize("n,mode,kw,max_out", INT_CASES, ids=[f"{c[0]}-{c[1]}" for c in INT_CASES])
+def test_speculate_integer_scores_exact(n, mode, kw, max_out):
+    """Long rows with large selections (sliced rows, sampled brackets, merges): x picks one input
+    channel and the partial weights and keys are small integers, so every score is an exact multiple of
+    the scale (a few thousand distinct values, equal ones exactly equal on both sides)."""
+    from sparse_attention_ig_amd import _lib as L
+    rng = np.random.default_rng(n + max_out)
+    B, H, r, D = 2, 4, 32, 256
+    x = np.zeros((B, D), np.float32)
+    x[:, 0] = 1.0
+    W = np.zeros((D, H * r), np.float32)
+    W[0] = rng.integers(-6, 7, H * r)
+    Kp = rng.integers(-8, 9, (B, H, n, r)).astype(np.float32)
+    x, W, Kp = gen.encode(x, "bf16"), gen.encode(W, "bf16"), gen.encode(Kp, "bf16")
+    scale = 0.5   # a power of two: every partial product and sum stays an exact float32
+    say(f"[speculate integer scores] n={n} mode={mode} {kw}")
+    idx, cnt = L.ig_speculate(dev(x), dev(np.ascontiguousarray(W.T)), dev(Kp), n, scale, mode, max_out, **kw)
+    idx, cnt = host(idx), host(cnt)
+    _, sc = O.rehearse(O.decode(x, "bf16"), O.decode(W, "bf16"), O.decode(Kp, "bf16"), n, H, r, scale)
     ridx, rcnt = O.select(sc, mode, max_out=max_out, **kw)
     assert np.array_equal(cnt, rcnt)
     for b in range(B):
