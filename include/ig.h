@@ -176,8 +176,7 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * those calls; modes IG_SEL_THRESHOLD and IG_SEL_TOPK.  A row's scores live in
  * LDS: when there are too few rows to fill the GPU, or n > 32768, each row is
  * cut into up to 16 slices that select locally, and a merge launch selects
- * among their candidates; IG_EUNSUPPORTED when the candidates (slices x
- * min(slice rows, max_out)) would exceed 32768.
+ * among their candidates; IG_EUNSUPPORTED when n > 16 x 32768.
  * q_part [B][H][r] and scores [B][H][ld] are written only when not NULL.
  * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
  * receives the victim.  One launch of one workgroup per (b, h), which projects

@@ -155,8 +155,8 @@ static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes) {
         return fail(IG_EINVAL, "%s: unknown mode %d", fn, c.mode);
     const SpecPlan plan = plan_speculate(B, H, D, r, n, max_out, dtype);
     if (!plan.ok)
-        return fail(IG_EUNSUPPORTED, "%s: n = %d with max_out = %d: the candidates of %d slices exceed %d; use "
-                    "ig_rehearse + ig_select", fn, n, max_out, plan.slices, kSpecMaxRows);
+        return fail(IG_EUNSUPPORTED, "%s: n = %d needs more than %d slices of %d rows; use ig_rehearse + "
+                    "ig_select", fn, n, kSpecMaxSlices, kSpecMaxRows);
     IG_REQUIRE(!c.counters || c.cmax >= 2, "%s: cmax must be >= 2", fn);
     IG_REQUIRE(H <= 0xFFFF, "%s: at most 65535 heads", fn);
     const size_t need = plan.ws_bytes;

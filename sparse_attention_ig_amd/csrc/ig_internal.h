@@ -44,6 +44,7 @@ AttnPlan plan_attn(int B, int H, int d, int max_out);
 size_t select_ws_bytes(int B, int H, int n, int max_out);
 
 constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
+constexpr int kSpecMaxSlices = 16;    // slices per row of the fused speculation
 struct SpecPlan {
     RehearsePlan rp;                  // the projection kernel of sliced rows
     int slices, slice_rows, cand_cap;

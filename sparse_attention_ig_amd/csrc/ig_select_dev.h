@@ -270,18 +270,36 @@ __device__ __forceinline__ void load_keys(const uint32_t* lk, int j, int end, ui
     for (int e = 0; e < E; ++e) k[e] = j + e < end ? lk[j + e] : 0u;
 }
 
+// Key sources of the selection primitives: keys held in LDS (16-byte aligned), or a row of keys in
+// global memory (any alignment, scalar loads).
+struct LdsKeys {
+    const uint32_t* p;
+    __device__ __forceinline__ uint32_t at(int j) const { return p[j]; }
+    template <int E>
+    __device__ __forceinline__ void load(int j, int end, uint32_t (&k)[E]) const { load_keys<E>(p, j, end, k); }
+};
+struct GlobalKeys {
+    const uint32_t* __restrict__ p;
+    __device__ __forceinline__ uint32_t at(int j) const { return p[j]; }
+    template <int E>
+    __device__ __forceinline__ void load(int j, int end, uint32_t (&k)[E]) const {
+#pragma unroll
+        for (int e = 0; e < E; ++e) k[e] = j + e < end ? p[j + e] : 0u;
+    }
+};
+
 // Keys per lane per step: 4 (one 16-byte LDS read) once every thread has at least 4 keys, else 1.
 template <int NT>
 __device__ __forceinline__ bool wide_rows(int n) { return n >= 4 * NT; }
 
 // One radix pass: hist[digit] counts of the keys whose bits above `shift + 8` equal `prefix`.
-template <int NT, int E>
-__device__ __forceinline__ void radix_hist(const uint32_t* lk, int n, uint32_t* h, int shift, uint32_t prefix,
-                                           uint32_t pmask, bool first) {
+template <int NT, int E, class KS>
+__device__ __forceinline__ void radix_hist(KS lk, int n, uint32_t* h, int shift, uint32_t prefix, uint32_t pmask,
+                                           bool first) {
     const int lane = threadIdx.x % kWave;
     for (int j0 = E * static_cast<int>(threadIdx.x); j0 < n; j0 += E * NT) {
         uint32_t k[E];
-        load_keys<E>(lk, j0, n, k);
+        lk.template load<E>(j0, n, k);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const uint32_t bin = (k[e] >> shift) & 255u;
@@ -313,9 +331,9 @@ __device__ __forceinline__ void radix_hist(const uint32_t* lk, int n, uint32_t* 
 // Per pass: LDS atomics into that pass's histogram, one barrier, then every wave finds the digit on
 // its own: lane L holds bins 255-4L .. 252-4L, a DPP prefix sum over the lanes gives the keys above
 // each bin, and the lane holding the bin where the count reaches rem broadcasts it.
-template <int NT = kSelThreads>
-__device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, uint32_t* T_out,
-                                              int* need_eq_out, int* eq_total_out) {
+template <int NT = kSelThreads, class KS>
+__device__ __forceinline__ void radix_kth_keys(KS lk, int n, int kk, FastSel& fs, uint32_t* T_out, int* need_eq_out,
+                                               int* eq_total_out) {
     const int tid = threadIdx.x, lane = tid % kWave;
     const bool wide = wide_rows<NT>(n);
     uint32_t prefix = 0, pmask = 0;
@@ -358,21 +376,32 @@ __device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk,
     *eq_total_out = dcount;
 }
 
-// Keys >= kc among lk[0..n), summed over the first NT threads (ends after barriers).
 template <int NT = kSelThreads>
-__device__ __forceinline__ int count_ge_lds(const uint32_t* lk, int n, uint32_t kc, SelScratch& sh) {
+__device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, uint32_t* T_out,
+                                              int* need_eq_out, int* eq_total_out) {
+    radix_kth_keys<NT>(LdsKeys{lk}, n, kk, fs, T_out, need_eq_out, eq_total_out);
+}
+
+// Keys >= kc among lk[0..n), summed over the first NT threads (ends after barriers).
+template <int NT = kSelThreads, class KS>
+__device__ __forceinline__ int count_ge(KS lk, int n, uint32_t kc, SelScratch& sh) {
     int c = 0;
     if (wide_rows<NT>(n)) {
         for (int j0 = 4 * static_cast<int>(threadIdx.x); j0 < n; j0 += 4 * NT) {
             uint32_t k[4];
-            load_keys<4>(lk, j0, n, k);
+            lk.template load<4>(j0, n, k);
 #pragma unroll
             for (int e = 0; e < 4; ++e) c += (j0 + e < n && k[e] >= kc) ? 1 : 0;
         }
     } else {
-        for (int j = threadIdx.x; j < n; j += NT) c += lk[j] >= kc ? 1 : 0;
+        for (int j = threadIdx.x; j < n; j += NT) c += lk.at(j) >= kc ? 1 : 0;
     }
     return block_sum<NT>(c, sh);
+}
+
+template <int NT = kSelThreads>
+__device__ __forceinline__ int count_ge_lds(const uint32_t* lk, int n, uint32_t kc, SelScratch& sh) {
+    return count_ge<NT>(LdsKeys{lk}, n, kc, sh);
 }
 
 // Ordered compaction of lk[0..n): the rows with key > T and the first need_eq rows with key == T (every
@@ -381,9 +410,9 @@ __device__ __forceinline__ int count_ge_lds(const uint32_t* lk, int n, uint32_t 
 // per-wave counts, and a second pass places each group with DPP prefix sums over the lanes' counts,
 // writing out[pos] = j and calling visit(pos, j).  Returns the number selected (block-uniform).  lk is
 // read by other waves while visit runs, so a visitor must not write lk.
-template <int NT, int E, typename Visit>
-__device__ int compact_lds_e(const uint32_t* lk, int n, uint32_t T, int need_eq, int eq_total,
-                             int32_t* __restrict__ out, int max_out, FastSel& fs, Visit visit) {
+template <int NT, int E, class KS, typename Visit>
+__device__ int compact_e(KS lk, int n, uint32_t T, int need_eq, int eq_total, int32_t* __restrict__ out, int max_out,
+                         FastSel& fs, Visit visit) {
     constexpr int NW = NT / kWave, G = kWave * E;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const bool all_eq = need_eq >= eq_total;
@@ -392,7 +421,7 @@ __device__ int compact_lds_e(const uint32_t* lk, int n, uint32_t T, int need_eq,
     int c_gt = 0, c_eq = 0;
     for (int j0 = lo + lane * E; j0 < hi; j0 += G) {
         uint32_t k[E];
-        load_keys<E>(lk, j0, hi, k);
+        lk.template load<E>(j0, hi, k);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             c_gt += (j0 + e < hi && k[e] > T) ? 1 : 0;
@@ -413,7 +442,7 @@ __device__ int compact_lds_e(const uint32_t* lk, int n, uint32_t T, int need_eq,
     for (int g0 = lo; g0 < hi; g0 += G) {  // whole wave in step: the DPP scans need every lane
         const int j0 = g0 + lane * E;
         uint32_t k[E];
-        load_keys<E>(lk, j0, hi, k);
+        lk.template load<E>(j0, hi, k);
         bool sel[E];
         int cs = 0;
         if (all_eq) {
@@ -456,11 +485,17 @@ __device__ int compact_lds_e(const uint32_t* lk, int n, uint32_t T, int need_eq,
     return gt_tot + take;
 }
 
+template <int NT = kSelThreads, class KS, typename Visit = NoVisit>
+__device__ int compact_keys(KS lk, int n, uint32_t T, int need_eq, int eq_total, int32_t* __restrict__ out,
+                            int max_out, FastSel& fs, Visit visit) {
+    if (wide_rows<NT>(n)) return compact_e<NT, 4>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
+    return compact_e<NT, 1>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
+}
+
 template <int NT = kSelThreads, typename Visit = NoVisit>
 __device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, int eq_total,
                            int32_t* __restrict__ out, int max_out, FastSel& fs, Visit visit) {
-    if (wide_rows<NT>(n)) return compact_lds_e<NT, 4>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
-    return compact_lds_e<NT, 1>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
+    return compact_keys<NT>(LdsKeys{lk}, n, T, need_eq, eq_total, out, max_out, fs, visit);
 }
 
 // Top-kk cut of a long row through a sampled bracket.  One key per thread at a fixed stride gives a
@@ -473,9 +508,9 @@ __device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, i
 // are the row's.  Without an upper bound the band is every key >= L.  Returns false (nothing decided;
 // run the full radix) when a bound fails.  The selection is then every key above *T plus the first
 // *need_eq keys equal to *T, *eq_total keys being equal to it.  Ends after a barrier.
-template <int NT = kSelThreads>
-__device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, SelScratch& sh, uint32_t* T_out,
-                                int* need_eq_out, int* eq_total_out) {
+template <int NT = kSelThreads, class KS>
+__device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, uint32_t* T_out, int* need_eq_out,
+                            int* eq_total_out) {
     const int tid = threadIdx.x, lane = tid % kWave;
     if (n < 8 * NT) return false;
     const double expect = static_cast<double>(kk) * NT / n;
@@ -485,7 +520,7 @@ __device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, 
     if (r_lo >= NT) return false;
     uint32_t* sample = fs.words + kSampleBase;
     uint32_t* cand = fs.words + kCandBase;
-    sample[tid] = lk[static_cast<int64_t>(tid) * n / NT];
+    sample[tid] = lk.at(static_cast<int>(static_cast<int64_t>(tid) * n / NT));
     __syncthreads();
     uint32_t L, U = 0;
     int ne, et;
@@ -505,7 +540,7 @@ __device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, 
     int c_hi = 0;
     for (int j0 = 4 * tid; j0 < n; j0 += 4 * NT) {  // n >= 8 NT: four keys per lane
         uint32_t k[4];
-        load_keys<4>(lk, j0, n, k);
+        lk.template load<4>(j0, n, k);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bool valid = j0 + e < n;
@@ -541,6 +576,12 @@ __device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, 
     *T_out = T < L ? L : T;
     __syncthreads();
     return true;
+}
+
+template <int NT = kSelThreads>
+__device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, SelScratch& sh, uint32_t* T_out,
+                                int* need_eq_out, int* eq_total_out) {
+    return sampled_kth<NT>(LdsKeys{lk}, n, kk, fs, sh, T_out, need_eq_out, eq_total_out);
 }
 
 }  // namespace ig

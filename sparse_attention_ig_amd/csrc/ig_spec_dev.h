@@ -71,8 +71,6 @@ struct SpecParams {
 // partial-query projection kernel (every slice of a row would otherwise project the same query).
 int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s);
 
-constexpr int kSpecMaxSlices = 16;
-
 template <int R>
 struct SpecShared {
     SelScratch sh;
@@ -151,14 +149,16 @@ struct IdentityIdx {
     __device__ __forceinline__ int operator()(int j) const { return j; }
 };
 
-// Selection over keys[0..m) and its results.  `rows`: the row count the limit refers to (the slice's
-// length in a slice workgroup, n otherwise); gidx(j): the row index of key j.  TO_CANDS: write the
-// selected keys and row indices as this slice's candidates; otherwise write idx / count and update the
-// counters (one integer atomic per selected slot, all in flight together; the last workgroup of
-// sequence b halves if any slot saturated and picks the victim).
-template <bool TO_CANDS, typename GIdx>
+// Selection over the keys ks[0..m) (held in LDS, or a merge's candidates in global memory) and its
+// results.  `rows`: the row count the limit refers to (the slice's length in a slice workgroup, n
+// otherwise); gidx(j): the row index of key j; lds: at least 1024 words of LDS scratch (may be the
+// keys' own storage).  TO_CANDS: write the selected keys and row indices as this slice's candidates
+// (the slice's unused candidate slots get key 0, below every score key); otherwise write idx / count
+// and update the counters (one integer atomic per selected slot, all in flight together; the last
+// workgroup of sequence b halves if any slot saturated and picks the victim).
+template <bool TO_CANDS, class KS, typename GIdx>
 __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, int slice, int m, int rows,
-                                            uint32_t kmax_all, uint32_t* keys, SelScratch& sh, FastSel& fs,
+                                            uint32_t kmax_all, KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs,
                                             int& s_last, GIdx gidx) {
     const int tid = threadIdx.x;
     int limit = min(rows, p.max_out);
@@ -168,7 +168,7 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
     int need_eq = INT_MAX, eq_total = INT_MAX;
     if (p.mode == IG_SEL_THRESHOLD) {
         const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
-        const int cnt = count_ge_lds<kSpecThreads>(keys, m, kc, sh);
+        const int cnt = count_ge<kSpecThreads>(keys, m, kc, sh);
         if (p.max_sel > 0) limit = min(limit, p.max_sel);
         if (cnt <= limit) {
             kth = kc;
@@ -179,19 +179,21 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
     } else {
         kk = min(p.k, limit);
     }
-    if (!done && !sampled_kth_lds(keys, m, kk, fs, sh, &kth, &need_eq, &eq_total))
-        radix_kth_lds(keys, m, kk, fs, &kth, &need_eq, &eq_total);
+    if (!done && !sampled_kth(keys, m, kk, fs, sh, &kth, &need_eq, &eq_total))
+        radix_kth_keys(keys, m, kk, fs, &kth, &need_eq, &eq_total);
 
     if constexpr (TO_CANDS) {
         const size_t base = (static_cast<size_t>(bh) * p.slices + slice) * p.cand_cap;
         uint32_t* ck = p.cand_key + base;
         int32_t* ci = p.cand_idx + base;
         auto put = [&](int pos, int j) {
-            ck[pos] = keys[j];
+            ck[pos] = keys.at(j);
             ci[pos] = gidx(j);
         };
-        const int written = compact_lds(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put);
-        if (tid == 0) p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = min(written, p.cand_cap);
+        const int written = min(compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put),
+                                p.cand_cap);
+        for (int i = written + tid; i < p.cand_cap; i += kSpecThreads) ck[i] = 0u;
+        if (tid == 0) p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = written;
         return;
     } else {
         const int n = p.n;
@@ -205,10 +207,10 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
                 out[pos] = j;
                 if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(j);
             };
-            written = compact_lds(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
+            written = compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
         } else {
             // key positions first, then every position mapped to its row index with batched loads
-            written = compact_lds(keys, m, kth, need_eq, eq_total, out, p.max_out, fs, NoVisit());
+            written = compact_keys(keys, m, kth, need_eq, eq_total, out, p.max_out, fs, NoVisit());
             __syncthreads();
             const int w = min(written, p.max_out);
             constexpr int U = 8;
@@ -274,8 +276,7 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
         __syncthreads();
         if (!s_last) return;
         const bool halve = s_last == 2;
-        // reuse the key storage for the argmin scratch
-        const int v = pool_finish<kSpecThreads>(crow, n, cmax, halve, p.victim != nullptr, keys, &sh.wtot[0]);
+        const int v = pool_finish<kSpecThreads>(crow, n, cmax, halve, p.victim != nullptr, lds, &sh.wtot[0]);
         if (tid == 0) {
             if (p.victim) p.victim[b] = v;
             __hip_atomic_store(&p.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -376,61 +377,62 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
 
     // 3. selection (and, for a whole row, counters)
     if (p.slices > 1)
-        spec_select<true>(p, b, bh, slice, n, n, kmax_all, keys, sh, fs, sm.last, [&](int j) { return r0 + j; });
+        spec_select<true>(p, b, bh, slice, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last,
+                          [&](int j) { return r0 + j; });
     else
-        spec_select<false>(p, b, bh, 0, n, n, kmax_all, keys, sh, fs, sm.last, IdentityIdx());
+        spec_select<false>(p, b, bh, 0, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last, IdentityIdx());
 }
 
-// Merge workgroup of a sliced row: the row's candidates (every slice's local selection, which together
-// hold the row's selection: a key among the row's top c is among its slice's top c) go to LDS in slice
-// order, which is row order, and the selection runs again over them with the row's rules.
+// Merge workgroup of a sliced row.  Slice sl left its selection in candidate slots [sl * cap, +cap) of
+// the row (unused slots hold key 0, below every score key), so the m = slices * cap slots are in row
+// order and together hold the row's selection: a key among the row's top c is among its slice's top c,
+// and a key at or above the row's threshold cut is at or above its slice's.  The selection runs again
+// over them with the row's rules: on a copy in LDS when m <= kSpecMaxRows, else straight from the
+// candidate arrays (L2-resident: the slices wrote them just before).
 template <int R>
 __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t* keys, SpecShared<R>& sm) {
     SelScratch& sh = sm.sh;
     FastSel& fs = sm.fs;
-    int* s_off = reinterpret_cast<int*>(sm.q);  // slice offsets (slices + 1 <= R words)
     const int tid = threadIdx.x;
     int b, h;
     spec_bh(p, wg, &b, &h);
-    const int bh = b * p.H + h, S = p.slices;
+    const int bh = b * p.H + h;
+    const int m = p.slices * p.cand_cap;
+    const size_t base = static_cast<size_t>(bh) * m;
+    const uint32_t* ck = p.cand_key + base;
+    const int32_t* ci = p.cand_idx + base;
+    auto gidx = [&](int j) { return static_cast<int>(ci[j]); };
     fast_sel_init(fs);
-    if (tid == 0) {
-        int o = 0;
-        for (int sl = 0; sl < S; ++sl) {
-            s_off[sl] = o;
-            o += p.cand_cnt[static_cast<size_t>(bh) * S + sl];
-        }
-        s_off[S] = o;
-    }
-    __syncthreads();
-    const int m = s_off[S];
-    const size_t base = static_cast<size_t>(bh) * S * p.cand_cap;
     uint32_t kmax = 0;
-    for (int sl = 0; sl < S; ++sl) {
-        const int o = s_off[sl], c = s_off[sl + 1] - o;
-        const uint32_t* ck = p.cand_key + base + static_cast<size_t>(sl) * p.cand_cap;
-        constexpr int U = 8;  // 8 loads per lane in flight
-        for (int i0 = tid; i0 < c; i0 += kSpecThreads * U) {
+    constexpr int U = 8;  // loads per lane in flight
+    if (m <= kSpecMaxRows) {
+        for (int i0 = tid; i0 < m; i0 += kSpecThreads * U) {
             uint32_t v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < c ? ck[i0 + u * kSpecThreads] : 0u;
+            for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < m ? ck[i0 + u * kSpecThreads] : 0u;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (i0 + u * kSpecThreads < c) {
-                    keys[o + i0 + u * kSpecThreads] = v[u];
+                if (i0 + u * kSpecThreads < m) {
+                    keys[i0 + u * kSpecThreads] = v[u];
                     kmax = v[u] > kmax ? v[u] : kmax;
                 }
             }
         }
+        const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
+        spec_select<false>(p, b, bh, 0, m, p.n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last, gidx);
+        return;
     }
-    const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
-    const int32_t* ci = p.cand_idx + base;
-    auto gidx = [&](int j) {
-        int sl = 0;
-        while (sl + 1 < S && s_off[sl + 1] <= j) ++sl;
-        return static_cast<int>(ci[static_cast<size_t>(sl) * p.cand_cap + (j - s_off[sl])]);
-    };
-    spec_select<false>(p, b, bh, 0, m, p.n, kmax_all, keys, sh, fs, sm.last, gidx);
+    if (p.mode == IG_SEL_THRESHOLD) {
+        for (int i0 = tid; i0 < m; i0 += kSpecThreads * U) {
+            uint32_t v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < m ? ck[i0 + u * kSpecThreads] : 0u;
+#pragma unroll
+            for (int u = 0; u < U; ++u) kmax = v[u] > kmax ? v[u] : kmax;
+        }
+    }
+    const uint32_t kmax_all = block_max_u32(kmax, sh);  // (also the barrier after fast_sel_init)
+    spec_select<false>(p, b, bh, 0, m, p.n, kmax_all, GlobalKeys{ck}, keys, sh, fs, sm.last, gidx);
 }
 
 }  // namespace ig

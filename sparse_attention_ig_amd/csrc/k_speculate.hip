@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kSpecThreads) void k_speculate(SpecParams p) {
 }
 
 __global__ __launch_bounds__(kSpecThreads) void k_spec_merge(SpecParams p) {
-    extern __shared__ __align__(16) uint32_t keys[];  // max(candidates, 1024) keys
+    extern __shared__ __align__(16) uint32_t keys[];  // the candidates' keys (up to kSpecMaxRows), or scratch
     __shared__ SpecShared<kSpecMaxSlices + 1> sm;
     spec_merge(p, blockIdx.x, keys, sm);
 }
@@ -30,7 +30,8 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     SpecPlan sp{};
     const int64_t rows = static_cast<int64_t>(B) * H;
     // slices per row: enough for every row to fit in LDS, more (up to 16, at least 2048 rows each) when
-    // there are too few rows to fill the chip, fewer if the candidates would not fit the merge's LDS
+    // there are too few rows to fill the chip; fewer while the merge's candidates would not fit its LDS,
+    // down to what the occupancy needs (a merge over more candidates reads them from global memory)
     const int s_min = (n + kSpecMaxRows - 1) / kSpecMaxRows;
     int S = static_cast<int>(std::min<int64_t>(kSpecMaxSlices, (256 + rows - 1) / rows));
     S = std::min(S, std::max(1, n / 2048));
@@ -43,7 +44,7 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
         --S;
     }
     S = (n + slice_rows - 1) / slice_rows;
-    sp.ok = S <= kSpecMaxSlices && (S == 1 || static_cast<int64_t>(S) * cap <= kSpecMaxRows);
+    sp.ok = S <= kSpecMaxSlices;
     sp.slices = S;
     sp.slice_rows = S > 1 ? slice_rows : n;
     sp.cand_cap = S > 1 ? cap : 0;
@@ -106,8 +107,9 @@ static int launch_merge(const SpecParams& p, hipStream_t s) {
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
+    const int m = p.slices * p.cand_cap;
     hipLaunchKernelGGL(k_spec_merge, dim3(p.B * p.H), dim3(kSpecThreads),
-                       speculate_lds_bytes(p.slices * p.cand_cap, 0), s, p);
+                       speculate_lds_bytes(m <= kSpecMaxRows ? m : 0, 0), s, p);
     return static_cast<int>(hipGetLastError());
 }
 

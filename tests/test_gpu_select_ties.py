@@ -132,6 +132,8 @@ INT_CASES = [
     (65536, "topk", dict(k=6000), 6000),                        # five slices, a merge of 30000 candidates
     (40000, "threshold", dict(alpha=1e9, max_sel=7000), 7000),  # every row passes; the cap decides
     (32768, "topk", dict(k=5243), 5243),
+    (131072, "topk", dict(k=12000), 12000),                     # 4 x 12000 candidates: merged from HBM
+    (98304, "threshold", dict(alpha=1e9, max_sel=15000), 15000),
 ]
 
 

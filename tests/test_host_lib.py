@@ -130,10 +130,9 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     assert lib.ig_pool_touch(p, p, p, 1, 64, 5000, 5000, 1000, 15, None, None, 0, None) == L.IG_EINVAL
     # full pool without a victim
     assert lib.ig_append_kv(p, p, p, p, p, p, p, None, 1, 1, 64, 8, 4, 4, L.IG_BF16, None, None) == L.IG_EINVAL
-    # fused speculation: candidates of a sliced row beyond one merge's LDS (2 slices x 20000), or the
-    # head-average mode, are unsupported
-    assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 40000, 40000, L.IG_BF16, f(1.0), L.IG_SEL_TOPK, f(0.0), 4, 0,
-                            p, p, 20000, None, 15, None, None, None, 40000, None, 0, None) == L.IG_EUNSUPPORTED
+    # fused speculation: rows beyond 16 slices of 32768, or the head-average mode, are unsupported
+    assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 600000, 600000, L.IG_BF16, f(1.0), L.IG_SEL_TOPK, f(0.0), 4,
+                            0, p, p, 20000, None, 15, None, None, None, 600000, None, 0, None) == L.IG_EUNSUPPORTED
     assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 40, 40, L.IG_BF16, f(1.0), L.IG_SEL_HEADAVG, f(1.0), 4, 0,
                             p, p, 4, None, 15, None, None, None, 40, None, 0, None) == L.IG_EUNSUPPORTED
     # no workspace
