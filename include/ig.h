@@ -181,11 +181,13 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
  * receives the victim.  One launch of one workgroup per (b, h), which projects
  * its own partial query and then scores, selects and updates the counters
- * (with slices: the partial-query projection, the slices, then the merges).
+ * (with B > 8, the partial-query projection kernel first; with slices, the
+ * projection, the slices, then the merges).
  * D * element size must not exceed 131072 bytes.  The workspace
  * (IG_OP_SPECULATE bytes, required) starts with one uint32 arrival word per
- * sequence ([B] at offset 0), followed by the projection's partial sums and
- * the slices' candidates when there are slices; it must have been zero-filled once with
+ * sequence ([B] at offset 0), followed by the projection's partial sums (when
+ * the projection kernel runs) and the slices' candidates (when there are
+ * slices); it must have been zero-filled once with
  * ig_workspace_init, and every call returns the arrival words to zero.  Calls
  * sharing a workspace must not overlap.  H <= 65535.
  */
@@ -204,10 +206,11 @@ int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const
  * layer l over the rows selected for it, and the speculation for layer l+1.
  * `attn` holds the arguments of ig_sparse_decode_attn for layer l, `spec` those
  * of ig_speculate for layer l+1 (B, H, dtype shared; d is the attention's head
- * dim); either may be NULL (then this is that one call).  With both: one
- * launch in which the speculation's (b, h) workgroups and the attention's run
- * side by side (no ordering between
- * the two halves, so spec->idx, count, counters, victim, q_part, scores must not
+ * dim); either may be NULL (then this is that one call).  With both: (beyond
+ * 8 batch rows, the projection kernel of ig_speculate, then) one launch in
+ * which the speculation's (b, h) workgroups and the attention's run side by
+ * side (no ordering between the two halves, so spec->idx, count, counters,
+ * victim, q_part, scores must not
  * alias anything attn reads), then the split combine of the attention if it
  * splits.  Results: those of the two calls (the attention's float sums may
  * associate differently).  Falls back to the two calls in sequence for shapes

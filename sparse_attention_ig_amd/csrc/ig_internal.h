@@ -48,6 +48,7 @@ constexpr int kSpecMaxSlices = 16;    // slices per row of the fused speculation
 struct SpecPlan {
     RehearsePlan rp;                  // the projection kernel of sliced rows
     int slices, slice_rows, cand_cap;
+    bool proj_kernel;                 // the partial query comes from the projection kernel's partial sums
     bool ok;                          // false: rows too long for the candidates to fit one merge
     size_t off_arrive, off_part, off_cnt, off_key, off_idx, ws_bytes;
 };

@@ -7,8 +7,8 @@
 //  1. The workgroup projects its own partial query: x[b] staged in LDS, the
 //     head's r rows of the partial weight read along D by groups of lanes
 //     (the batch rows of a head share those rows through the L2 cache).  Sliced
-//     rows instead add the split partials of one projection kernel
-//     (k_rehearse_proj, shared with ig_rehearse).
+//     rows and batches beyond 8 rows instead add the split partials of one
+//     projection kernel (k_rehearse_proj, shared with ig_rehearse).
 //  2. Scores of every cached row go to LDS as order-preserving keys (and to
 //     HBM only if the caller asks for them), streaming the partial-key rows in
 //     double-buffered batches of 8 rows x 16 bytes per lane.
@@ -67,8 +67,9 @@ struct SpecParams {
     int32_t* cand_cnt;       // [B*H][slices]
 };
 
-// Fills the row kernel's parameters of a speculation call; with sliced rows, first launches the
-// partial-query projection kernel (every slice of a row would otherwise project the same query).
+// Fills the row kernel's parameters of a speculation call; with sliced rows (every slice of a row
+// would otherwise project the same query) or more than 8 batch rows, first launches the partial-query
+// projection kernel.
 int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s);
 
 template <int R>

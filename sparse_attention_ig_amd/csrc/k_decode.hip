@@ -113,7 +113,7 @@ int launch_decode_layer(const AttnCall* a, const SpecCall* sc, hipStream_t s) {
         return e ? e : launch_attn_call(*a, s);
     }
     SpecParams p;
-    int e = begin_speculate(*sc, &p, s);  // (no launch: the fused set has no slices)
+    int e = begin_speculate(*sc, &p, s);  // (the projection kernel first, beyond 8 batch rows)
     if (e) return e;
     const AttnPlan ap = plan_attn(a->B, a->H, a->d, a->max_out);
     const AttnArgs aa{a->q, a->K, a->V, a->ld_rows, a->idx, a->count, a->d, a->max_out, ap.rows_per_split, ap.nsplit,

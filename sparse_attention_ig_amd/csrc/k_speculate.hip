@@ -46,13 +46,16 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     S = (n + slice_rows - 1) / slice_rows;
     sp.ok = S <= kSpecMaxSlices;
     sp.slices = S;
+    // the projection kernel reads the partial weight once; inside the row workgroups every batch row of
+    // a head reads it again (from L2), which costs more than the extra launch beyond 8 batch rows
+    sp.proj_kernel = S > 1 || B > 8;
     sp.slice_rows = S > 1 ? slice_rows : n;
     sp.cand_cap = S > 1 ? cap : 0;
     const size_t cands = static_cast<size_t>(rows) * S * sp.cand_cap;
     sp.off_arrive = 0;
     sp.rp = plan_rehearse(B, H, D, r, n, dtype);
     sp.off_part = align256(static_cast<size_t>(B) * sizeof(uint32_t));
-    sp.off_cnt = sp.off_part + (S > 1 ? align256(sp.rp.ws_bytes) : 0);
+    sp.off_cnt = sp.off_part + (sp.proj_kernel ? align256(sp.rp.ws_bytes) : 0);
     sp.off_key = sp.off_cnt + (S > 1 ? align256(static_cast<size_t>(rows) * S * sizeof(int32_t)) : 0);
     sp.off_idx = sp.off_key + (S > 1 ? align256(cands * sizeof(uint32_t)) : 0);
     sp.ws_bytes = sp.off_idx + (S > 1 ? align256(cands * sizeof(int32_t)) : 0);
@@ -117,7 +120,7 @@ int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s) {
     const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
     char* ws = static_cast<char*>(c.ws);
     float* part = nullptr;
-    if (sp.slices > 1) {
+    if (sp.proj_kernel) {
         part = reinterpret_cast<float*>(ws + sp.off_part);
         const int e = launch_proj(c.x, c.Wq_part, c.B, c.D, c.H * c.r, c.dtype, sp.rp, part, s);
         if (e) return e;
