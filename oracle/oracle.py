@@ -363,6 +363,64 @@ def pool_append(K_bits, V_bits, Kp_bits, C, chan, k_new, v_new, n: int, victim=N
     return slots, min(n + 1, cap)
 
 
+# ---------------------------------------------------------------- INT4 host pool (follow-up)
+INT4_GROUP = 32   # elements per quantisation group (along the head dimension)
+
+
+def quantize_int4(X_bits: np.ndarray, dtype: str, group: int = INT4_GROUP):
+    """Group-wise asymmetric 4-bit quantisation of stored key or value rows: the INT4 scheme the
+    pages name among the baselines (section 5 "Evaluation Methodology", the quantised-KV baseline)
+    and propose to combine with the speculative selection (the "Follow-Up Research" paragraph on
+    combining prefetching with KV cache quantisation).
+
+    Per group of `group` consecutive elements v of a row: mn = min v, mx = max v; the group keeps
+    its minimum and step s = (mx - mn) / 15 as float16 (nearest-even), m16 and s16, and one code per
+    element, q = clamp(rint((v - m16) / s16), 0, 15) (q = 0 when s16 is 0).
+    Readings: the pages give neither the group size nor the storage of the group constants; groups
+    run along the head dimension and the constants are float16.  A code is an integer decided by
+    floating-point arithmetic, so it is decided in float32 (the precision the kernel computes in),
+    with rint rounding half to even; the values must lie in float16's range.
+    Returns codes uint8 [..., d] (0..15, one per element), s16 and m16 float16 [..., d / group]."""
+    v = decode(X_bits, dtype).astype(np.float32)
+    d = v.shape[-1]
+    assert d % group == 0
+    g = v.reshape(v.shape[:-1] + (d // group, group))
+    mn = g.min(axis=-1)
+    mx = g.max(axis=-1)
+    s = (mx - mn) / np.float32(15.0)
+    s16 = s.astype(np.float16)
+    m16 = mn.astype(np.float16)
+    sf = s16.astype(np.float32)[..., None]
+    mf = m16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = (g - mf) / sf
+    q = np.where(sf > 0, np.clip(np.rint(t), 0, 15), 0).astype(np.uint8)
+    return q.reshape(v.shape), s16, m16
+
+
+def dequantize_int4(q: np.ndarray, s16: np.ndarray, m16: np.ndarray, group: int = INT4_GROUP) -> np.ndarray:
+    """Values of quantised rows, float64: v = m16 + q * s16 for each element of a group."""
+    d = q.shape[-1]
+    qg = q.astype(np.float64).reshape(q.shape[:-1] + (d // group, group))
+    v = m16.astype(np.float64)[..., None] + qg * s16.astype(np.float64)[..., None]
+    return v.reshape(q.shape)
+
+
+def gather_kv_int4(Kq, Ks, Km, Vq, Vs, Vm, idx: np.ndarray, count: np.ndarray, max_out: int, dtype: str,
+                   group: int = INT4_GROUP):
+    """Step 5 on a quantised pool: the selected rows, dequantised (float64, then stored in `dtype`
+    as a float32-computing kernel stores them), in compact buffers [B][H][max_out][d]."""
+    B, H, _, d = Kq.shape
+    Kc = np.zeros((B, H, max_out, d))
+    Vc = np.zeros((B, H, max_out, d))
+    for b in range(B):
+        for h in range(H):
+            rows = idx[b, h, :int(count[b, h])]
+            Kc[b, h, :len(rows)] = dequantize_int4(Kq[b, h, rows], Ks[b, h, rows], Km[b, h, rows], group)
+            Vc[b, h, :len(rows)] = dequantize_int4(Vq[b, h, rows], Vs[b, h, rows], Vm[b, h, rows], group)
+    return store(Kc, dtype), store(Vc, dtype)
+
+
 # ---------------------------------------------------------------- one decode layer-step
 def decode_step(x, Wq_part, Kp, q, K, V, C, *, n, H, r, scale, mode, alpha=math.inf, k=0,
                 max_sel=0, max_out=0, cmax=65535, bq_part=None, want_victim=False):
