@@ -63,7 +63,8 @@ def main() -> int:
                     help="layer (fused path): ig_decode_layer, layer l's attention beside the speculation for "
                          "layer l+1 in one launch; serial: call after call on one stream; streams: the same "
                          "overlap from two streams")
-    ap.add_argument("--workload", choices=["opt-6.7b", "llama2-7b-long", "llama2-13b-pipeline", "opt-30b-pool"],
+    ap.add_argument("--workload", choices=["opt-6.7b", "llama2-7b-long", "llama2-13b-pipeline", "opt-30b-pool",
+                                          "opt-30b-pool-int4"],
                     default="opt-6.7b",
                     help="opt-6.7b: the headline layer; the others are extra measurements")
     ap.add_argument("--n", type=int, default=0, help="context rows (llama2-7b-long)")
@@ -110,8 +111,8 @@ def main() -> int:
 
     if args.workload == "llama2-13b-pipeline":
         return bench_pipeline(args)
-    if args.workload == "opt-30b-pool":
-        return bench_pool(args)
+    if args.workload in ("opt-30b-pool", "opt-30b-pool-int4"):
+        return bench_pool(args, int4=args.workload.endswith("int4"))
     if args.workload == "llama2-7b-long":
         spec = gen.llama2_7b_long(n=args.n or 32768, B=args.batch or 1, frac=args.frac)
     else:
@@ -401,11 +402,13 @@ def bench_pipeline(args) -> int:
     return 0
 
 
-def bench_pool(args) -> int:
-    """OPT-30B-shaped layers with the full KV cache in a pinned host pool (threshold alpha 5, 20% cap).
+def bench_pool(args, int4: bool = False) -> int:
+    """OPT-30B-shaped layers with the full KV cache in a pinned host pool (threshold alpha 5, 20% cap):
+    bf16 rows, or (int4) records of 4-bit group-wise codes with a float16 step and minimum per group of 32.
     Per layer: speculation in HBM on the main stream; the selected rows gathered over the host link
-    (zero-copy) on a side stream; attention on the compact rows once the gather is done.  The gather of
-    layer l overlaps the speculation of layer l+1 and the attention of layer l-1."""
+    (zero-copy, dequantised on the way for int4) on a side stream; attention on the compact rows once the
+    gather is done.  The gather of layer l overlaps the speculation of layer l+1 and the attention of
+    layer l-1."""
     import numpy as np
     import torch
     from sparse_attention_ig_amd import _lib, gen
@@ -417,7 +420,7 @@ def bench_pool(args) -> int:
         spec = gen.opt_30b(n=n, B=16, n_cap=4096)
         print(f"[bench] preparing opt-30b pool n={n} x {nl} host-resident layers", file=sys.stderr, flush=True)
         host = prepare_layer(spec)
-        layers = [PoolLayer(host, max_out=spec.max_sel) for _ in range(nl)]
+        layers = [PoolLayer(host, max_out=spec.max_sel, int4=int4) for _ in range(nl)]
         main = torch.cuda.current_stream()
         side = torch.cuda.Stream()
         ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -454,7 +457,7 @@ def bench_pool(args) -> int:
         ms = a.elapsed_time(b) / args.steps
         g_ms = float(np.mean([s0.elapsed_time(f) for G0, F in gathers for s0, f in zip(G0, F)]))
         cnt = sum(int(l.count.sum().item()) for l in layers) / nl
-        link_bytes = cnt * spec.d * 2 * 2
+        link_bytes = cnt * layers[0].record_bytes   # K and V rows (or the token's record) per selected row
         res[n] = {"ms_per_step": round(ms, 3), "layers": nl, "t_layer_us": round(ms * 1e3 / nl, 1),
                   "tokens_s_layer": round(spec.B * nl / (ms / 1e3), 1),
                   "selected_rows_per_layer": int(cnt), "gather_us": round(g_ms * 1e3, 1),
@@ -478,7 +481,8 @@ def bench_pool(args) -> int:
            "steps": args.steps, "warmup": 2, "ms_per_step": res[4096]["ms_per_step"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded OPT-30B-shaped draws; one layer's pool copied into each pinned buffer)",
-           "config": {"workload": f"opt-30b pinned host KV pool B16 H56 d128 D7168 r32 alpha 5 cap 20%, {nl} layers",
+           "config": {"workload": f"opt-30b pinned host KV pool{' (INT4 records, 160 B per token)' if int4 else ''} "
+                                  f"B16 H56 d128 D7168 r32 alpha 5 cap 20%, {nl} layers",
                       "per_n": res, "pinned_h2d_copy_GBs": round(h2d, 2)}}
     print(json.dumps(out), flush=True)
     return 0

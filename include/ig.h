@@ -55,7 +55,7 @@ const char* ig_last_error(void);
 /* ABI version: bumped on any signature or layout change (2: ig_pool_touch takes a
  * workspace; 3: Wq_part is stored one row per partial column, [H*r][D];
  * 4: ig_decode_layer; 5: ig_partial_weight_index_dev; 6: the speculation
- * workspace starts with its arrival words). */
+ * workspace starts with its arrival words; 7: the INT4 pool calls). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -339,12 +339,63 @@ int ig_build_partial_cache(const void* K, const int32_t* chan, void* Kp,
  * else victim[b] (victim required then); K[b][h][slot] = k_new[b][h],
  * V[b][h][slot] = v_new[b][h], Kp[b][h][slot][c] = k_new[b][h][chan[h][c]],
  * counters[b][slot] = 0 (if counters not NULL); slot_out[b] = slot (if not
- * NULL).  k_new, v_new [B][H][d] dtype.
+ * NULL).  k_new, v_new [B][H][d] dtype.  K and V may both be NULL (a pool kept
+ * as INT4 records, see ig_quantize_kv): then only the partial key row, the
+ * counter and slot_out are written.
  */
 int ig_append_kv(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan,
                  const void* k_new, const void* v_new, const int32_t* victim,
                  int B, int H, int d, int r, int n_cap, int n, int dtype,
                  int32_t* slot_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ INT4 pool */
+
+/*
+ * A KV pool stored at 4 bits per element, of which only the speculated rows
+ * are fetched: the combination the summary proposes under "Follow-Up
+ * Research" (speculative prefetching of a quantised pool), with the 4-bit
+ * group-wise asymmetric quantisation of its section 5 baselines.  The partial
+ * key cache (Kp) stays at full precision in HBM, so the speculation is
+ * unchanged.
+ *
+ * Record of one token's key and value rows of d elements each (d a multiple
+ * of 32), of ig_int4_record_bytes(d) bytes (160 for d = 128): K codes in
+ * bytes [0, d/2), V codes in [d/2, d) (element i in byte i/2 of its half, low
+ * nibble for even i); then for each group g of 32 elements, the K groups
+ * first, a float16 step s16 and a float16 minimum m16 (bytes d + 4g and
+ * d + 4g + 2, little endian); zero padding to a multiple of 32 bytes.  A
+ * fetched token costs three 64-byte reads over the host link (a bf16 K and V
+ * row, eight).  Record arrays are [B][H][q_rows][record bytes].
+ */
+size_t ig_int4_record_bytes(int d);   /* 0 if d is not a positive multiple of 32 */
+
+/*
+ * Quantise rows [row0, row0 + nrows) of every (b, h) of K and V
+ * [B][H][ld_rows][d] (dtype bf16 or f32, device memory) into the records of
+ * KVq (device or host-mapped memory; writes over the host link are zero-copy).  Per group of
+ * 32 values: mn, mx; s16 = half((mx - mn) / 15) and m16 = half(mn), nearest
+ * even; code = clamp(rint((v - m16) / s16), 0, 15) in float32 (correctly
+ * rounded division, halves to even), 0 when s16 is 0.  Values must lie in
+ * float16's range.  Destination row = the source row, or, with slot [B] (not
+ * NULL), slot[b] + (row - row0): the append of a new token, with K, V = the
+ * new rows [B][H][1][d], row0 = 0, nrows = 1 and the slot_out of ig_append_kv
+ * (called with K = V = NULL, which then writes only the partial key row and
+ * the counter).  Destination rows are clamped into [0, q_rows).
+ */
+int ig_quantize_kv(const void* K, const void* V, int B, int H, int d, int ld_rows, int dtype, int row0, int nrows,
+                   const int32_t* slot, void* KVq, int q_rows, hipStream_t stream);
+
+/*
+ * Step 5 on a quantised pool: for i < min(count[b][h], max_out) and
+ * j = idx[b][h][i] (clamped into [0, q_rows)), Kc[b][h][i] and Vc[b][h][i]
+ * = the dequantised rows, v = m16 + code * s16 in float32, stored as
+ * dtype_out (bf16, nearest even, or f32).  KVq: the record array in device
+ * or host-mapped memory (zero-copy reads over the host link); Kc, Vc
+ * [B][H][max_out][d] device.
+ */
+int ig_gather_kv_int4(const void* KVq, const int32_t* idx, const int32_t* count,
+                      int B, int H, int d, int q_rows, int max_out, int dtype_out,
+                      void* Kc, void* Vc, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,9 @@ _SIGS = {
     "ig_partial_weight_index_dev": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "ig_build_partial_cache": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "ig_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "ig_int4_record_bytes": (_sz, [_i]),
+    "ig_quantize_kv": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp]),
+    "ig_gather_kv_int4": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -379,9 +382,42 @@ def ig_build_partial_cache(K, chan, Kp, row0: int, row1: int, *, stream=None):
 
 
 def ig_append_kv(K, V, Kp, counters, chan, k_new, v_new, n: int, *, victim=None, slot_out=None, stream=None):
-    B, H, n_cap, d = K.shape
-    r = Kp.shape[3]
+    """K = V = None: a pool kept as INT4 records (only the partial key row, counter and slot are written)."""
+    B, H, n_cap, r = Kp.shape
+    d = k_new.shape[2]
     _check(load().ig_append_kv(_ptr(K), _ptr(V), _ptr(Kp), _ptr(counters), _ptr(chan), _ptr(k_new), _ptr(v_new),
-                               _ptr(victim), B, H, d, r, n_cap, n, _dtype_of(K), _ptr(slot_out), _stream(stream)),
+                               _ptr(victim), B, H, d, r, n_cap, n, _dtype_of(k_new), _ptr(slot_out),
+                               _stream(stream)),
            "ig_append_kv")
     return slot_out
+
+
+# ---------------------------------------------------------------- INT4 pool
+def ig_int4_record_bytes(d: int) -> int:
+    return int(load().ig_int4_record_bytes(int(d)))
+
+
+def ig_quantize_kv(K, V, KVq, row0: int = 0, nrows: Optional[int] = None, *, slot=None, stream=None):
+    """Records of rows [row0, row0 + nrows) of K, V [B][H][ld_rows][d] into KVq [B][H][q_rows][record bytes]
+    (a uint8 device tensor or a MappedHost view); slot [B] int32: destination slot[b] + row - row0."""
+    B, H, ld_rows, d = K.shape
+    q_rows = KVq.shape[2]
+    nrows = ld_rows - row0 if nrows is None else nrows
+    _check(load().ig_quantize_kv(_ptr(K), _ptr(V), B, H, d, ld_rows, _dtype_of(K), int(row0), int(nrows), _ptr(slot),
+                                 _ptr(KVq), q_rows, _stream(stream)), "ig_quantize_kv")
+    return KVq
+
+
+def ig_gather_kv_int4(KVq, idx, count, d: int, *, Kc=None, Vc=None, dtype_out=None, stream=None):
+    """Selected records of KVq [B][H][q_rows][record bytes], dequantised into compact Kc, Vc
+    [B][H][max_out][d] (bf16 unless Kc is given as float32)."""
+    torch = _torch()
+    B, H, q_rows, _ = KVq.shape
+    max_out = idx.shape[2]
+    if Kc is None:
+        dt = torch.bfloat16 if dtype_out in (None, "bf16") else torch.float32
+        Kc = torch.empty((B, H, max_out, d), dtype=dt, device=idx.device)
+        Vc = torch.empty_like(Kc)
+    _check(load().ig_gather_kv_int4(_ptr(KVq), _ptr(idx), _ptr(count), B, H, d, q_rows, max_out,
+                                    _dtype_of(Kc), _ptr(Kc), _ptr(Vc), _stream(stream)), "ig_gather_kv_int4")
+    return Kc, Vc

@@ -22,7 +22,7 @@ OUT = os.path.join(PKG, "libig.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["ig_capi.cpp", "ig_setup.cpp", "k_rehearse.hip", "k_select.hip", "k_attn.hip", "k_pool.hip", "k_speculate.hip", "k_decode.hip", "k_setup.hip"]
+SOURCES = ["ig_capi.cpp", "ig_setup.cpp", "k_rehearse.hip", "k_select.hip", "k_attn.hip", "k_pool.hip", "k_speculate.hip", "k_decode.hip", "k_setup.hip", "k_quant.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include")]

@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 6; }
+int ig_version(void) { return 7; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 
@@ -301,13 +301,41 @@ int ig_append_kv(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* 
                  const void* v_new, const int32_t* victim, int B, int H, int d, int r, int n_cap, int n, int dtype,
                  int32_t* slot_out, hipStream_t stream) {
     IG_REQUIRE_DTYPE("ig_append_kv", dtype);
-    IG_REQUIRE(K && V && Kp && chan && k_new && v_new, "ig_append_kv: NULL required pointer");
+    IG_REQUIRE(Kp && chan && k_new && v_new && (K != nullptr) == (V != nullptr), "ig_append_kv: NULL required pointer");
     IG_REQUIRE(B >= 1 && H >= 1 && d >= 1 && r >= 1 && r <= d && 0 <= n && n <= n_cap && n_cap >= 1,
                "ig_append_kv: bad sizes");
     IG_REQUIRE(n < n_cap || victim, "ig_append_kv: the pool is full (n == n_cap): victim is required");
     return hip_status(launch_append(K, V, Kp, counters, chan, k_new, v_new, victim, B, H, d, r, n_cap, n, dtype,
                                     slot_out, stream),
                       "ig_append_kv");
+}
+
+size_t ig_int4_record_bytes(int d) { return d >= 32 && d % 32 == 0 ? int4_record_bytes(d) : 0; }
+
+int ig_quantize_kv(const void* K, const void* V, int B, int H, int d, int ld_rows, int dtype, int row0, int nrows,
+                   const int32_t* slot, void* KVq, int q_rows, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_quantize_kv", dtype);
+    IG_REQUIRE(K && V && KVq, "ig_quantize_kv: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && d >= 32 && d % 32 == 0 && d <= 4096, "ig_quantize_kv: d must be a multiple of 32 "
+               "(got %d)", d);
+    IG_REQUIRE(0 <= row0 && nrows >= 0 && row0 + nrows <= ld_rows && q_rows >= 1,
+               "ig_quantize_kv: bad rows (row0=%d nrows=%d ld_rows=%d q_rows=%d)", row0, nrows, ld_rows, q_rows);
+    IG_REQUIRE(slot || row0 + nrows <= q_rows, "ig_quantize_kv: rows beyond the record array");
+    IG_REQUIRE(aligned16(K) && aligned16(V) && aligned16(KVq), "ig_quantize_kv: K, V and KVq must be 16-byte aligned");
+    return hip_status(launch_quantize(K, V, B, H, d, ld_rows, dtype, row0, nrows, slot, KVq, q_rows, stream),
+                      "ig_quantize_kv");
+}
+
+int ig_gather_kv_int4(const void* KVq, const int32_t* idx, const int32_t* count, int B, int H, int d, int q_rows,
+                      int max_out, int dtype_out, void* Kc, void* Vc, hipStream_t stream) {
+    IG_REQUIRE_DTYPE("ig_gather_kv_int4", dtype_out);
+    IG_REQUIRE(KVq && idx && count && Kc && Vc, "ig_gather_kv_int4: NULL required pointer");
+    IG_REQUIRE(B >= 1 && H >= 1 && q_rows >= 1 && max_out >= 1, "ig_gather_kv_int4: bad sizes");
+    IG_REQUIRE(d >= 32 && d % 32 == 0 && d <= 4096, "ig_gather_kv_int4: d must be a multiple of 32 (got %d)", d);
+    IG_REQUIRE(aligned16(KVq) && aligned16(Kc) && aligned16(Vc), "ig_gather_kv_int4: KVq, Kc, Vc must be 16-byte "
+               "aligned");
+    return hip_status(launch_gather_q4(KVq, idx, count, B, H, d, q_rows, max_out, dtype_out, Kc, Vc, stream),
+                      "ig_gather_kv_int4");
 }
 
 }  // extern "C"

@@ -15,6 +15,13 @@ template <> struct Vec<float> { static constexpr int N = 4; };
 template <> struct Vec<uint16_t> { static constexpr int N = 8; };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// float32 -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
 
 // 16-byte load of N elements, widened to float.
 __device__ __forceinline__ void load_vec(const float* __restrict__ p, float (&v)[4]) {

@@ -132,6 +132,11 @@ struct SpecCall {
 constexpr int kDecodeMaxRows = 16384;  // rows per (b, h) for the fused decode launch (LDS with two roles)
 bool decode_fusable(const AttnCall& a, const SpecCall& s);
 int launch_decode_layer(const AttnCall* a, const SpecCall* s, hipStream_t st);
+size_t int4_record_bytes(int d);
+int launch_quantize(const void* K, const void* V, int B, int H, int d, int ld_rows, int dtype, int row0, int nrows,
+                    const int32_t* slot, void* KVq, int q_rows, hipStream_t s);
+int launch_gather_q4(const void* KVq, const int32_t* idx, const int32_t* count, int B, int H, int d, int q_rows,
+                     int max_out, int dtype_out, void* Kc, void* Vc, hipStream_t s);
 int launch_build_partial(const void* K, const int32_t* chan, void* Kp, int B, int H, int d, int r,
                          int n_cap, int row0, int row1, int dtype, hipStream_t s);
 int launch_append(void* K, void* V, void* Kp, uint32_t* counters, const int32_t* chan,

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void k_append(T* __restrict__ K, T* __restrict
     int slot = n < n_cap ? n : victim[b];
     slot = min(max(slot, 0), n_cap - 1);
     const size_t row = (static_cast<size_t>(bh) * n_cap + slot);
-    for (int t = threadIdx.x; t < d; t += 256) {
+    for (int t = threadIdx.x; K && t < d; t += 256) {  // (no full rows: a quantised pool takes them)
         K[row * d + t] = k_new[static_cast<size_t>(bh) * d + t];
         V[row * d + t] = v_new[static_cast<size_t>(bh) * d + t];
     }

@@ -237,27 +237,42 @@ class MappedHost:
 
 
 class PoolLayer:
-    """A layer whose full key / value cache lives in pinned host memory (the KV pool), with the partial
-    key cache, weights, query and counters in HBM.  The selected rows are fetched over the host link by
+    """A layer whose full key / value cache lives in pinned host memory (the KV pool: bf16 rows, or INT4
+    records with ``int4``), with the partial key cache, weights, query and counters in HBM.  The selected rows are fetched over the host link by
     ig_gather_kv (zero-copy reads of the pinned pool) into compact HBM buffers, and the attention runs on
     those (the summary's section 3.2 Pool Manager and section 3.4 "Decoding Stage" step 5)."""
 
-    def __init__(self, host: HostLayer, max_out: int):
+    def __init__(self, host: HostLayer, max_out: int, int4: bool = False):
         import torch
         from . import _lib as L
         s = host.spec
         self.spec = s
         self.max_out = max_out
-        self.Kh_host = torch.from_numpy(host.K.view(np.int16)).view(torch.bfloat16).pin_memory()
-        self.Vh_host = torch.from_numpy(host.V.view(np.int16)).view(torch.bfloat16).pin_memory()
-        self.Kh, self.Vh = MappedHost(self.Kh_host), MappedHost(self.Vh_host)
+        self.int4 = int4
         self.x = to_device(host.x)
         self.Wq_part = to_device(host.Wq_part)
         self.chan = to_device(host.chan)
         self.q = to_device(host.q)
         dv = "cuda"
         self.Kp = torch.zeros((s.B, s.H, s.cap, s.r), dtype=torch.bfloat16, device=dv)
-        L.ig_build_partial_cache(self.Kh, self.chan, self.Kp, 0, s.n)   # reads the pinned pool directly
+        if int4:
+            # the pool as INT4 records (ig_quantize_kv writes them over the host link from a transient
+            # device copy of the prefilled cache); the partial key cache keeps full precision in HBM
+            rec = L.ig_int4_record_bytes(s.d)
+            self.KVq_host = torch.zeros((s.B, s.H, s.cap, rec), dtype=torch.uint8).pin_memory()
+            self.KVq = MappedHost(self.KVq_host)
+            Kd, Vd = to_device(host.K), to_device(host.V)
+            L.ig_quantize_kv(Kd, Vd, self.KVq, 0, s.n)
+            L.ig_build_partial_cache(Kd, self.chan, self.Kp, 0, s.n)
+            torch.cuda.synchronize()
+            del Kd, Vd
+            self.record_bytes = rec
+        else:
+            self.Kh_host = torch.from_numpy(host.K.view(np.int16)).view(torch.bfloat16).pin_memory()
+            self.Vh_host = torch.from_numpy(host.V.view(np.int16)).view(torch.bfloat16).pin_memory()
+            self.Kh, self.Vh = MappedHost(self.Kh_host), MappedHost(self.Vh_host)
+            L.ig_build_partial_cache(self.Kh, self.chan, self.Kp, 0, s.n)   # reads the pinned pool directly
+            self.record_bytes = 2 * s.d * 2   # a K and a V row
         self.counters = torch.zeros((s.B, s.cap), dtype=torch.int32, device=dv)
         self.idx = torch.empty((s.B, s.H, max_out), dtype=torch.int32, device=dv)
         self.count = torch.empty((s.B, s.H), dtype=torch.int32, device=dv)
@@ -283,7 +298,28 @@ class PoolLayer:
 
     def gather(self, stream=None):
         from . import _lib as L
-        L.ig_gather_kv(self.Kh, self.Vh, self.idx, self.count, Kc=self.Kc, Vc=self.Vc, stream=stream)
+        if self.int4:
+            L.ig_gather_kv_int4(self.KVq, self.idx, self.count, self.spec.d, Kc=self.Kc, Vc=self.Vc, stream=stream)
+        else:
+            L.ig_gather_kv(self.Kh, self.Vh, self.idx, self.count, Kc=self.Kc, Vc=self.Vc, stream=stream)
+
+    def append(self, k_new, v_new, n: int, *, victim=None, slot_out=None, stream=None):
+        """The new token's rows into the pool (slot n, or the victim when full): full rows, or INT4 records
+        written at the slot ig_append_kv picked; the partial key row and the counter in HBM."""
+        import torch
+        from . import _lib as L
+        s = self.spec
+        if slot_out is None:
+            slot_out = torch.empty((s.B,), dtype=torch.int32, device="cuda")
+        if self.int4:
+            L.ig_append_kv(None, None, self.Kp, self.counters, self.chan, k_new, v_new, n, victim=victim,
+                           slot_out=slot_out, stream=stream)
+            L.ig_quantize_kv(k_new.view(s.B, s.H, 1, s.d), v_new.view(s.B, s.H, 1, s.d), self.KVq, 0, 1, slot=slot_out,
+                             stream=stream)
+        else:
+            L.ig_append_kv(self.Kh, self.Vh, self.Kp, self.counters, self.chan, k_new, v_new, n, victim=victim,
+                           slot_out=slot_out, stream=stream)
+        return slot_out
 
     def attend(self, stream=None):
         from . import _lib as L

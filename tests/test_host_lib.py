@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(L.exported_symbols())
     for name in declared:
         assert hasattr(lib, name)
-    assert L.ig_version() == 6
+    assert L.ig_version() == 7
 
 
 @pytest.mark.parametrize("m,d", [(256, 64), (128, 128), (64, 16)])
@@ -138,6 +138,16 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     # no workspace
     assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 40, 40, L.IG_BF16, f(1.0), L.IG_SEL_TOPK, f(0.0), 4, 0,
                             p, p, 4, p, 15, None, None, None, 40, None, 0, None) == L.IG_EINVAL
+    # INT4 pool: d not a multiple of 32, rows past the record array, NULL records
+    assert L.ig_int4_record_bytes(128) == 160 and L.ig_int4_record_bytes(64) == 96 and L.ig_int4_record_bytes(48) == 0
+    assert lib.ig_quantize_kv(p, p, 1, 1, 48, 8, L.IG_BF16, 0, 8, None, p, 8, None) == L.IG_EINVAL
+    assert lib.ig_quantize_kv(p, p, 1, 1, 64, 8, L.IG_BF16, 0, 8, None, p, 4, None) == L.IG_EINVAL
+    assert lib.ig_quantize_kv(p, p, 1, 1, 64, 8, L.IG_BF16, 4, 8, None, p, 16, None) == L.IG_EINVAL
+    assert lib.ig_quantize_kv(p, None, 1, 1, 64, 8, L.IG_BF16, 0, 8, None, p, 8, None) == L.IG_EINVAL
+    assert lib.ig_gather_kv_int4(None, p, p, 1, 1, 64, 8, 4, L.IG_BF16, p, p, None) == L.IG_EINVAL
+    assert lib.ig_gather_kv_int4(p, p, p, 1, 1, 40, 8, 4, L.IG_BF16, p, p, None) == L.IG_EINVAL
+    # append: K without V
+    assert lib.ig_append_kv(p, None, p, p, p, p, p, None, 1, 1, 64, 8, 4, 1, L.IG_BF16, None, None) == L.IG_EINVAL
     # host setup: m < d
     args = L.SkewArgs(0, 1, 8, 4, 16, None, None, None, None, 16, None, None, None, None, None, 1)
     assert lib.ig_skew_weights(ctypes.byref(args)) == L.IG_EINVAL
