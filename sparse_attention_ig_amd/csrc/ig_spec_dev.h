@@ -87,7 +87,8 @@ struct SpecShared {
 // barrier; q (and q_out, when not NULL) then hold the sums.
 template <typename T, int NT, int R, int U>
 __device__ __forceinline__ void project_partial(const T* __restrict__ x, const T* __restrict__ W, int D,
-                                                const float* __restrict__ bias, uint4* xs, float* q, float* q_out) {
+                                                const float* __restrict__ bias, int rot, uint4* xs, float* q,
+                                                float* q_out) {
     constexpr int VEC = Vec<T>::N;
     constexpr int G = NT / R < 64 ? NT / R : 64;
     static_assert(G >= 1, "at most one partial channel per thread");
@@ -96,9 +97,12 @@ __device__ __forceinline__ void project_partial(const T* __restrict__ x, const T
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     for (int i = tid; i < nv; i += NT) xs[i] = xv[i];
     __syncthreads();
-    const int c = tid / G, g = tid % G;
+    // lane group tid / G takes row (tid / G + rot) mod R: workgroups that read the same rows at once
+    // (the batch rows of a head) start on different rows; a row's sum order does not depend on rot
+    const bool on = tid / G < R;
+    const int c = (tid / G + rot) % R, g = tid % G;
     float acc = 0.f;
-    if (c < R) {
+    if (on) {
         const uint4* wv = reinterpret_cast<const uint4*>(W + static_cast<size_t>(c) * D);
         for (int i0 = g; i0 < nv; i0 += G * U) {
             uint4 w[U];
@@ -121,7 +125,7 @@ __device__ __forceinline__ void project_partial(const T* __restrict__ x, const T
         }
     }
     acc = group_sum<G>(acc);  // whole groups: threads past R * G hold zeros in groups of their own
-    if (c < R && g == 0) {
+    if (on && g == 0) {
         const float v = bias ? acc + bias[c] : acc;
         q[c] = v;
         if (q_out) q_out[c] = v;
@@ -328,8 +332,8 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
     else
         project_partial<T, kSpecThreads, R, PU>(static_cast<const T*>(p.x) + static_cast<size_t>(b) * p.D,
                                                 static_cast<const T*>(p.W) + static_cast<size_t>(h) * R * p.D, p.D,
-                                                p.bias ? p.bias + h * R : nullptr, reinterpret_cast<uint4*>(keys), s_q,
-                                                q_out);
+                                                p.bias ? p.bias + h * R : nullptr, b * R / p.B,
+                                                reinterpret_cast<uint4*>(keys), s_q, q_out);
     if constexpr (!PRE) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
