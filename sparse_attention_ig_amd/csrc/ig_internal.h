@@ -46,7 +46,7 @@ size_t select_ws_bytes(int B, int H, int n, int max_out);
 constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
 constexpr int kSpecMaxSlices = 16;    // slices per row of the fused speculation
 struct SpecPlan {
-    RehearsePlan rp;                  // the projection kernel of sliced rows
+    RehearsePlan rp;                  // the projection kernel (sliced rows, batches beyond 8 rows)
     int slices, slice_rows, cand_cap;
     bool proj_kernel;                 // the partial query comes from the projection kernel's partial sums
     bool ok;                          // false: rows too long for the candidates to fit one merge

@@ -1,10 +1,11 @@
 // Fused speculation entry point: one 1024-thread workgroup per (b, h) running
 // spec_row (partial query, scores, selection and counters with the scores kept
-// on chip).  Sliced rows: the partial-query projection kernel first.  Few rows, or rows longer than one
-// workgroup's LDS: each row is cut into slices, one workgroup each, that leave
-// their local selection as candidates, and a merge workgroup per row selects
-// among them.  InfiniGen, arXiv 2406.19707, paper-graph-ui summary, section
-// 3.4 "Decoding Stage" steps 1-3 and 5.
+// on chip).  Few rows, or rows longer than one workgroup's LDS: each row is cut
+// into slices, one workgroup each, that leave their local selection as
+// candidates, and a merge workgroup per row selects among them.  Sliced rows
+// and batches beyond 8 rows take their partial query from the projection
+// kernel launched first.  InfiniGen, arXiv 2406.19707, paper-graph-ui summary,
+// section 3.4 "Decoding Stage" steps 1-3 and 5.
 #include <algorithm>
 
 #include "ig_spec_dev.h"
