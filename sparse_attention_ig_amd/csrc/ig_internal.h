@@ -45,12 +45,14 @@ size_t select_ws_bytes(int B, int H, int n, int max_out);
 
 constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
 constexpr int kSpecMaxSlices = 16;    // slices per row of the fused speculation
+constexpr int64_t kBitsTouchMin = 262144;  // selected slots per call from which sliced rows use bitmaps
 struct SpecPlan {
     RehearsePlan rp;                  // the projection kernel (sliced rows, batches beyond 8 rows)
     int slices, slice_rows, cand_cap;
     bool proj_kernel;                 // the partial query comes from the projection kernel's partial sums
+    bool bits;                        // the merge leaves bitmaps and a counter kernel applies them
     bool ok;                          // false: rows too long for the candidates to fit one merge
-    size_t off_arrive, off_part, off_cnt, off_key, off_idx, ws_bytes;
+    size_t off_arrive, off_part, off_cnt, off_key, off_idx, off_bits, off_flags, ws_bytes;
 };
 SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);
@@ -75,6 +77,8 @@ int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n,
                  int n_cap, int max_out, uint32_t cmax, int32_t* victim, void* ws, hipStream_t s);
 size_t touch_ws_bytes(int B);
+int launch_touch_bits(uint32_t* counters, const uint32_t* bits, int B, int H, int n, int n_cap, uint32_t cmax,
+                      uint32_t* flags, int32_t* victim, hipStream_t s);
 bool touch_single_kernel(int H, int max_out);
 int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H,
                      int r, int n, int n_cap, int dtype, float scale, int mode, float alpha, int k, int max_sel,

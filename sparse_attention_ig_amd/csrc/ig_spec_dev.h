@@ -65,6 +65,9 @@ struct SpecParams {
     uint32_t* cand_key;      // [B*H][slices][cand_cap]
     int32_t* cand_idx;       // [B*H][slices][cand_cap] row indices
     int32_t* cand_cnt;       // [B*H][slices]
+    // large merges: the merge leaves each row's selection as a bitmap [B*H][ceil(n / 32)] and a counter
+    // kernel adds the heads' bits per slot (no atomics per selected slot); NULL: atomics in the merge
+    uint32_t* bits;
 };
 
 // Fills the row kernel's parameters of a speculation call; with sliced rows (every slice of a row
@@ -239,6 +242,21 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
         if (tid == 0) p.count[bh] = min(written, p.max_out);
         if (!crow) return;
         __syncthreads();
+        if (p.bits) {
+            // the row's selection as a bitmap of its n slots, built in LDS and written out whole
+            const int nw = (n + 31) / 32;
+            const int w = min(written, p.max_out);
+            for (int i = tid; i < nw; i += kSpecThreads) lds[i] = 0u;
+            __syncthreads();
+            for (int i = tid; i < w; i += kSpecThreads) {
+                const uint32_t j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
+                if (j < static_cast<uint32_t>(n)) atomicOr(&lds[j >> 5], 1u << (j & 31u));
+            }
+            __syncthreads();
+            uint32_t* dst = p.bits + static_cast<size_t>(bh) * nw;
+            for (int i = tid; i < nw; i += kSpecThreads) dst[i] = lds[i];
+            return;
+        }
         int sat = 0;
         // (written <= max_out and every staged index is < n by construction; both are re-checked so
         // that no counter update can land outside the row)

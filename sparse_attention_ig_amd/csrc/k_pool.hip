@@ -81,8 +81,9 @@ __global__ __launch_bounds__(256) void k_touch_inc(uint32_t* __restrict__ C, con
     }
 }
 
+// Per-sequence finish: halve if flagged, pick the victim; the flag is returned to zero.
 __global__ __launch_bounds__(kTouchThreads) void k_touch_finish(uint32_t* __restrict__ C, int n, int n_cap,
-                                                               uint32_t cmax, const uint32_t* __restrict__ flags,
+                                                               uint32_t cmax, uint32_t* __restrict__ flags,
                                                                int32_t* __restrict__ victim) {
     __shared__ uint32_t s_val[kTouchThreads / kWave];
     __shared__ int s_idx[kTouchThreads / kWave];
@@ -90,7 +91,55 @@ __global__ __launch_bounds__(kTouchThreads) void k_touch_finish(uint32_t* __rest
     const bool halve = flags[b] != 0u;
     const int v = pool_finish<kTouchThreads>(C + static_cast<size_t>(b) * n_cap, n, cmax, halve, victim != nullptr,
                                               s_val, s_idx);
-    if (victim && threadIdx.x == 0) victim[b] = v;
+    __syncthreads();  // every thread has read the flag
+    if (threadIdx.x == 0) {
+        if (victim) victim[b] = v;
+        flags[b] = 0u;
+    }
+}
+
+// Counters from the heads' selection bitmaps [B*H][ceil(n / 32)]: a workgroup owns 256 consecutive slots
+// of sequence b (8 bitmap words per head).  It stages those words of every head in LDS (coalesced loads),
+// then the thread of slot j adds the number of heads whose bit j is set to its counter (each slot has one
+// owner: no atomics; the counters are read and written coalesced); a workgroup that saturated a slot
+// flags its sequence for the finish.
+constexpr int kBitsHeadsMax = 128;
+__global__ __launch_bounds__(256) void k_touch_bits(uint32_t* __restrict__ C, const uint32_t* __restrict__ bits,
+                                                   int H, int n, int n_cap, uint32_t cmax,
+                                                   uint32_t* __restrict__ flags) {
+    __shared__ uint32_t s_w[kBitsHeadsMax * 8];
+    const int b = blockIdx.y, tid = threadIdx.x;
+    const int nw = (n + 31) / 32;
+    const int w0 = blockIdx.x * 8;
+    for (int e = tid; e < H * 8; e += 256) {
+        const int h = e / 8, w = w0 + e % 8;
+        s_w[e] = w < nw ? bits[(static_cast<size_t>(b) * H + h) * nw + w] : 0u;
+    }
+    __syncthreads();
+    const int j = blockIdx.x * 256 + tid;
+    int sat = 0;
+    if (j < n) {
+        uint32_t inc = 0;
+        const uint32_t* col = s_w + tid / 32;
+        for (int h = 0; h < H; ++h) inc += (col[h * 8] >> (tid & 31)) & 1u;
+        if (inc) {
+            uint32_t* c = C + static_cast<size_t>(b) * n_cap + j;
+            const uint32_t v = *c + inc;
+            *c = v;
+            sat = v >= cmax ? 1 : 0;
+        }
+    }
+    if (__syncthreads_or(sat) && tid == 0) atomicOr(&flags[b], 1u);
+}
+
+int launch_touch_bits(uint32_t* counters, const uint32_t* bits, int B, int H, int n, int n_cap, uint32_t cmax,
+                      uint32_t* flags, int32_t* victim, hipStream_t s) {
+    hipLaunchKernelGGL(k_touch_bits, dim3((n + 255) / 256, B), dim3(256), 0, s, counters, bits, H, n, n_cap, cmax,
+                       flags);
+    const int e = static_cast<int>(hipGetLastError());
+    if (e) return e;
+    hipLaunchKernelGGL(k_touch_finish, dim3(B), dim3(kTouchThreads), 0, s, counters, n, n_cap, cmax, flags, victim);
+    return static_cast<int>(hipGetLastError());
 }
 
 size_t touch_ws_bytes(int B) { return ((static_cast<size_t>(B) * sizeof(uint32_t) + 255) / 256) * 256; }

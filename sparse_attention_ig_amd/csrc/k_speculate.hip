@@ -59,7 +59,12 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     sp.off_cnt = sp.off_part + (sp.proj_kernel ? align256(sp.rp.ws_bytes) : 0);
     sp.off_key = sp.off_cnt + (S > 1 ? align256(static_cast<size_t>(rows) * S * sizeof(int32_t)) : 0);
     sp.off_idx = sp.off_key + (S > 1 ? align256(cands * sizeof(uint32_t)) : 0);
-    sp.ws_bytes = sp.off_idx + (S > 1 ? align256(cands * sizeof(int32_t)) : 0);
+    // many selected slots per sequence: counter atomics in the merge would be throughput-bound
+    sp.bits = S > 1 && H <= 128 && rows * std::min(max_out, n) >= kBitsTouchMin;
+    const size_t nw = (static_cast<size_t>(n) + 31) / 32;
+    sp.off_bits = sp.off_idx + (S > 1 ? align256(cands * sizeof(int32_t)) : 0);
+    sp.off_flags = sp.off_bits + (sp.bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
+    sp.ws_bytes = sp.off_flags + (sp.bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
     return sp;
 }
 
@@ -112,8 +117,8 @@ static int launch_merge(const SpecParams& p, hipStream_t s) {
         attr_set = true;
     }
     const int m = p.slices * p.cand_cap;
-    hipLaunchKernelGGL(k_spec_merge, dim3(p.B * p.H), dim3(kSpecThreads),
-                       speculate_lds_bytes(m <= kSpecMaxRows ? m : 0, 0), s, p);
+    const int words = std::max(m <= kSpecMaxRows ? m : 0, p.bits ? (p.n + 31) / 32 : 0);  // keys or the bitmap
+    hipLaunchKernelGGL(k_spec_merge, dim3(p.B * p.H), dim3(kSpecThreads), speculate_lds_bytes(words, 0), s, p);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -133,6 +138,7 @@ int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s) {
                     reinterpret_cast<uint32_t*>(ws + sp.off_arrive), c.H % 8 == 0 ? 1 : 0, sp.slices, sp.slice_rows,
                     sp.cand_cap, reinterpret_cast<uint32_t*>(ws + sp.off_key), reinterpret_cast<int32_t*>(ws + sp.off_idx),
                     reinterpret_cast<int32_t*>(ws + sp.off_cnt)};
+    if (sp.bits && c.counters) p->bits = reinterpret_cast<uint32_t*>(ws + sp.off_bits);
     return 0;
 }
 
@@ -147,7 +153,10 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     if (e) return e;
     e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
     if (e || p.slices == 1) return e;
-    return launch_merge(p, s);
+    if ((e = launch_merge(p, s)) || !p.bits) return e;
+    const SpecPlan sp = plan_speculate(B, H, D, r, n, max_out, dtype);
+    return launch_touch_bits(counters, p.bits, B, H, n, n_cap, cmax,
+                             reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), victim, s);
 }
 
 __global__ void k_zero_words(uint32_t* p, size_t n) {

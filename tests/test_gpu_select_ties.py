@@ -162,3 +162,38 @@ def test_speculate_integer_scores_exact(n, mode, kw, max_out):
         for h in range(H):
             c = rcnt[b, h]
             assert np.array_equal(idx[b, h, :c], ridx[b, h, :c]), (b, h)
+
+
+@pytest.mark.parametrize("cmax", [65535, 12], ids=["no-halving", "halving"])
+def test_speculate_counters_from_bitmaps_exact(cmax):
+    """Sliced rows with many selected slots per call (2 x 16 heads x 8192 of 65536): the merge leaves
+    bitmaps and a counter kernel adds them.  Counters (with the halving when a slot reaches cmax) and the
+    victim must equal the oracle's pool update exactly, on integer-valued scores."""
+    import torch
+    from sparse_attention_ig_amd import _lib as L
+    rng = np.random.default_rng(cmax)
+    B, H, r, D, n, k = 2, 16, 32, 256, 65536, 8192
+    x = np.zeros((B, D), np.float32)
+    x[:, 0] = 1.0
+    W = np.zeros((D, H * r), np.float32)
+    W[0] = rng.integers(-6, 7, H * r)
+    Kp = rng.integers(-8, 9, (B, H, n, r)).astype(np.float32)
+    x, W, Kp = gen.encode(x, "bf16"), gen.encode(W, "bf16"), gen.encode(Kp, "bf16")
+    C0 = rng.integers(0, min(cmax, 6) - 1, (B, n)).astype(np.uint32)
+    counters = dev(C0)
+    victim = torch.empty((B,), dtype=torch.int32, device="cuda")
+    say(f"[speculate bitmap counters] cmax={cmax}")
+    idx, cnt = L.ig_speculate(dev(x), dev(np.ascontiguousarray(W.T)), dev(Kp), n, 0.5, "topk", k, k=k,
+                              counters=counters, cmax=cmax, victim=victim)
+    idx, cnt, C, v = host(idx), host(cnt), host(counters).view(np.uint32), host(victim)
+    _, sc = O.rehearse(O.decode(x, "bf16"), O.decode(W, "bf16"), O.decode(Kp, "bf16"), n, H, r, 0.5)
+    ridx, rcnt = O.select(sc, "topk", k=k, max_out=k)
+    assert np.array_equal(cnt, rcnt)
+    for b in range(B):
+        for h in range(H):
+            assert np.array_equal(idx[b, h, :rcnt[b, h]], ridx[b, h, :rcnt[b, h]]), (b, h)
+    C_ref, v_ref = O.pool_touch(C0.copy(), ridx, rcnt, n, cmax, True)
+    assert np.array_equal(C, C_ref)
+    assert np.array_equal(v, v_ref)
+    if cmax == 12:
+        assert (C_ref.max(axis=1) <= cmax // 2).any()   # the halving happened in some sequence
