@@ -46,6 +46,7 @@ size_t select_ws_bytes(int B, int H, int n, int max_out);
 constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
 constexpr int kSpecMaxSlices = 16;    // slices per row of the fused speculation
 constexpr int64_t kBitsTouchMin = 262144;  // selected slots per call from which sliced rows use bitmaps
+constexpr int kSliceSlackMin = 2048;       // max_out from which slices get spare candidate slots
 struct SpecPlan {
     RehearsePlan rp;                  // the projection kernel (sliced rows, batches beyond 8 rows)
     int slices, slice_rows, cand_cap;

@@ -578,6 +578,29 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
     return true;
 }
 
+// A superset of the top kk of ks[0..n) of at most `cap` keys: every key >= L, for L the sample's
+// r-th largest key (r as in sampled_kth), when at least kk and at most cap keys are >= L (the top kk
+// are then among them).  Returns false (histograms cleared again) when that count is out of range.
+template <int NT = kSelThreads, class KS>
+__device__ bool sampled_superset(KS lk, int n, int kk, int cap, FastSel& fs, SelScratch& sh, uint32_t* L_out) {
+    const int tid = threadIdx.x;
+    if (n < 8 * NT || cap < kk) return false;
+    const double expect = static_cast<double>(kk) * NT / n;
+    const int r_lo = static_cast<int>(expect + 2.5 * sqrt(expect) + 4.0);
+    if (r_lo >= NT) return false;
+    uint32_t* sample = fs.words + kSampleBase;
+    sample[tid] = lk.at(static_cast<int>(static_cast<int64_t>(tid) * n / NT));
+    __syncthreads();
+    uint32_t L;
+    int ne, et;
+    radix_kth_lds<NT>(sample, NT, r_lo, fs, &L, &ne, &et);
+    const int c = count_ge<NT>(lk, n, L, sh);
+    fast_sel_init(fs);  // (the compaction that follows needs no histograms; a fallback needs clean ones)
+    __syncthreads();
+    *L_out = L;
+    return c >= kk && c <= cap;  // uniform: c is a block sum
+}
+
 template <int NT = kSelThreads>
 __device__ bool sampled_kth_lds(const uint32_t* lk, int n, int kk, FastSel& fs, SelScratch& sh, uint32_t* T_out,
                                 int* need_eq_out, int* eq_total_out) {

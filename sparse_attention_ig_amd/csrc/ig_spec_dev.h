@@ -161,7 +161,8 @@ struct IdentityIdx {
 // results.  `rows`: the row count the limit refers to (the slice's length in a slice workgroup, n
 // otherwise); gidx(j): the row index of key j; lds: at least 1024 words of LDS scratch (may be the
 // keys' own storage).  TO_CANDS: write the selected keys and row indices as this slice's candidates
-// (the slice's unused candidate slots get key 0, below every score key); otherwise write idx / count
+// (a superset of the slice's selection, at most cand_cap keys; the slice's unused candidate slots get
+// key 0, below every score key); otherwise write idx / count
 // and update the counters (one integer atomic per selected slot, all in flight together; the last
 // workgroup of sequence b halves if any slot saturated and picks the victim).
 template <bool TO_CANDS, class KS, typename GIdx>
@@ -186,6 +187,11 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
         }
     } else {
         kk = min(p.k, limit);
+    }
+    // a slice only has to hand on a superset of its own selection (its candidate slots hold more than
+    // max_out keys): every key at or above a sampled lower bound of its cut, when they fit
+    if constexpr (TO_CANDS) {
+        if (!done && p.cand_cap > kk + kk / 8 && sampled_superset(keys, m, kk, p.cand_cap, fs, sh, &kth)) done = true;
     }
     if (!done && !sampled_kth(keys, m, kk, fs, sh, &kth, &need_eq, &eq_total))
         radix_kth_keys(keys, m, kk, fs, &kth, &need_eq, &eq_total);

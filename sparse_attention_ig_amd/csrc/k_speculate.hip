@@ -38,9 +38,16 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     S = std::min(S, std::max(1, n / 2048));
     S = std::max(S, s_min);
     int slice_rows = 0, cap = 0;
+    // candidate slots per slice: for large selections max_out and half again, so that a slice can hand
+    // on every key above a sampled bound of its cut instead of finding the exact cut (small selections
+    // find the exact cut cheaply, and more slots would only grow the merge)
+    const int slack = max_out >= kSliceSlackMin
+                          ? static_cast<int>(std::min<int64_t>(static_cast<int64_t>(max_out) + max_out / 2 + 64,
+                                                               INT32_MAX))
+                          : max_out;
     for (;;) {
         slice_rows = (n + S - 1) / S;
-        cap = std::min(slice_rows, max_out);
+        cap = std::min(slice_rows, slack);
         if (S == 1 || static_cast<int64_t>(S) * cap <= kSpecMaxRows || S == s_min) break;
         --S;
     }
