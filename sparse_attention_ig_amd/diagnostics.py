@@ -102,10 +102,13 @@ class ExactTopk:
         return self.idx, self.count, self.logits
 
 
-def speculation_fidelity(hosts: Sequence, xs: np.ndarray, max_out: int, *, new_rows=None) -> Dict:
+def speculation_fidelity(hosts: Sequence, xs: np.ndarray, max_out: int, *, new_rows=None,
+                         same_input: bool = False) -> Dict:
     """Runs the decode pipeline over xs [steps][layers][B][D] and measures every layer l >= 1 at every
     step, before the step's new token is appended.  ``new_rows[t][l]`` = (k, v) rows to append
-    (default: the generator's draws)."""
+    (default: the generator's draws).  ``same_input``: the speculation for layer l uses layer l's own
+    input x_l(t) instead of x_{l-1}(t), which isolates the error of the partial channels from that of
+    the cross-layer input."""
     import torch
     from .pipeline import DecodePipeline
     from .runtime import to_device, to_host
@@ -119,7 +122,7 @@ def speculation_fidelity(hosts: Sequence, xs: np.ndarray, max_out: int, *, new_r
     for t in range(steps):
         n, c = pipe.n, pipe.topk()
         xd = [to_device(xs[t, l]) for l in range(nl)]
-        pipe.step(xd, append=False)
+        pipe.step(xd[1:] + xd[-1:] if same_input else xd, append=False)
         for l in range(1, nl):
             lay = pipe.layers[l]
             ti, tc, tl = exact[l](xd[l], lay.K, n, c)
@@ -146,6 +149,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--n", type=int, default=4096)
+    ap.add_argument("--r", type=int, default=32, help="partial channels per head (8, 16, 32, 64 or 128)")
+    ap.add_argument("--same-input", action="store_true",
+                    help="speculate each layer from its own input instead of the previous layer's")
     args = ap.parse_args()
     import torch
     if not torch.cuda.is_available():
@@ -153,16 +159,19 @@ def main() -> int:
         return 1
     L.load()
     from .runtime import prepare_layer
-    spec = gen.llama2_13b(n=args.n, B=args.batch, n_cap=args.n + max(256, args.steps))
+    base = gen.llama2_13b(n=args.n, B=args.batch, n_cap=args.n + max(256, args.steps))
+    spec = gen.Spec(**{**base.__dict__, "r": args.r})
     xs = gen.pipeline_x(spec, args.layers, args.steps)
     hosts = []
     for l in range(args.layers):
         print(f"[fidelity] preparing layer {l}", file=sys.stderr, flush=True)
         hosts.append(prepare_layer(spec, l, lay=gen.draw_layer(spec, l, x_bits=xs[0, l], with_wk=False)))
-    res = speculation_fidelity(hosts, xs, int(math.ceil(0.05 * spec.cap)))
+    res = speculation_fidelity(hosts, xs, int(math.ceil(0.05 * spec.cap)), same_input=args.same_input)
     res.pop("raw")
     r4 = lambda v: round(v, 4)
+    src = "x_l (same layer)" if args.same_input else "x_{l-1} (previous layer)"
     out = {"workload": f"llama2-13b-shaped pipeline B{spec.B} H{spec.H} d{spec.d} r{spec.r} n{spec.n} top-5%",
+           "speculation_input": src,
            "layers": args.layers, "steps": args.steps,
            **{k: r4(v) for k, v in res.items() if k != "per_layer"},
            "per_layer": {l: {k: r4(v) for k, v in d.items()} for l, d in res["per_layer"].items()}}
