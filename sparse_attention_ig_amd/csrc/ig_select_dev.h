@@ -1,9 +1,10 @@
 // Block-level selection primitives (InfiniGen, arXiv 2406.19707, paper-graph-ui
-// summary, section 3.4 "Decoding Stage" steps 3-5): block reductions and scans
-// for 1024-thread workgroups, an exact MSB-first radix select of the k-th
-// largest order-preserving key, and the ordered compaction that writes the
-// selected indices ascending.  Used by the standalone selection kernel and by
-// the fused speculation kernel.
+// summary, section 3.4 "Decoding Stage" steps 3-5): block reductions for
+// 1024-thread workgroups, an exact MSB-first radix select of the k-th largest
+// order-preserving key (and a sampled bracket that narrows it), and the
+// ordered compaction that writes the selected indices ascending.  The keys
+// come from LDS or from global memory (a key source).  Used by the standalone
+// selection kernel and by the fused speculation kernel.
 #pragma once
 
 #include <climits>
@@ -16,7 +17,7 @@ namespace ig {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kSelLdsKeys = 32768;  // rows per (b, h) held in LDS (up to 128 KB of dynamic LDS)
-constexpr int kSelPerThread = 8;    // consecutive rows per thread in the compaction
+constexpr int kSelPerThread = 8;    // consecutive rows per thread in the compaction of rows in HBM
 
 // mode values beyond the public ones: count-only pass of the head average
 constexpr int kSelCountOnly = 100;
@@ -108,6 +109,9 @@ __device__ __forceinline__ void for_each_key(const float* __restrict__ srow, con
     }
 }
 
+// ------------------------------------------------------------------ rows streamed from HBM
+// (the standalone selection of rows longer than the LDS key store: each pass streams the scores with
+// coalesced loads, several in flight per lane)
 // Radix select: the kk-th largest key (1 <= kk <= n) and how many keys equal
 // to it belong to the top kk.
 template <bool IN_LDS>
@@ -230,11 +234,8 @@ __device__ int ordered_compact(const float* __restrict__ srow, const uint32_t* l
     return written;
 }
 
-}  // namespace ig
 
-namespace ig {
-
-// ------------------------------------------------------------------ rows held in LDS
+// ------------------------------------------------------------------ radix select and compaction
 // One 256-bin histogram per radix pass, three of them in rotation: pass p adds into buffer p % 3 and,
 // after its barrier, clears buffer (p + 2) % 3 (last read in pass p - 1), so a pass needs a single
 // barrier and every wave derives the digit on its own.  The histogram words are free after the
@@ -247,6 +248,7 @@ constexpr int kMaxCand = kFastStage - kCandBase;
 struct __align__(16) FastSel {  // 16-byte aligned: the histograms are read 4 bins at a time
     uint32_t words[kFastStage];  // hist[3][256], samples and candidates during the select, then staging
     int wtot[kSelWaves];
+    int wtot2[kSelWaves];
     __device__ uint32_t* hist(int i) { return words + 256 * i; }
     __device__ uint32_t* stage() { return words; }
 };
@@ -273,12 +275,14 @@ __device__ __forceinline__ void load_keys(const uint32_t* lk, int j, int end, ui
 // Key sources of the selection primitives: keys held in LDS (16-byte aligned), or a row of keys in
 // global memory (any alignment, scalar loads).
 struct LdsKeys {
+    static constexpr int kE = 4;  // keys per lane per step on long rows (one 16-byte LDS read)
     const uint32_t* p;
     __device__ __forceinline__ uint32_t at(int j) const { return p[j]; }
     template <int E>
     __device__ __forceinline__ void load(int j, int end, uint32_t (&k)[E]) const { load_keys<E>(p, j, end, k); }
 };
 struct GlobalKeys {
+    static constexpr int kE = 8;  // keys per lane per step on long rows (loads in flight together)
     const uint32_t* __restrict__ p;
     __device__ __forceinline__ uint32_t at(int j) const { return p[j]; }
     template <int E>
@@ -287,10 +291,6 @@ struct GlobalKeys {
         for (int e = 0; e < E; ++e) k[e] = j + e < end ? p[j + e] : 0u;
     }
 };
-
-// Keys per lane per step: 4 (one 16-byte LDS read) once every thread has at least 4 keys, else 1.
-template <int NT>
-__device__ __forceinline__ bool wide_rows(int n) { return n >= 4 * NT; }
 
 // One radix pass: hist[digit] counts of the keys whose bits above `shift + 8` equal `prefix`.
 template <int NT, int E, class KS>
@@ -335,13 +335,14 @@ template <int NT = kSelThreads, class KS>
 __device__ __forceinline__ void radix_kth_keys(KS lk, int n, int kk, FastSel& fs, uint32_t* T_out, int* need_eq_out,
                                                int* eq_total_out) {
     const int tid = threadIdx.x, lane = tid % kWave;
-    const bool wide = wide_rows<NT>(n);
+    constexpr int E = KS::kE;
+    const bool wide = n >= E * NT;
     uint32_t prefix = 0, pmask = 0;
     int rem = kk, dcount = 0;
     for (int pass = 0, shift = 24; shift >= 0; ++pass, shift -= 8) {
         uint32_t* h = fs.hist(pass % 3);
         if (wide)
-            radix_hist<NT, 4>(lk, n, h, shift, prefix, pmask, pass == 0);
+            radix_hist<NT, E>(lk, n, h, shift, prefix, pmask, pass == 0);
         else
             radix_hist<NT, 1>(lk, n, h, shift, prefix, pmask, pass == 0);
         __syncthreads();
@@ -385,13 +386,14 @@ __device__ __forceinline__ void radix_kth_lds(const uint32_t* lk, int n, int kk,
 // Keys >= kc among lk[0..n), summed over the first NT threads (ends after barriers).
 template <int NT = kSelThreads, class KS>
 __device__ __forceinline__ int count_ge(KS lk, int n, uint32_t kc, SelScratch& sh) {
+    constexpr int E = KS::kE;
     int c = 0;
-    if (wide_rows<NT>(n)) {
-        for (int j0 = 4 * static_cast<int>(threadIdx.x); j0 < n; j0 += 4 * NT) {
-            uint32_t k[4];
-            lk.template load<4>(j0, n, k);
+    if (n >= E * NT) {
+        for (int j0 = E * static_cast<int>(threadIdx.x); j0 < n; j0 += E * NT) {
+            uint32_t k[E];
+            lk.template load<E>(j0, n, k);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) c += (j0 + e < n && k[e] >= kc) ? 1 : 0;
+            for (int e = 0; e < E; ++e) c += (j0 + e < n && k[e] >= kc) ? 1 : 0;
         }
     } else {
         for (int j = threadIdx.x; j < n; j += NT) c += lk.at(j) >= kc ? 1 : 0;
@@ -428,17 +430,20 @@ __device__ int compact_e(KS lk, int n, uint32_t T, int need_eq, int eq_total, in
             c_eq += (j0 + e < hi && k[e] == T) ? 1 : 0;
         }
     }
-    // per-wave counts packed as gt | eq << 16 (each <= n <= 32768), prefix-summed over the waves
-    const int packed = wave_sum_i32(c_gt | (c_eq << 16));
-    if (lane == 0) fs.wtot[wave] = packed;
+    // per-wave counts, prefix-summed over the waves
+    const int w_gt = wave_sum_i32(c_gt), w_eq = wave_sum_i32(c_eq);
+    if (lane == 0) {
+        fs.wtot[wave] = w_gt;
+        fs.wtot2[wave] = w_eq;
+    }
     __syncthreads();
-    const int incl = wave_incl_scan(lane < NW ? fs.wtot[lane] : 0);
-    const int before = wave > 0 ? read_lane(incl, wave - 1) : 0;
-    const int total = read_lane(incl, NW - 1);
-    int eq_before = before >> 16;
-    const int gt_tot = total & 0xFFFF, eq_tot = total >> 16;
+    const int incl_gt = wave_incl_scan(lane < NW ? fs.wtot[lane] : 0);
+    const int incl_eq = wave_incl_scan(lane < NW ? fs.wtot2[lane] : 0);
+    const int gt_before = wave > 0 ? read_lane(incl_gt, wave - 1) : 0;
+    int eq_before = wave > 0 ? read_lane(incl_eq, wave - 1) : 0;
+    const int gt_tot = read_lane(incl_gt, NW - 1), eq_tot = read_lane(incl_eq, NW - 1);
     const int take = all_eq ? eq_tot : min(eq_tot, need_eq);
-    int pos = (before & 0xFFFF) + min(eq_before, take);
+    int pos = gt_before + min(eq_before, take);
     for (int g0 = lo; g0 < hi; g0 += G) {  // whole wave in step: the DPP scans need every lane
         const int j0 = g0 + lane * E;
         uint32_t k[E];
@@ -488,7 +493,7 @@ __device__ int compact_e(KS lk, int n, uint32_t T, int need_eq, int eq_total, in
 template <int NT = kSelThreads, class KS, typename Visit = NoVisit>
 __device__ int compact_keys(KS lk, int n, uint32_t T, int need_eq, int eq_total, int32_t* __restrict__ out,
                             int max_out, FastSel& fs, Visit visit) {
-    if (wide_rows<NT>(n)) return compact_e<NT, 4>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
+    if (n >= KS::kE * NT) return compact_e<NT, KS::kE>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
     return compact_e<NT, 1>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
 }
 
@@ -510,8 +515,9 @@ __device__ int compact_lds(const uint32_t* lk, int n, uint32_t T, int need_eq, i
 // *need_eq keys equal to *T, *eq_total keys being equal to it.  Ends after a barrier.
 template <int NT = kSelThreads, class KS>
 __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, uint32_t* T_out, int* need_eq_out,
-                            int* eq_total_out) {
+                            int* eq_total_out, uint32_t* band = nullptr, int band_cap = kMaxCand) {
     const int tid = threadIdx.x, lane = tid % kWave;
+    constexpr int E = KS::kE;
     if (n < 8 * NT) return false;
     const double expect = static_cast<double>(kk) * NT / n;
     const double margin = 2.5 * sqrt(expect) + 4.0;
@@ -519,7 +525,7 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
     const int r_hi = static_cast<int>(expect - margin);
     if (r_lo >= NT) return false;
     uint32_t* sample = fs.words + kSampleBase;
-    uint32_t* cand = fs.words + kCandBase;
+    uint32_t* cand = band ? band : fs.words + kCandBase;  // (a caller's band store: at least band_cap words)
     sample[tid] = lk.at(static_cast<int>(static_cast<int64_t>(tid) * n / NT));
     __syncthreads();
     uint32_t L, U = 0;
@@ -527,7 +533,7 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
     // (an early exit gives a lower value: L is still a lower bound, and U is checked by the count)
     radix_kth_lds<NT>(sample, NT, r_lo, fs, &L, &ne, &et);
     // the upper bound only when the keys >= L are expected to overflow the candidate space
-    const bool want_hi = r_hi >= 1 && static_cast<double>(r_lo) * n / NT > 0.75 * kMaxCand;
+    const bool want_hi = r_hi >= 1 && static_cast<double>(r_lo) * n / NT > 0.75 * band_cap;
     if (want_hi) {
         __syncthreads();  // every wave has read the last histogram before it is cleared
         fast_sel_init(fs);
@@ -538,11 +544,11 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
     if (tid == 0) fs.wtot[0] = 0;  // band keys placed so far
     __syncthreads();
     int c_hi = 0;
-    for (int j0 = 4 * tid; j0 < n; j0 += 4 * NT) {  // n >= 8 NT: four keys per lane
-        uint32_t k[4];
-        lk.template load<4>(j0, n, k);
+    for (int j0 = E * tid; j0 < n; j0 += E * NT) {  // E keys per lane
+        uint32_t k[E];
+        lk.template load<E>(j0, n, k);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < E; ++e) {
             const bool valid = j0 + e < n;
             const bool hi = valid && has_hi && k[e] >= U;
             const bool in = valid && !hi && k[e] >= L;
@@ -554,14 +560,14 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
                 if (lane == 0) base = atomicAdd(&fs.wtot[0], __popcll(m));
                 base = read_lane(base, 0);
                 const int pos = base + __popcll(m & lanemask_lt());
-                if (in && pos < kMaxCand) cand[pos] = k[e];
+                if (in && pos < band_cap) cand[pos] = k[e];
             }
         }
     }
     __syncthreads();
     const int c_band = fs.wtot[0];
     c_hi = block_sum<NT>(c_hi, sh);
-    if (c_hi >= kk || c_hi + c_band < kk || c_band > kMaxCand) {  // uniform: block-wide counts
+    if (c_hi >= kk || c_hi + c_band < kk || c_band > band_cap) {  // uniform: block-wide counts
         // the sample's passes left counts in the histograms: the full radix starts from clean ones
         fast_sel_init(fs);
         __syncthreads();
