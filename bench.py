@@ -59,10 +59,9 @@ def main() -> int:
     ap.add_argument("--mode", choices=["topk", "threshold"], default="topk")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: ig_speculate + ig_sparse_decode_attn; unfused: the six-call path")
-    ap.add_argument("--schedule", choices=["layer", "serial", "streams"], default="layer",
-                    help="layer (fused path): ig_decode_layer, layer l's attention beside the speculation for "
-                         "layer l+1 in one launch; serial: call after call on one stream; streams: the same "
-                         "overlap from two streams")
+    ap.add_argument("--schedule", choices=["layer", "serial"], default="layer",
+                    help="layer: ig_decode_layer runs layer l's attention beside the speculation for layer l+1 "
+                         "in one launch; serial: call after call on one stream")
     ap.add_argument("--workload", choices=["opt-6.7b", "llama2-7b-long", "llama2-13b-pipeline", "opt-30b-pool",
                                           "opt-30b-pool-int4"],
                     default="opt-6.7b",
@@ -137,37 +136,6 @@ def main() -> int:
     if args.path != "fused" and args.schedule == "layer":
         args.schedule = "serial"   # the fused decode layer needs the fused speculation
 
-    spec_parts = tuple(p for p in PARTS if p != "attn")
-    s_spec, s_attn = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
-    ev_spec = [torch.cuda.Event() for _ in layers]
-    ev_attn = [torch.cuda.Event() for _ in layers]
-
-    def run_overlap():
-        """Decode dependencies across layers: the speculation of layer l reads the attention input of
-        layer l-1, which exists once layer l-2's attention is done; layer l's attention needs its own
-        selection and layer l-1's output.  So the speculation of layer l+1 runs beside layer l's
-        attention, on a second stream."""
-        cur = torch.cuda.current_stream()
-        s_spec.wait_stream(cur)
-        s_attn.wait_stream(cur)
-        L = len(layers)
-
-        def spec(i):
-            if i >= 2:
-                s_spec.wait_event(ev_attn[i - 2])
-            layers[i].step(**step_kw, parts=spec_parts, stream=s_spec)
-            ev_spec[i].record(s_spec)
-
-        spec(0)
-        for i in range(L):
-            if i + 1 < L:
-                spec(i + 1)
-            s_attn.wait_event(ev_spec[i])
-            layers[i].step(**step_kw, parts=("attn",), stream=s_attn)
-            ev_attn[i].record(s_attn)
-        cur.wait_stream(s_spec)
-        cur.wait_stream(s_attn)
-
     def run_layer():
         """One launch per layer after the projection: layer l's attention beside the speculation for
         layer l+1 (ig_decode_layer); the first layer's speculation and the last layer's attention are
@@ -177,8 +145,6 @@ def main() -> int:
             decode_layer(layers[i], layers[i + 1] if i + 1 < len(layers) else None, step_kw)
 
     def run(parts=PARTS):
-        if parts == PARTS and args.schedule == "streams":
-            return run_overlap()
         if parts == PARTS and args.schedule == "layer":
             return run_layer()
         # stream=None: torch's current stream, which is the capture stream inside a graph capture
