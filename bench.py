@@ -505,10 +505,10 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-# the kernels a call may launch (rocprofv3 kernel names start with these; the projection kernel and the
-# merge run only for sliced rows, the combine only for a split attention)
-CALL_KERNELS = {"ig_decode_layer": ("void ig::k_rehearse_proj<", "void ig::k_decode_layer<", "ig::k_attn_combine"),
-                "ig_speculate": ("void ig::k_rehearse_proj<", "void ig::k_speculate<", "ig::k_spec_merge"),
+# the kernels a call may launch (rocprofv3 kernel names start with these; the merge runs only for sliced
+# rows, the combine only for a split attention)
+CALL_KERNELS = {"ig_decode_layer": ("void ig::k_decode_layer<", "ig::k_attn_combine"),
+                "ig_speculate": ("void ig::k_speculate<", "ig::k_spec_merge"),
                 "ig_rehearse": ("void ig::k_rehearse_proj<", "void ig::k_rehearse_score<")}
 
 

@@ -55,7 +55,9 @@ const char* ig_last_error(void);
 /* ABI version: bumped on any signature or layout change (2: ig_pool_touch takes a
  * workspace; 3: Wq_part is stored one row per partial column, [H*r][D];
  * 4: ig_decode_layer; 5: ig_partial_weight_index_dev; 6: the speculation
- * workspace starts with its arrival words; 7: the INT4 pool calls). */
+ * workspace starts with its arrival words; 7: the INT4 pool calls; 8: the
+ * speculation's partial query comes from projection workgroups of the same
+ * launch, whose arrival words follow the sequences' in the workspace). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -179,17 +181,16 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * among their candidates; IG_EUNSUPPORTED when n > 16 x 32768.
  * q_part [B][H][r] and scores [B][H][ld] are written only when not NULL.
  * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
- * receives the victim.  One launch of one workgroup per (b, h), which projects
- * its own partial query and then scores, selects and updates the counters
- * (with B > 8, the partial-query projection kernel first; with slices, the
- * projection, the slices, then the merges).
- * D * element size must not exceed 131072 bytes.  The workspace
- * (IG_OP_SPECULATE bytes, required) starts with one uint32 arrival word per
- * sequence ([B] at offset 0), followed by the projection's partial sums (when
- * the projection kernel runs) and the slices' candidates (when there are
- * slices); it must have been zero-filled once with
- * ig_workspace_init, and every call returns the arrival words to zero.  Calls
- * sharing a workspace must not overlap.  H <= 65535.
+ * receives the victim.  One launch: projection workgroups (each one block of
+ * partial columns over one split of 512 inputs of D, for every batch row) and
+ * one workgroup per (b, h) (or per slice), which adds its head's split
+ * partial sums in split order, then scores, selects and updates the counters;
+ * with slices, a merge launch follows.  The workspace (IG_OP_SPECULATE bytes,
+ * required) starts with one uint32 arrival word per sequence ([B] at offset
+ * 0), then the projection's arrival words and split partial sums, then the
+ * slices' candidates (when there are slices); it must have been zero-filled
+ * once with ig_workspace_init, and every call returns the arrival words to
+ * zero.  Calls sharing a workspace must not overlap.  H <= 65535.
  */
 int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
                  int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
@@ -206,17 +207,16 @@ int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const
  * layer l over the rows selected for it, and the speculation for layer l+1.
  * `attn` holds the arguments of ig_sparse_decode_attn for layer l, `spec` those
  * of ig_speculate for layer l+1 (B, H, dtype shared; d is the attention's head
- * dim); either may be NULL (then this is that one call).  With both: (beyond
- * 8 batch rows, the projection kernel of ig_speculate, then) one launch in
- * which the speculation's (b, h) workgroups and the attention's run side by
- * side (no ordering between the two halves, so spec->idx, count, counters,
+ * dim); either may be NULL (then this is that one call).  With both: one
+ * launch in which the speculation's projection and (b, h) workgroups and the
+ * attention's run side by side (no ordering between the two halves, so
+ * spec->idx, count, counters,
  * victim, q_part, scores must not
  * alias anything attn reads), then the split combine of the attention if it
  * splits.  Results: those of the two calls (the attention's float sums may
  * associate differently).  Falls back to the two calls in sequence for shapes
  * outside the fused set (spec r / (16 / element size) in {2, 4, 8}, attn d /
- * (16 / element size) in {8, 16, 32}, spec n <= 16384 without slices, spec
- * D * element size <= 65536 bytes).
+ * (16 / element size) in {8, 16, 32}, spec n <= 16384 without slices).
  */
 typedef struct {
     const void* q;

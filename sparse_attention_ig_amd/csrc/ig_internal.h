@@ -48,16 +48,15 @@ constexpr int kSpecMaxSlices = 16;    // slices per row of the fused speculation
 constexpr int64_t kBitsTouchMin = 262144;  // selected slots per call from which sliced rows use bitmaps
 constexpr int kSliceSlackMin = 2048;       // max_out from which slices get spare candidate slots
 struct SpecPlan {
-    RehearsePlan rp;                  // the projection kernel (sliced rows, batches beyond 8 rows)
     int slices, slice_rows, cand_cap;
-    bool proj_kernel;                 // the partial query comes from the projection kernel's partial sums
+    int proj_blocks, splits, proj_wgs;  // projection workgroups: column blocks x splits of the D inputs
     bool bits;                        // the merge leaves bitmaps and a counter kernel applies them
     bool ok;                          // false: rows too long for the candidates to fit one merge
-    size_t off_arrive, off_part, off_cnt, off_key, off_idx, off_bits, off_flags, ws_bytes;
+    size_t off_arrive, off_pdone, off_part, off_cnt, off_key, off_idx, off_bits, off_flags, ws_bytes;
 };
 SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);
-size_t speculate_lds_bytes(int n, int x_bytes);
+size_t speculate_lds_bytes(int n);
 
 // kernel launchers (return hipError_t as int)
 int launch_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,

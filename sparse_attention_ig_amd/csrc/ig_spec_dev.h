@@ -3,15 +3,19 @@
 // "KV Cache Pool Management Under Memory Pressure"): partial query, speculated
 // scores, threshold or top-k selection, and the access-counter update.
 //
-// One 1024-thread workgroup per (b, h); scores never leave the chip.
-//  1. The workgroup projects its own partial query: x[b] staged in LDS, the
-//     head's r rows of the partial weight read along D by groups of lanes
-//     (the batch rows of a head share those rows through the L2 cache).  Sliced
-//     rows and batches beyond 8 rows instead add the split partials of one
-//     projection kernel (k_rehearse_proj, shared with ig_rehearse).
+// A speculation launch has two kinds of workgroups:
+//  0. Projection workgroups (the lowest workgroup indices of the launch, never
+//     waiting on anything): each multiplies the attention input x by one block
+//     of columns of the partial weight over one split of 512 inputs of D for
+//     every batch row, reading its weight rows once from HBM, and stores the
+//     split partial sums [splits][B][H*r].
+//  1. One 1024-thread row workgroup per (b, h) (or per slice of a row): it
+//     issues its first partial-key loads, polls its head's split partials
+//     until all are stored, adds them in a fixed order (its partial query),
+//     then:
 //  2. Scores of every cached row go to LDS as order-preserving keys (and to
 //     HBM only if the caller asks for them), streaming the partial-key rows in
-//     double-buffered batches of 8 rows x 16 bytes per lane.
+//     double-buffered batches of 16 bytes per lane.
 //  3. Selection runs on the LDS keys with the same rules as ig_select; the
 //     compaction leaves the selected indices in LDS.
 //  4. Every selected slot's counter gets an integer atomic increment, all
@@ -19,9 +23,13 @@
 //     word per sequence in the workspace) applies the halving and picks the
 //     victim, then returns the word to zero.
 //
+// The waits are safe without co-residency guarantees: a row workgroup only
+// waits on workgroups with lower indices, which the hardware dispatches first
+// and which run to completion unconditionally; every wait is also bounded.
+//
 // The workgroup index `wg` of the row is passed in (the fused decode kernel
 // runs rows after other roles' workgroups); the caller provides the LDS:
-// `keys` holds max(n, 1024, D * element size / 4) words, `sm` the fixed scratch.
+// `keys` holds max(n, kProjStageWords) words, `sm` the fixed scratch.
 #pragma once
 
 #include <climits>
@@ -40,8 +48,8 @@ struct SpecParams {
     const void* x;       // [B][D] attention input
     const void* W;       // [H*r][D] partial query weight (one row per partial column)
     int D;
-    const float* part;   // NULL: each workgroup projects its partial query from x and W; else the
-    int splits;          //   projection kernel's partial sums [splits][B][H*r], added in fixed order
+    float* part;         // split partial sums [splits][B][H*r] of the launch's projection workgroups
+    int splits;          //   (splits of kProjSplit inputs), added by each row in split order
     const float* bias;
     const void* Kp;
     int B, H, r, n, n_cap, ld;
@@ -68,12 +76,14 @@ struct SpecParams {
     // large merges: the merge leaves each row's selection as a bitmap [B*H][ceil(n / 32)] and a counter
     // kernel adds the heads' bits per slot (no atomics per selected slot); NULL: atomics in the merge
     uint32_t* bits;
+    // projection workgroups: the first proj_wgs workgroups of the launch (proj_blocks column blocks x
+    // splits); row_wgs: the row workgroups; pdone [B*H]: slices of a row done reading its partial sums
+    int proj_wgs, proj_blocks, row_wgs;
+    uint32_t* pdone;
 };
 
-// Fills the row kernel's parameters of a speculation call; with sliced rows (every slice of a row
-// would otherwise project the same query) or more than 8 batch rows, first launches the partial-query
-// projection kernel.
-int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s);
+// Fills the launch parameters of a speculation call (projection and row workgroups).
+int begin_speculate(const SpecCall& c, SpecParams* p);
 
 template <int R>
 struct SpecShared {
@@ -83,55 +93,146 @@ struct SpecShared {
     int last;
 };
 
-// Partial query of one (b, h) inside its workgroup (summary section 3.4 "Decoding Stage" step 1):
-// q[c] = x . W[c] (+ bias[c]) for c < R, W the head's R rows of D inputs.  x is staged in LDS (xs, D
-// elements); row c is read by a group of G = min(64, NT / R) lanes, 16 bytes per lane per step along D
-// with U steps in flight, and the group's partial sums are added by DPP in a fixed order.  Ends with a
-// barrier; q (and q_out, when not NULL) then hold the sums.
-template <typename T, int NT, int R, int U>
-__device__ __forceinline__ void project_partial(const T* __restrict__ x, const T* __restrict__ W, int D,
-                                                const float* __restrict__ bias, int rot, uint4* xs, float* q,
-                                                float* q_out) {
+// Projection workgroups (summary section 3.4 "Decoding Stage" step 1, the partial query
+// x . W~_Q^partial).  Workgroup pw takes column block pw % proj_blocks (proj_cols<T>() partial
+// columns, one lane group each) and split pw / proj_blocks of the inputs (kProjSplit of them, two
+// 16-byte vectors of weight per lane); the attention-input rows of the split are staged in LDS a few
+// batch rows at a time, each lane group's sum is added by DPP in a fixed order, and the sums of the
+// workgroup leave through LDS as whole rows of columns.
+//
+// Hand-over without flags: a partial-sum slot holds 0 (all bits clear) while it is empty.  A
+// producer never writes those bits (a sum of +0.0 is stored as -0.0, which adds the same in the
+// readers' sums, all started from +0.0), so a reader polls its slots until none is 0, then returns
+// them to 0 for the next call (the last reader of a sliced row does, counted per row).  Slots and
+// counts travel through device-coherent stores and loads (agent scope: written through to the
+// level all XCDs share, read from there); no fence is needed (on this chip an agent-scope fence
+// writes back the XCD's whole L2).  The workspace starts zero-filled.
+constexpr int kProjSplit = 512;        // inputs per split partial
+constexpr int kProjStageWords = 2048;  // LDS words of staged attention-input rows (also the least `keys` size)
+constexpr uint32_t kProjSpinLimit = 1u << 22;  // polls before a row workgroup stops waiting
+template <typename T>
+__host__ __device__ constexpr int proj_lanes() { return kProjSplit / (2 * Vec<T>::N); }
+template <typename T>
+__host__ __device__ constexpr int proj_cols() { return kSpecThreads / proj_lanes<T>(); }
+
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ void proj_role(const SpecParams& p, int pw, uint32_t* lds) {
     constexpr int VEC = Vec<T>::N;
-    constexpr int G = NT / R < 64 ? NT / R : 64;
-    static_assert(G >= 1, "at most one partial channel per thread");
-    const int tid = threadIdx.x;
-    const int nv = D / VEC;  // D is a multiple of VEC and both operands are 16-byte aligned
-    const uint4* xv = reinterpret_cast<const uint4*>(x);
-    for (int i = tid; i < nv; i += NT) xs[i] = xv[i];
-    __syncthreads();
-    // lane group tid / G takes row (tid / G + rot) mod R: workgroups that read the same rows at once
-    // (the batch rows of a head) start on different rows; a row's sum order does not depend on rot
-    const bool on = tid / G < R;
-    const int c = (tid / G + rot) % R, g = tid % G;
-    float acc = 0.f;
-    if (on) {
-        const uint4* wv = reinterpret_cast<const uint4*>(W + static_cast<size_t>(c) * D);
-        for (int i0 = g; i0 < nv; i0 += G * U) {
-            uint4 w[U];
+    constexpr int LG = proj_lanes<T>();   // lanes per column
+    constexpr int CPW = proj_cols<T>();   // columns per workgroup
+    constexpr int XV = kProjSplit / VEC;  // 16-byte vectors per staged row
+    constexpr int BB = kProjStageWords * 4 / (kProjSplit * static_cast<int>(sizeof(T)));  // rows per round
+    static_assert(BB >= 1 && CPW * LG == kSpecThreads && BB * CPW <= kSpecThreads, "projection tiling");
+    const int tid = threadIdx.x, cl = tid / LG, g = tid % LG;
+    const int N = p.H * p.r, D = p.D, B = p.B;
+    const int blk = pw % p.proj_blocks, s = pw / p.proj_blocks;
+    const int col = blk * CPW + cl;
+    const int e0 = s * kProjSplit;
+    const T* __restrict__ x = static_cast<const T*>(p.x);
+    const T* __restrict__ W = static_cast<const T*>(p.W);
+    uint4 w[2];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * G;
-                w[u] = i < nv ? wv[i] : make_uint4(0, 0, 0, 0);
-            }
+    for (int k = 0; k < 2; ++k) {
+        const int e = e0 + (k * LG + g) * VEC;  // D is a multiple of VEC: whole vectors
+        w[k] = (col < N && e < D) ? load_raw16(W + static_cast<size_t>(col) * D + e) : make_uint4(0, 0, 0, 0);
+    }
+    uint4* xs = reinterpret_cast<uint4*>(lds);
+    float* sums = reinterpret_cast<float*>(lds + kProjStageWords);  // [BB][CPW]
+    float* out = p.part + static_cast<size_t>(s) * B * N;
+    for (int b0 = 0; b0 < B; b0 += BB) {
+        const int nb = min(BB, B - b0);
+        for (int i = tid; i < nb * XV; i += kSpecThreads) {
+            const int e = e0 + (i % XV) * VEC;
+            xs[i] = e < D ? load_raw16(x + static_cast<size_t>(b0 + i / XV) * D + e) : make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
+        // all staged rows at once: BB independent sums per lane, reduced together
+        float a0[VEC], a1[VEC], acc[BB];
+        unpack_raw(w[0], a0);
+        unpack_raw(w[1], a1);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * G;
-                if (i < nv) {
-                    float a[VEC], xe[VEC];
-                    unpack_raw(w[u], a);
-                    unpack_raw(xs[i], xe);
+        for (int bi = 0; bi < BB; ++bi) {
+            acc[bi] = 0.f;
+            if (bi < nb) {
+                float xe[VEC];
+                unpack_raw(xs[bi * XV + g], xe);
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) acc = fmaf(xe[v], a[v], acc);
-                }
+                for (int v = 0; v < VEC; ++v) acc[bi] = fmaf(xe[v], a0[v], acc[bi]);
+                unpack_raw(xs[bi * XV + LG + g], xe);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[bi] = fmaf(xe[v], a1[v], acc[bi]);
             }
         }
+#pragma unroll
+        for (int bi = 0; bi < BB; ++bi) acc[bi] = group_sum<LG>(acc[bi]);
+        if (g == 0) {
+#pragma unroll
+            for (int bi = 0; bi < BB; ++bi)
+                if (bi < nb) sums[bi * CPW + cl] = __float_as_uint(acc[bi]) == 0u ? -0.f : acc[bi];  // never empty bits
+        }
+        __syncthreads();
+        if (tid < nb * CPW) {
+            const int bi = tid / CPW, c = blk * CPW + tid % CPW;
+            if (c < N) coherent_store(out + static_cast<size_t>(b0 + bi) * N + c, sums[tid]);
+        }
+        // (the next round's staging and sums are written only after its first barrier)
     }
-    acc = group_sum<G>(acc);  // whole groups: threads past R * G hold zeros in groups of their own
-    if (on && g == 0) {
-        const float v = bias ? acc + bias[c] : acc;
+}
+
+// Row workgroup: the partial query q[c] (c < R) of row b, columns [col0, col0 + R): poll the split
+// partials until every slot is filled, add them in a fixed order (thread (c, i) adds splits i, i + P,
+// .. in turn, then the P threads of column c are added by DPP; bias last), and return the slots to
+// empty.  Writes q (and q_out when not NULL); ends with a barrier.
+template <int R>
+__device__ __forceinline__ void wait_partial_query(const SpecParams& p, int b, int bh, int col0, float* q,
+                                                   float* q_out) {
+    constexpr int P = kSpecThreads / R < 64 ? kSpecThreads / R : 64;  // threads per column
+    const int tid = threadIdx.x;
+    const bool on = tid < R * P;
+    const int c = tid / P, i = tid % P;
+    const int N = p.H * p.r;
+    const bool sole = p.slices == 1;  // the only reader of these slots
+    float acc = 0.f;
+    for (int s0 = 0; s0 < p.splits; s0 += P) {
+        const int s = s0 + i;
+        const bool mine = on && s < p.splits;
+        float* src = p.part + (static_cast<size_t>(s) * p.B + b) * N + col0 + c;
+        float v = 0.f;
+        uint32_t polls = 0;
+        for (;;) {
+            if (mine) v = coherent_load(src);
+            if (!__syncthreads_or(mine && __float_as_uint(v) == 0u) || ++polls >= kProjSpinLimit) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (mine) {
+            acc += v;
+            if (sole) coherent_store(src, 0.f);
+        }
+    }
+    acc = group_sum<P>(acc);
+    if (on && i == 0) {
+        const float v = p.bias ? acc + p.bias[col0 + c] : acc;
         q[c] = v;
         if (q_out) q_out[c] = v;
+    }
+    if (!sole) {
+        // slices of one row read the same slots: the last one to finish reading empties them
+        int last = 0;
+        if (tid == 0)
+            last = __hip_atomic_fetch_add(&p.pdone[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   static_cast<uint32_t>(p.slices - 1);
+        if (__syncthreads_or(last)) {
+            for (int k = tid; k < p.splits * R; k += kSpecThreads)
+                coherent_store(p.part + (static_cast<size_t>(k / R) * p.B + b) * N + col0 + k % R, 0.f);
+            if (tid == 0) __hip_atomic_store(&p.pdone[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
 }
@@ -313,12 +414,11 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
     }
 }
 
-// Workgroup wg of the speculation launch: one (b, h) row, or (slices > 1) one slice of one row
-// (wg = slice * B*H + row).  The partial query projected in the workgroup, the slice's scores as LDS
-// keys from its partial-key rows, then the selection.
-// PU: partial-weight loads per lane in flight during the projection; PRE: the first partial-key batch
-// is issued before the projection (it then holds registers through it).
-template <typename T, int LPR, int BATCH = kSpecBatch, int PU = BATCH, bool PRE = true>
+// Row workgroup wg of the speculation launch (counted from the first row workgroup): one (b, h) row,
+// or (slices > 1) one slice of one row (wg = slice * B*H + row).  The first partial-key batch is
+// issued, the partial query is read from the projection workgroups' partial sums, the slice's scores
+// go to LDS keys from its partial-key rows, then the selection.
+template <typename T, int LPR, int BATCH = kSpecBatch, bool PRE = true>
 __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* keys, SpecShared<LPR * Vec<T>::N>& sm) {
     constexpr int VEC = Vec<T>::N;
     constexpr int R = LPR * VEC;               // partial channels per head
@@ -338,7 +438,7 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
     const int n = p.slices > 1 ? min(p.n - r0, p.slice_rows) : p.n;  // this workgroup's rows
     const T* kp = static_cast<const T*>(p.Kp) + (static_cast<size_t>(bh) * p.n_cap + r0) * R + li * VEC;
 
-    fast_sel_init(fs);  // the barriers of the partial-query sum publish the cleared histograms
+    fast_sel_init(fs);  // the barriers of the partial-query wait publish the cleared histograms
 
     // 1. the partial query of this (b, h), with the first partial-key batch in flight (PRE) or after
     uint4 cur[BATCH], nxt[BATCH];
@@ -350,14 +450,7 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
         }
     }
     float* q_out = (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr;
-    if (p.part)
-        sum_partials<kSpecThreads>(p.part, p.splits, p.B, p.H * R, b, h * R, R, p.bias, s_q,
-                                   reinterpret_cast<float*>(keys), q_out);
-    else
-        project_partial<T, kSpecThreads, R, PU>(static_cast<const T*>(p.x) + static_cast<size_t>(b) * p.D,
-                                                static_cast<const T*>(p.W) + static_cast<size_t>(h) * R * p.D, p.D,
-                                                p.bias ? p.bias + h * R : nullptr, b * R / p.B,
-                                                reinterpret_cast<uint4*>(keys), s_q, q_out);
+    wait_partial_query<R>(p, b, bh, h * R, s_q, q_out);
     if constexpr (!PRE) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {

@@ -5,13 +5,17 @@
 // the attention of layer l over the rows its speculation selected, beside the
 // speculation for layer l+1 (scores, selection and counters).
 //
-// One grid holds both roles: workgroups [0, B*H) run spec_row for layer l+1
-// (its own partial-query projection included), the rest run attention items of layer l (one (b, h, split) each, all
-// 1024 threads of the workgroup on it).  The two roles touch disjoint buffers,
-// so they need no synchronisation; a CU holds one workgroup of each role, and
-// the attention's K/V gathers fill the memory pipeline while the speculation
-// is in its latency-bound selection.  Splits of an attention row are merged by
-// the usual combine kernel afterwards.
+// One grid holds three roles, in this order: the partial-query projection
+// workgroups for layer l+1, one spec_row workgroup per (b, h) for layer l+1,
+// which waits only for the projection workgroups (lower indices, never waiting
+// themselves), then the attention items of layer l (one (b, h, split) each,
+// all 1024 threads of the workgroup on it), which take the slots the
+// projection leaves.  The row workgroups are resident from the start, with
+// their first partial-key loads in flight while the partial sums are made.  The attention and the
+// speculation touch disjoint buffers; a CU holds two workgroups, and the
+// attention's K/V gathers fill the memory pipeline while the speculation is in
+// its latency-bound selection.  Splits of an attention row are merged by the
+// usual combine kernel afterwards.
 #include "ig_attn_dev.h"
 #include "ig_spec_dev.h"
 
@@ -31,20 +35,21 @@ union DecodeShared {
 // buffered) and 2 K/V rows (64 lane groups x 2 = 128 rows per pass).
 constexpr int kDecodeSpecBatch = 4;
 constexpr int kDecodeAttnRows = 2;
-// partial-weight loads per lane in flight in the projection (the partial-key rows are issued after it)
-constexpr int kDecodeProjLoads = 6;
 
 template <typename T, int LPR_S, int LPR_A>
-__global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int n_spec, int bh_attn) {
-    extern __shared__ __align__(16) uint32_t keys[];  // the speculation role's score keys
+__global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int bh_attn) {
+    extern __shared__ __align__(16) uint32_t keys[];  // staged x (projection) or the speculation's score keys
     __shared__ DecodeShared<LPR_S * Vec<T>::N, LPR_A, Vec<T>::N> sm;
     const int wg = blockIdx.x;
-    if (wg < n_spec) {
-        spec_row<T, LPR_S, kDecodeSpecBatch, kDecodeProjLoads, false>(p, wg, keys, sm.spec);
-        return;
+    const int n_spec = p.proj_wgs + p.row_wgs;
+    if (wg < p.proj_wgs) {
+        proj_role<T>(p, wg, keys);
+    } else if (wg < n_spec) {
+        spec_row<T, LPR_S, kDecodeSpecBatch>(p, wg - p.proj_wgs, keys, sm.spec);
+    } else {
+        const int item = wg - n_spec;
+        attn_item<T, LPR_A, kDecodeThreads, kDecodeAttnRows>(a, item % bh_attn, item / bh_attn, sm.attn);
     }
-    const int item = wg - n_spec;
-    attn_item<T, LPR_A, kDecodeThreads, kDecodeAttnRows>(a, item % bh_attn, item / bh_attn, sm.attn);
 }
 
 template <typename T, int LPR_S, int LPR_A>
@@ -53,14 +58,13 @@ static int launch_fused(const SpecParams& p, const AttnArgs& a, int bh_attn, hip
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_layer<T, LPR_S, LPR_A>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(speculate_lds_bytes(kDecodeMaxRows, 0)));
+                                                 static_cast<int>(speculate_lds_bytes(kDecodeMaxRows)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
-    const int n_spec = p.B * p.H;
-    const int grid = n_spec + a.nsplit * bh_attn;
-    hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A>), dim3(grid), dim3(kDecodeThreads), speculate_lds_bytes(p.n, p.D * static_cast<int>(sizeof(T))),
-                       s, p, a, n_spec, bh_attn);
+    const int grid = p.proj_wgs + p.row_wgs + a.nsplit * bh_attn;
+    hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A>), dim3(grid), dim3(kDecodeThreads),
+                       speculate_lds_bytes(p.n), s, p, a, bh_attn);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -69,7 +73,7 @@ static int lpr_of(int len, int dtype) { return len / (dtype == IG_BF16 ? 8 : 4);
 
 bool decode_fusable(const AttnCall& a, const SpecCall& s) {
     const int ls = lpr_of(s.r, s.dtype), la = lpr_of(a.d, a.dtype);
-    return a.dtype == s.dtype && s.n <= kDecodeMaxRows && s.D * (s.dtype == IG_BF16 ? 2 : 4) <= 4 * kDecodeMaxRows &&
+    return a.dtype == s.dtype && s.n <= kDecodeMaxRows &&
            plan_speculate(s.B, s.H, s.D, s.r, s.n, s.max_out, s.dtype).slices == 1 &&
            (ls == 2 || ls == 4 || ls == 8) && (la == 8 || la == 16 || la == 32);
 }
@@ -113,7 +117,7 @@ int launch_decode_layer(const AttnCall* a, const SpecCall* sc, hipStream_t s) {
         return e ? e : launch_attn_call(*a, s);
     }
     SpecParams p;
-    int e = begin_speculate(*sc, &p, s);  // (the projection kernel first, beyond 8 batch rows)
+    int e = begin_speculate(*sc, &p);
     if (e) return e;
     const AttnPlan ap = plan_attn(a->B, a->H, a->d, a->max_out);
     const AttnArgs aa{a->q, a->K, a->V, a->ld_rows, a->idx, a->count, a->d, a->max_out, ap.rows_per_split, ap.nsplit,

@@ -1,11 +1,10 @@
-// Fused speculation entry point: one 1024-thread workgroup per (b, h) running
-// spec_row (partial query, scores, selection and counters with the scores kept
-// on chip).  Few rows, or rows longer than one workgroup's LDS: each row is cut
-// into slices, one workgroup each, that leave their local selection as
-// candidates, and a merge workgroup per row selects among them.  Sliced rows
-// and batches beyond 8 rows take their partial query from the projection
-// kernel launched first.  InfiniGen, arXiv 2406.19707, paper-graph-ui summary,
-// section 3.4 "Decoding Stage" steps 1-3 and 5.
+// Fused speculation entry point: projection workgroups for the partial query,
+// then one 1024-thread workgroup per (b, h) running spec_row (scores, selection
+// and counters with the scores kept on chip), all in one launch.  Few rows, or
+// rows longer than one workgroup's LDS: each row is cut into slices, one
+// workgroup each, that leave their local selection as candidates, and a merge
+// workgroup per row selects among them.  InfiniGen, arXiv 2406.19707,
+// paper-graph-ui summary, section 3.4 "Decoding Stage" steps 1-3 and 5.
 #include <algorithm>
 
 #include "ig_spec_dev.h"
@@ -13,10 +12,14 @@
 namespace ig {
 
 template <typename T, int LPR>
-__global__ __launch_bounds__(kSpecThreads) void k_speculate(SpecParams p) {
-    extern __shared__ __align__(16) uint32_t keys[];  // staged x, then the slice's order-preserving score keys
+__global__ __launch_bounds__(kSpecThreads, 8) void k_speculate(SpecParams p) {
+    extern __shared__ __align__(16) uint32_t keys[];  // staged x (projection), or the slice's score keys
     __shared__ SpecShared<LPR * Vec<T>::N> sm;
-    spec_row<T, LPR, kSpecBatch, 16>(p, blockIdx.x, keys, sm);
+    const int wg = blockIdx.x;
+    if (wg < p.proj_wgs)
+        proj_role<T>(p, wg, keys);
+    else
+        spec_row<T, LPR, 4>(p, wg - p.proj_wgs, keys, sm);
 }
 
 __global__ __launch_bounds__(kSpecThreads) void k_spec_merge(SpecParams p) {
@@ -54,16 +57,18 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     S = (n + slice_rows - 1) / slice_rows;
     sp.ok = S <= kSpecMaxSlices;
     sp.slices = S;
-    // the projection kernel reads the partial weight once; inside the row workgroups every batch row of
-    // a head reads it again (from L2), which costs more than the extra launch beyond 8 batch rows
-    sp.proj_kernel = S > 1 || B > 8;
     sp.slice_rows = S > 1 ? slice_rows : n;
     sp.cand_cap = S > 1 ? cap : 0;
     const size_t cands = static_cast<size_t>(rows) * S * sp.cand_cap;
+    // projection workgroups: column blocks x splits of the D inputs
+    const int cpw = dtype == IG_BF16 ? proj_cols<uint16_t>() : proj_cols<float>();
+    sp.proj_blocks = (H * r + cpw - 1) / cpw;
+    sp.splits = (D + kProjSplit - 1) / kProjSplit;
+    sp.proj_wgs = sp.proj_blocks * sp.splits;
     sp.off_arrive = 0;
-    sp.rp = plan_rehearse(B, H, D, r, n, dtype);
-    sp.off_part = align256(static_cast<size_t>(B) * sizeof(uint32_t));
-    sp.off_cnt = sp.off_part + (sp.proj_kernel ? align256(sp.rp.ws_bytes) : 0);
+    sp.off_pdone = align256(static_cast<size_t>(B) * sizeof(uint32_t));
+    sp.off_part = sp.off_pdone + align256(static_cast<size_t>(rows) * sizeof(uint32_t));
+    sp.off_cnt = sp.off_part + align256(static_cast<size_t>(sp.splits) * B * H * r * sizeof(float));
     sp.off_key = sp.off_cnt + (S > 1 ? align256(static_cast<size_t>(rows) * S * sizeof(int32_t)) : 0);
     sp.off_idx = sp.off_key + (S > 1 ? align256(cands * sizeof(uint32_t)) : 0);
     // many selected slots per sequence: counter atomics in the merge would be throughput-bound
@@ -79,10 +84,10 @@ size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dt
     return plan_speculate(B, H, D, r, n, max_out, dtype).ws_bytes;
 }
 
-// keys for the rows of a workgroup; at least one word per thread (the argmin scratch of the pool
-// finish) and the attention input x (staged there first for the partial-query projection)
-size_t speculate_lds_bytes(int n, int x_bytes) {
-    const size_t w = static_cast<size_t>(std::max({n, kSpecThreads, (x_bytes + 3) / 4}));
+// keys for the rows of a workgroup; at least the projection workgroups' staged attention-input rows
+// and their sums (which also covers the pool finish's argmin scratch of one word per thread)
+size_t speculate_lds_bytes(int n) {
+    const size_t w = static_cast<size_t>(std::max(n, kProjStageWords + kSpecThreads));
     return w * sizeof(uint32_t);
 }
 
@@ -92,12 +97,12 @@ static int launch_spec_tl(const SpecParams& p, hipStream_t s) {
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_speculate<T, L>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows, 0)));
+                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_speculate<T, L>), dim3(p.B * p.H * p.slices), dim3(kSpecThreads),
-                       speculate_lds_bytes(p.slice_rows, p.D * static_cast<int>(sizeof(T))), s, p);
+    hipLaunchKernelGGL((k_speculate<T, L>), dim3(p.proj_wgs + p.row_wgs), dim3(kSpecThreads),
+                       speculate_lds_bytes(p.slice_rows), s, p);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -119,33 +124,31 @@ static int launch_merge(const SpecParams& p, hipStream_t s) {
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_spec_merge),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows, 0)));
+                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
     const int m = p.slices * p.cand_cap;
     const int words = std::max(m <= kSpecMaxRows ? m : 0, p.bits ? (p.n + 31) / 32 : 0);  // keys or the bitmap
-    hipLaunchKernelGGL(k_spec_merge, dim3(p.B * p.H), dim3(kSpecThreads), speculate_lds_bytes(words, 0), s, p);
+    hipLaunchKernelGGL(k_spec_merge, dim3(p.B * p.H), dim3(kSpecThreads), speculate_lds_bytes(words), s, p);
     return static_cast<int>(hipGetLastError());
 }
 
-int begin_speculate(const SpecCall& c, SpecParams* p, hipStream_t s) {
+int begin_speculate(const SpecCall& c, SpecParams* p) {
     const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
     char* ws = static_cast<char*>(c.ws);
-    float* part = nullptr;
-    if (sp.proj_kernel) {
-        part = reinterpret_cast<float*>(ws + sp.off_part);
-        const int e = launch_proj(c.x, c.Wq_part, c.B, c.D, c.H * c.r, c.dtype, sp.rp, part, s);
-        if (e) return e;
-    }
-    // all batch rows of a head on one XCD when the heads split evenly over the 8 XCDs (they share the
-    // head's partial weight rows through that XCD's L2)
-    *p = SpecParams{c.x, c.Wq_part, c.D, part, sp.rp.splits, c.bq_part, c.Kp, c.B, c.H, c.r, c.n, c.n_cap, c.ld, c.scale, c.mode, c.alpha,
+    // all batch rows of a head on one XCD when the heads split evenly over the 8 XCDs
+    *p = SpecParams{c.x, c.Wq_part, c.D, reinterpret_cast<float*>(ws + sp.off_part), sp.splits, c.bq_part, c.Kp, c.B,
+                    c.H, c.r, c.n, c.n_cap, c.ld, c.scale, c.mode, c.alpha,
                     c.k, c.max_sel, c.max_out, c.idx, c.count, c.q_part, c.scores, c.counters, c.cmax, c.victim,
                     reinterpret_cast<uint32_t*>(ws + sp.off_arrive), c.H % 8 == 0 ? 1 : 0, sp.slices, sp.slice_rows,
                     sp.cand_cap, reinterpret_cast<uint32_t*>(ws + sp.off_key), reinterpret_cast<int32_t*>(ws + sp.off_idx),
                     reinterpret_cast<int32_t*>(ws + sp.off_cnt)};
     if (sp.bits && c.counters) p->bits = reinterpret_cast<uint32_t*>(ws + sp.off_bits);
+    p->proj_wgs = sp.proj_wgs;
+    p->proj_blocks = sp.proj_blocks;
+    p->row_wgs = c.B * c.H * sp.slices;
+    p->pdone = reinterpret_cast<uint32_t*>(ws + sp.off_pdone);
     return 0;
 }
 
@@ -156,7 +159,7 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     const SpecCall c{x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, mode, alpha, k, max_sel, idx, count,
                      max_out, counters, cmax, victim, q_part, scores, ld, ws};
     SpecParams p;
-    int e = begin_speculate(c, &p, s);
+    int e = begin_speculate(c, &p);
     if (e) return e;
     e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
     if (e || p.slices == 1) return e;

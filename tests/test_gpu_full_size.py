@@ -2,8 +2,8 @@
 one by one on its own inputs):
 
   * the 40-layer Llama-2-13B pipeline's layer pair (B16 H40 d128 D5120 r32, n = 4096, top 5%): layer 0
-    dense attention, layer 0's ig_decode_layer (the projection kernel at B = 16, then the speculation for
-    layer 1 beside layer 0's attention), layer 1's attention over the speculated rows;
+    dense attention, layer 0's ig_decode_layer (the projection and speculation for layer 1 beside
+    layer 0's attention, one launch), layer 1's attention over the speculated rows;
   * the OPT-30B pinned host pool (B16 H56 d128 D7168 r32, n = 2048 of 4096 slots, alpha 5, 20% cap),
     with bf16 rows and with INT4 records: speculation in HBM, zero-copy gather, attention;
   * the long-context Llama-2-7B layer at its largest benchmark size (B4, n = 131072, top 4%).
@@ -118,7 +118,7 @@ def test_pool_full_size_sampled(int4):
 
 def test_long_context_b4_full_size_sampled():
     """Llama-2-7B-shaped layer at 131072 rows, batch 4, top 4% (5243 rows per head), the fused path:
-    the projection kernel, 4 slices of 32768 rows per row, a merge of 20972 candidates per row; then the
+    the projection workgroups, 4 slices of 32768 rows per row, a merge of 20972 candidates per row; then the
     attention split over the selected rows.  Sampled heads against the oracle, every head's counters."""
     from sparse_attention_ig_amd.runtime import DeviceLayer
     from tests.gpu_util import to_host
