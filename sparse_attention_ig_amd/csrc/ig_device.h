@@ -175,4 +175,34 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// ------------------------------------------------------------------ matrix-core projection step
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One 16x16 MFMA step per element type.  Operand lane layout (16x16xK): lane l supplies row l % 16
+// of A (here x: one batch row) and column l % 16 of B (one partial-weight column), each with E
+// consecutive k values of k-group l / 16; the 16x16 float result puts rows 4 (l / 16) .. + 3 of
+// column l % 16 in lane l.  Only the pairing of A's and B's k values matters for the sum, and both
+// operands use the same one.
+template <typename T> struct ProjMma;
+template <> struct ProjMma<uint16_t> {
+    static constexpr int K = 32, E = 8, CHUNK = 8;  // k per step, elements per lane, steps in flight
+    using vec = uint4;
+    static __device__ __forceinline__ vec load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+    static __device__ __forceinline__ vec zero() { return make_uint4(0, 0, 0, 0); }
+    static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+template <> struct ProjMma<float> {
+    static constexpr int K = 4, E = 1, CHUNK = 16;
+    using vec = float;
+    static __device__ __forceinline__ vec load(const float* p) { return *p; }
+    static __device__ __forceinline__ vec zero() { return 0.f; }
+    static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
 }  // namespace ig

@@ -29,7 +29,7 @@
 //
 // The workgroup index `wg` of the row is passed in (the fused decode kernel
 // runs rows after other roles' workgroups); the caller provides the LDS:
-// `keys` holds max(n, kProjStageWords) words, `sm` the fixed scratch.
+// `keys` holds max(n, kProjLdsWords) words, `sm` the fixed scratch.
 #pragma once
 
 #include <climits>
@@ -94,11 +94,13 @@ struct SpecShared {
 };
 
 // Projection workgroups (summary section 3.4 "Decoding Stage" step 1, the partial query
-// x . W~_Q^partial).  Workgroup pw takes column block pw % proj_blocks (proj_cols<T>() partial
-// columns, one lane group each) and split pw / proj_blocks of the inputs (kProjSplit of them, two
-// 16-byte vectors of weight per lane); the attention-input rows of the split are staged in LDS a few
-// batch rows at a time, each lane group's sum is added by DPP in a fixed order, and the sums of the
-// workgroup leave through LDS as whole rows of columns.
+// x . W~_Q^partial, a dense contraction: M = batch rows, N = H*r partial columns, K = D).  Workgroup
+// pw takes column block pw % proj_blocks (kProjCols columns) and split pw / proj_blocks of the D
+// inputs (kProjSplit of them).  Wave w owns 16-column tile w % kProjTiles and input slice
+// w / kProjTiles (kProjSplit / kProjSlices inputs) and runs it on the matrix cores (16x16x32 bf16 or
+// 16x16x4 f32 MFMA, x rows as A in blocks of 16 batch rows, weight columns as B, both loaded 16 bytes
+// (bf16) along k: the weight straight from HBM, x from L2); the slices' 16x16 results meet in LDS and
+// are added in slice order.
 //
 // Hand-over without flags: a partial-sum slot holds 0 (all bits clear) while it is empty.  A
 // producer never writes those bits (a sum of +0.0 is stored as -0.0, which adds the same in the
@@ -107,13 +109,12 @@ struct SpecShared {
 // counts travel through device-coherent stores and loads (agent scope: written through to the
 // level all XCDs share, read from there); no fence is needed (on this chip an agent-scope fence
 // writes back the XCD's whole L2).  The workspace starts zero-filled.
-constexpr int kProjSplit = 512;        // inputs per split partial
-constexpr int kProjStageWords = 2048;  // LDS words of staged attention-input rows (also the least `keys` size)
+constexpr int kProjSplit = 512;   // inputs per split partial
+constexpr int kProjTiles = 2;     // 16-column tiles per projection workgroup
+constexpr int kProjCols = 16 * kProjTiles;
+constexpr int kProjSlices = kSpecThreads / kWave / kProjTiles;  // input slices (one wave per tile and slice)
+constexpr int kProjLdsWords = kProjSlices * kProjTiles * 256;   // the slices' results (also the least `keys` size)
 constexpr uint32_t kProjSpinLimit = 1u << 22;  // polls before a row workgroup stops waiting
-template <typename T>
-__host__ __device__ constexpr int proj_lanes() { return kProjSplit / (2 * Vec<T>::N); }
-template <typename T>
-__host__ __device__ constexpr int proj_cols() { return kSpecThreads / proj_lanes<T>(); }
 
 __device__ __forceinline__ void coherent_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -124,65 +125,54 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 
 template <typename T>
 __device__ __forceinline__ void proj_role(const SpecParams& p, int pw, uint32_t* lds) {
-    constexpr int VEC = Vec<T>::N;
-    constexpr int LG = proj_lanes<T>();   // lanes per column
-    constexpr int CPW = proj_cols<T>();   // columns per workgroup
-    constexpr int XV = kProjSplit / VEC;  // 16-byte vectors per staged row
-    constexpr int BB = kProjStageWords * 4 / (kProjSplit * static_cast<int>(sizeof(T)));  // rows per round
-    static_assert(BB >= 1 && CPW * LG == kSpecThreads && BB * CPW <= kSpecThreads, "projection tiling");
-    const int tid = threadIdx.x, cl = tid / LG, g = tid % LG;
+    using M = ProjMma<T>;
+    constexpr int KPS = kProjSplit / kProjSlices;  // inputs per slice
+    constexpr int STEPS = KPS / M::K;              // MFMA steps per slice
+    constexpr int CH = STEPS < 8 ? STEPS : 8;      // steps whose loads are in flight together
+    static_assert(KPS % M::K == 0 && STEPS % CH == 0, "projection tiling");
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int tile = wave % kProjTiles, slice = wave / kProjTiles;
+    const int kg = lane / 16;
     const int N = p.H * p.r, D = p.D, B = p.B;
     const int blk = pw % p.proj_blocks, s = pw / p.proj_blocks;
-    const int col = blk * CPW + cl;
-    const int e0 = s * kProjSplit;
+    const int col = blk * kProjCols + tile * 16 + lane % 16;
+    const bool col_ok = col < N;
+    const int k0 = s * kProjSplit + slice * KPS + kg * M::E;  // this lane's first input (D % E == 0)
     const T* __restrict__ x = static_cast<const T*>(p.x);
-    const T* __restrict__ W = static_cast<const T*>(p.W);
-    uint4 w[2];
+    const T* __restrict__ wrow = static_cast<const T*>(p.W) + static_cast<size_t>(col_ok ? col : 0) * D;
+    float* red = reinterpret_cast<float*>(lds);  // [slice][tile][16 rows][16 columns]
+    for (int b0 = 0; b0 < B; b0 += 16) {
+        const int b = b0 + lane % 16;
+        const T* __restrict__ xrow = x + static_cast<size_t>(b < B ? b : 0) * D;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int e = e0 + (k * LG + g) * VEC;  // D is a multiple of VEC: whole vectors
-        w[k] = (col < N && e < D) ? load_raw16(W + static_cast<size_t>(col) * D + e) : make_uint4(0, 0, 0, 0);
-    }
-    uint4* xs = reinterpret_cast<uint4*>(lds);
-    float* sums = reinterpret_cast<float*>(lds + kProjStageWords);  // [BB][CPW]
-    float* out = p.part + static_cast<size_t>(s) * B * N;
-    for (int b0 = 0; b0 < B; b0 += BB) {
-        const int nb = min(BB, B - b0);
-        for (int i = tid; i < nb * XV; i += kSpecThreads) {
-            const int e = e0 + (i % XV) * VEC;
-            xs[i] = e < D ? load_raw16(x + static_cast<size_t>(b0 + i / XV) * D + e) : make_uint4(0, 0, 0, 0);
+        for (int c0 = 0; c0 < STEPS; c0 += CH) {
+            typename M::vec w[CH], xv[CH];
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                const int k = k0 + (c0 + u) * M::K;
+                w[u] = (col_ok && k < D) ? M::load(wrow + k) : M::zero();
+                xv[u] = (b < B && k < D) ? M::load(xrow + k) : M::zero();
+            }
+#pragma unroll
+            for (int u = 0; u < CH; ++u) acc = M::mma(xv[u], w[u], acc);
         }
+        // lane l holds rows 4 (l / 16) .. + 3 of column l % 16
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[((slice * kProjTiles + tile) * 16 + 4 * kg + q) * 16 + lane % 16] = acc[q];
         __syncthreads();
-        // all staged rows at once: BB independent sums per lane, reduced together
-        float a0[VEC], a1[VEC], acc[BB];
-        unpack_raw(w[0], a0);
-        unpack_raw(w[1], a1);
+        const int t = threadIdx.x;
+        if (t < kProjTiles * 256) {
+            const int tl = t / 256, row = (t / 16) % 16, c = blk * kProjCols + tl * 16 + t % 16;
+            if (b0 + row < B && c < N) {
+                float v = 0.f;
 #pragma unroll
-        for (int bi = 0; bi < BB; ++bi) {
-            acc[bi] = 0.f;
-            if (bi < nb) {
-                float xe[VEC];
-                unpack_raw(xs[bi * XV + g], xe);
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[bi] = fmaf(xe[v], a0[v], acc[bi]);
-                unpack_raw(xs[bi * XV + LG + g], xe);
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[bi] = fmaf(xe[v], a1[v], acc[bi]);
+                for (int sl = 0; sl < kProjSlices; ++sl) v += red[(sl * kProjTiles + tl) * 256 + row * 16 + t % 16];
+                coherent_store(p.part + (static_cast<size_t>(s) * B + b0 + row) * N + c,
+                               __float_as_uint(v) == 0u ? -0.f : v);  // never the empty bits
             }
         }
-#pragma unroll
-        for (int bi = 0; bi < BB; ++bi) acc[bi] = group_sum<LG>(acc[bi]);
-        if (g == 0) {
-#pragma unroll
-            for (int bi = 0; bi < BB; ++bi)
-                if (bi < nb) sums[bi * CPW + cl] = __float_as_uint(acc[bi]) == 0u ? -0.f : acc[bi];  // never empty bits
-        }
-        __syncthreads();
-        if (tid < nb * CPW) {
-            const int bi = tid / CPW, c = blk * CPW + tid % CPW;
-            if (c < N) coherent_store(out + static_cast<size_t>(b0 + bi) * N + c, sums[tid]);
-        }
-        // (the next round's staging and sums are written only after its first barrier)
+        __syncthreads();  // red is reused by the next block of batch rows
     }
 }
 

@@ -61,8 +61,7 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     sp.cand_cap = S > 1 ? cap : 0;
     const size_t cands = static_cast<size_t>(rows) * S * sp.cand_cap;
     // projection workgroups: column blocks x splits of the D inputs
-    const int cpw = dtype == IG_BF16 ? proj_cols<uint16_t>() : proj_cols<float>();
-    sp.proj_blocks = (H * r + cpw - 1) / cpw;
+    sp.proj_blocks = (H * r + kProjCols - 1) / kProjCols;
     sp.splits = (D + kProjSplit - 1) / kProjSplit;
     sp.proj_wgs = sp.proj_blocks * sp.splits;
     sp.off_arrive = 0;
@@ -84,10 +83,10 @@ size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dt
     return plan_speculate(B, H, D, r, n, max_out, dtype).ws_bytes;
 }
 
-// keys for the rows of a workgroup; at least the projection workgroups' staged attention-input rows
-// and their sums (which also covers the pool finish's argmin scratch of one word per thread)
+// keys for the rows of a workgroup; at least the projection workgroups' slice results (which also
+// covers the pool finish's argmin scratch of one word per thread)
 size_t speculate_lds_bytes(int n) {
-    const size_t w = static_cast<size_t>(std::max(n, kProjStageWords + kSpecThreads));
+    const size_t w = static_cast<size_t>(std::max(n, kProjLdsWords));
     return w * sizeof(uint32_t);
 }
 
