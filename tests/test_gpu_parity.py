@@ -43,6 +43,16 @@ def long_global():
     return _spec(gen.llama2_7b_long(n=20000), H=2, topk=200)
 
 
+def batch20_r16():
+    # two 16-row batch blocks in the projection; a 32-column block spans two heads; D = 384 is not a
+    # whole number of 512-input splits
+    return _spec(gen.opt_6_7b(n=600, B=20), H=3, r=16, heavy=12, topk=50)
+
+
+def tiny_batch17():
+    return _spec(gen.tiny_fp32(), B=17)
+
+
 CASES = [
     # name, spec factory, mode, kwargs
     ("tiny-threshold", gen.tiny_fp32, "threshold", dict(alpha=4.0)),
@@ -57,6 +67,8 @@ CASES = [
     ("opt6.7b-topk128", gen.opt_6_7b, "topk", dict(k=128, counters="random", victim=True)),
     ("long-global-topk", long_global, "topk", dict(k=200)),
     ("long-global-threshold", long_global, "threshold", dict(alpha=5.0, max_sel=4000, cap=True)),
+    ("batch20-r16-topk", batch20_r16, "topk", dict(k=50)),
+    ("tiny-batch17-threshold", tiny_batch17, "threshold", dict(alpha=4.0)),
 ]
 
 
