@@ -189,8 +189,12 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * required) starts with one uint32 arrival word per sequence ([B] at offset
  * 0), then the projection's arrival words and split partial sums, then the
  * slices' candidates (when there are slices); it must have been zero-filled
- * once with ig_workspace_init, and every call returns the arrival words to
- * zero.  Calls sharing a workspace must not overlap.  H <= 65535.
+ * once with ig_workspace_init, and every call returns the arrival words, the
+ * counts and the partial-sum slots to zero.  Calls sharing a workspace must
+ * not overlap and must agree on B, H, D and r (the places of those regions
+ * depend on them; n, max_out and the mode may change from call to call): run
+ * ig_workspace_init again before a call with other B, H, D or r.
+ * H <= 65535.
  */
 int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
                  int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
