@@ -158,3 +158,16 @@ def test_workspace_sizes(lib):
     assert L.ig_workspace_size(L.IG_OP_ATTN, 1, 1, 0, 128, 0, 0, 16) == 0   # a single split needs none
     assert L.ig_workspace_size(L.IG_OP_ATTN, 1, 32, 0, 128, 0, 0, 5243) > 0
     assert L.ig_workspace_size(L.IG_OP_SELECT, 2, 3, 0, 0, 0, 100, 10) == 2 * 3 * 4
+
+
+def test_speculation_workspace_holds_its_documented_regions(lib):
+    """The speculation workspace holds (in this order, each 256-byte aligned) one arrival word per
+    sequence, one slice count per row, and the projection's split partial sums [ceil(D/512)][B][H*r]
+    float32, then the slices' candidates when rows are sliced; its size only grows with n."""
+    a256 = lambda v: (v + 255) // 256 * 256
+    for B, H, D, r, n, max_out in [(8, 32, 4096, 32, 2048, 128), (16, 40, 5120, 32, 4352, 218),
+                                   (1, 4, 256, 16, 256, 32), (20, 3, 384, 16, 600, 50), (4, 32, 4096, 32, 131072, 5243)]:
+        need = a256(4 * B) + a256(4 * B * H) + a256(-(-D // 512) * B * H * r * 4)
+        sizes = [L.ig_workspace_size(L.IG_OP_SPECULATE, B, H, D, 128, r, nn, max_out) for nn in (max(1, n // 4), n)]
+        assert sizes[1] >= need, (B, H, D, r, n)
+        assert sizes[1] >= sizes[0], (B, H, D, r, n)
