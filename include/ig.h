@@ -57,7 +57,8 @@ const char* ig_last_error(void);
  * 4: ig_decode_layer; 5: ig_partial_weight_index_dev; 6: the speculation
  * workspace starts with its arrival words; 7: the INT4 pool calls; 8: the
  * speculation's partial query comes from projection workgroups of the same
- * launch, whose arrival words follow the sequences' in the workspace). */
+ * launch, whose arrival words follow the sequences' in the workspace;
+ * 9: ig_select takes a workspace for rows longer than 32768 keys). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -275,6 +276,12 @@ int ig_decode_layer(int B, int H, int d, int dtype, const ig_attn_call* attn, co
  * Ties go to the lower index; the comparison is in float32.  Output:
  * idx [B][H][max_out] int32 ascending (entries >= count unspecified),
  * count [B][H] int32 in [1, max_out].  Scores must not be NaN.
+ * One workgroup per (b, h) row with the row's keys in LDS up to n = 32768.
+ * Longer threshold and top-k rows are cut into slices that select locally and
+ * hand on candidates to a merge launch (up to 16 slices of 32768 rows; longer
+ * rows, and the head-average mode, are streamed from HBM in every pass).  The
+ * workspace (IG_OP_SELECT bytes) is required in the head-average mode and for
+ * sliced rows (ws may be NULL otherwise); it needs no initialisation.
  */
 int ig_select(const float* scores, int B, int H, int n, int ld, int mode,
               float alpha, int k, int max_sel,

@@ -270,7 +270,7 @@ def ig_select(scores, mode: str, max_out: int, *, n=None, alpha: float = math.in
     if count is None:
         count = torch.empty((B, H), dtype=torch.int32, device=scores.device)
     m = _MODES[mode]
-    need = ig_workspace_size(IG_OP_SELECT, B, H, 0, 0, 0, n, max_out) if m == IG_SEL_HEADAVG else 0
+    need = ig_workspace_size(IG_OP_SELECT, B, H, 0, 0, 0, n, max_out)  # head average, sliced long rows
     ws, wsb = _ws(ws, need, scores.device)
     _check(load().ig_select(_ptr(scores), B, H, n, ld, m, float(alpha), int(k), int(max_sel), _ptr(idx),
                             _ptr(count), max_out, _ptr(ws), wsb, _stream(stream)), "ig_select")

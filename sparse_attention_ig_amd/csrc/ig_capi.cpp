@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 8; }
+int ig_version(void) { return 9; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 
@@ -185,7 +185,7 @@ int ig_select(const float* scores, int B, int H, int n, int ld, int mode, float 
         IG_REQUIRE(alpha >= 0.f && !std::isnan(alpha), "ig_select: alpha must be >= 0 (inf allowed)");
     else
         IG_REQUIRE(k >= 1, "ig_select: k must be >= 1");
-    const size_t need = mode == IG_SEL_HEADAVG ? select_ws_bytes(B, H, n, max_out) : 0;
+    const size_t need = select_needs_ws(B, H, n, max_out, mode) ? select_ws_bytes(B, H, n, max_out) : 0;
     IG_REQUIRE(need == 0 || (ws && ws_bytes >= need), "ig_select: workspace of %zu bytes needed", need);
     return hip_status(launch_select(scores, B, H, n, ld, mode, alpha, k, max_sel, idx, count, max_out, ws, stream),
                       "ig_select");

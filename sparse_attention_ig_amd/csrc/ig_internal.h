@@ -42,11 +42,22 @@ struct AttnPlan {
 AttnPlan plan_attn(int B, int H, int d, int max_out);
 
 size_t select_ws_bytes(int B, int H, int n, int max_out);
+bool select_needs_ws(int B, int H, int n, int max_out, int mode);  // head average, or sliced long rows
 
 constexpr int kSpecMaxRows = 32768;   // rows (or candidates) one speculation workgroup holds in LDS
 constexpr int kSpecMaxSlices = 16;    // slices per row of the fused speculation
 constexpr int64_t kBitsTouchMin = 262144;  // selected slots per call from which sliced rows use bitmaps
 constexpr int kSliceSlackMin = 2048;       // max_out from which slices get spare candidate slots
+// Slices of rows too long for one workgroup's LDS, or too few to fill the chip: `slices` workgroups
+// per row of `slice_rows` rows each, handing on up to `cap` candidates each to a merge workgroup per
+// row (the fused speculation and ig_select's long rows).  ok is false when a row would need more than
+// kSpecMaxSlices slices.
+struct SlicePlan {
+    int slices, slice_rows, cap;
+    bool ok;
+};
+SlicePlan plan_slices(int64_t rows, int n, int max_out);
+
 struct SpecPlan {
     int slices, slice_rows, cand_cap;
     int proj_blocks, splits, proj_wgs;  // projection workgroups: column blocks x splits of the D inputs

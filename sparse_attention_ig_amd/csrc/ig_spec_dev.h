@@ -84,6 +84,8 @@ struct SpecParams {
 
 // Fills the launch parameters of a speculation call (projection and row workgroups).
 int begin_speculate(const SpecCall& c, SpecParams* p);
+// The merge launch of sliced rows: one workgroup per row over the slices' candidate slots.
+int launch_spec_merge(const SpecParams& p, hipStream_t s);
 
 template <int R>
 struct SpecShared {

@@ -14,10 +14,19 @@
 //    exclusive scan of per-thread counts (wave shuffles + per-wave totals in
 //    LDS) gives each selected row its output slot, so idx comes out ascending
 //    without any sort and the result is deterministic.
+// Threshold and top-k rows longer than the LDS holds are cut into slices, as in
+// the fused speculation: each slice workgroup keeps its slice's keys in LDS and
+// hands on a superset of its own selection as candidates, and a merge
+// workgroup per row applies the row's rules to them (a key among the row's top
+// k is among its slice's top k, and a key at or above the row's cut is at or
+// above its slice's, whose maximum is at most the row's).  The head-average
+// mode, and rows beyond 16 slices, stream the row from HBM in every pass.
+#include <algorithm>
 #include <type_traits>
 
 #include "ig_internal.h"
 #include "ig_select_dev.h"
+#include "ig_spec_dev.h"
 
 namespace ig {
 
@@ -96,14 +105,119 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     if (tid == 0) count[bh] = min(w, max_out);
 }
 
-size_t select_ws_bytes(int B, int H, int n, int max_out) {
-    (void)n;
-    (void)max_out;
-    return static_cast<size_t>(B) * H * sizeof(int32_t);  // per-head counts of the head-average mode
+// Slice workgroup (slice, row) of a long row: the slice's keys in LDS, then its candidates.
+__global__ __launch_bounds__(kSpecThreads) void k_select_slice(SpecParams p, const float* __restrict__ scores,
+                                                               int ld) {
+    extern __shared__ __align__(16) uint32_t keys[];  // the slice's keys (slice_rows <= kSpecMaxRows)
+    __shared__ SpecShared<kSpecMaxSlices + 1> sm;
+    const int tid = threadIdx.x;
+    const int nrow = p.B * p.H;
+    const int slice = blockIdx.x / nrow, bh = blockIdx.x - slice * nrow;
+    const int r0 = slice * p.slice_rows;
+    const int m = min(p.n - r0, p.slice_rows);
+    const float* __restrict__ srow = scores + static_cast<size_t>(bh) * ld + r0;
+    fast_sel_init(sm.fs);  // published by the barriers of block_max_u32
+    constexpr int U = 8;   // loads per lane in flight
+    uint32_t kmax = 0;
+    for (int j0 = tid; j0 < m; j0 += kSpecThreads * U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = j0 + u * kSpecThreads < m ? srow[j0 + u * kSpecThreads] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * kSpecThreads;
+            if (j < m) {
+                const uint32_t key = score_key(v[u]);
+                keys[j] = key;
+                kmax = key > kmax ? key : kmax;
+            }
+        }
+    }
+    const uint32_t kmax_all = block_max_u32(kmax, sm.sh);  // also publishes the LDS keys
+    spec_select<true>(p, bh / p.H, bh, slice, m, m, kmax_all, LdsKeys{keys}, keys, sm.sh, sm.fs, sm.last,
+                      [&](int j) { return r0 + j; });
+}
+
+// Workspace of a select call: the head-average mode's per-head counts, then (rows longer than the LDS
+// holds) the slices' candidate counts, keys and row indices.
+struct SelectPlan {
+    SlicePlan sl;
+    bool sliced;
+    size_t off_cnt, off_key, off_idx, bytes;
+};
+
+static size_t align256s(size_t v) { return (v + 255) / 256 * 256; }
+
+static SelectPlan plan_select(int B, int H, int n, int max_out) {
+    SelectPlan sp{};
+    const int64_t rows = static_cast<int64_t>(B) * H;
+    sp.off_cnt = align256s(static_cast<size_t>(rows) * sizeof(int32_t));
+    sp.bytes = static_cast<size_t>(rows) * sizeof(int32_t);
+    if (n > kSelLdsKeys) {
+        sp.sl = plan_slices(rows, n, std::min(n, max_out));
+        sp.sliced = sp.sl.ok && sp.sl.slices > 1;
+    }
+    if (sp.sliced) {
+        const size_t cands = static_cast<size_t>(rows) * sp.sl.slices * sp.sl.cap;
+        sp.off_key = sp.off_cnt + align256s(static_cast<size_t>(rows) * sp.sl.slices * sizeof(int32_t));
+        sp.off_idx = sp.off_key + align256s(cands * sizeof(uint32_t));
+        sp.bytes = sp.off_idx + cands * sizeof(int32_t);
+    }
+    return sp;
+}
+
+size_t select_ws_bytes(int B, int H, int n, int max_out) { return plan_select(B, H, n, max_out).bytes; }
+
+bool select_needs_ws(int B, int H, int n, int max_out, int mode) {
+    return mode == IG_SEL_HEADAVG || plan_select(B, H, n, max_out).sliced;
+}
+
+static int launch_select_sliced(const SelectPlan& sp, const float* scores, int B, int H, int n, int ld, int mode,
+                                float alpha, int k, int max_sel, int32_t* idx, int32_t* count, int max_out,
+                                void* ws, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select_slice),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(speculate_lds_bytes(kSpecMaxRows)));
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr_set = true;
+    }
+    char* w = static_cast<char*>(ws);
+    SpecParams p{};
+    p.B = B;
+    p.H = H;
+    p.n = n;
+    p.n_cap = n;
+    p.ld = ld;
+    p.scale = 1.f;
+    p.mode = mode;
+    p.alpha = alpha;
+    p.k = k;
+    p.max_sel = max_sel;
+    p.max_out = max_out;
+    p.idx = idx;
+    p.count = count;
+    p.xcd_heads = 0;  // merge workgroup wg is row wg: b = wg / H
+    p.slices = sp.sl.slices;
+    p.slice_rows = sp.sl.slice_rows;
+    p.cand_cap = sp.sl.cap;
+    p.cand_key = reinterpret_cast<uint32_t*>(w + sp.off_key);
+    p.cand_idx = reinterpret_cast<int32_t*>(w + sp.off_idx);
+    p.cand_cnt = reinterpret_cast<int32_t*>(w + sp.off_cnt);
+    hipLaunchKernelGGL(k_select_slice, dim3(B * H * sp.sl.slices), dim3(kSpecThreads),
+                       speculate_lds_bytes(sp.sl.slice_rows), s, p, scores, ld);
+    const int e = static_cast<int>(hipGetLastError());
+    return e ? e : launch_spec_merge(p, s);
 }
 
 int launch_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k, int max_sel,
                   int32_t* idx, int32_t* count, int max_out, void* ws, hipStream_t s) {
+    if (mode != IG_SEL_HEADAVG) {
+        const SelectPlan sp = plan_select(B, H, n, max_out);
+        if (sp.sliced)
+            return launch_select_sliced(sp, scores, B, H, n, ld, mode, alpha, k, max_sel, idx, count, max_out, ws, s);
+    }
     const dim3 grid(B * H), block(kSelThreads);
     int32_t* hc = static_cast<int32_t*>(ws);
     const bool lds = n <= kSelLdsKeys;

@@ -30,9 +30,7 @@ __global__ __launch_bounds__(kSpecThreads) void k_spec_merge(SpecParams p) {
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype) {
-    SpecPlan sp{};
-    const int64_t rows = static_cast<int64_t>(B) * H;
+SlicePlan plan_slices(int64_t rows, int n, int max_out) {
     // slices per row: enough for every row to fit in LDS, more (up to 16, at least 2048 rows each) when
     // there are too few rows to fill the chip; fewer while the merge's candidates would not fit its LDS,
     // down to what the occupancy needs (a merge over more candidates reads them from global memory)
@@ -54,11 +52,23 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
         if (S == 1 || static_cast<int64_t>(S) * cap <= kSpecMaxRows || S == s_min) break;
         --S;
     }
-    S = (n + slice_rows - 1) / slice_rows;
-    sp.ok = S <= kSpecMaxSlices;
+    SlicePlan pl{};
+    pl.slices = (n + slice_rows - 1) / slice_rows;
+    pl.ok = pl.slices <= kSpecMaxSlices;
+    pl.slice_rows = pl.slices > 1 ? slice_rows : n;
+    pl.cap = pl.slices > 1 ? cap : 0;
+    return pl;
+}
+
+SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype) {
+    SpecPlan sp{};
+    const int64_t rows = static_cast<int64_t>(B) * H;
+    const SlicePlan pl = plan_slices(rows, n, max_out);
+    const int S = pl.slices;
+    sp.ok = pl.ok;
     sp.slices = S;
-    sp.slice_rows = S > 1 ? slice_rows : n;
-    sp.cand_cap = S > 1 ? cap : 0;
+    sp.slice_rows = pl.slice_rows;
+    sp.cand_cap = pl.cap;
     const size_t cands = static_cast<size_t>(rows) * S * sp.cand_cap;
     // projection workgroups: column blocks x splits of the D inputs
     sp.proj_blocks = (H * r + kProjCols - 1) / kProjCols;
@@ -118,7 +128,7 @@ static int launch_spec_t(const SpecParams& p, hipStream_t s) {
     }
 }
 
-static int launch_merge(const SpecParams& p, hipStream_t s) {
+int launch_spec_merge(const SpecParams& p, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_spec_merge),
@@ -162,7 +172,7 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     if (e) return e;
     e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
     if (e || p.slices == 1) return e;
-    if ((e = launch_merge(p, s)) || !p.bits) return e;
+    if ((e = launch_spec_merge(p, s)) || !p.bits) return e;
     const SpecPlan sp = plan_speculate(B, H, D, r, n, max_out, dtype);
     return launch_touch_bits(counters, p.bits, B, H, n, n_cap, cmax,
                              reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), victim, s);

@@ -65,13 +65,15 @@ SELECT_CASES = [
     (30000, "wide", "topk", dict(k=6000), 6000),
     (32000, "dense", "threshold", dict(alpha=1.5, max_sel=6400), 6400),
     (24576, "few", "topk", dict(k=5000), 5000),                         # bounds on equal keys: full radix
-    # rows beyond the LDS key store: the same primitives read the scores from global memory
+    # rows beyond the LDS key store: cut into slices of at most 32768 keys that hand on candidates to a
+    # merge (threshold and top-k)
     (40000, "wide", "topk", dict(k=8000), 8000),
     (50000, "dense", "topk", dict(k=500), 500),
     (45000, "few", "threshold", dict(alpha=1.0, max_sel=9000), 9000),
     (36000, "dense", "threshold", dict(alpha=2.0), 36000),
     (100000, "dense", "threshold", dict(alpha=float("inf")), 100000),  # every row kept: counts past 65535
     (90000, "equal", "topk", dict(k=80000), 80000),                     # 90000 equal keys, the first 80000
+    (600000, "wide", "topk", dict(k=3000), 3000),                       # beyond 16 slices: streamed from HBM
 ]
 
 

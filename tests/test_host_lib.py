@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(L.exported_symbols())
     for name in declared:
         assert hasattr(lib, name)
-    assert L.ig_version() == 8
+    assert L.ig_version() == 9
 
 
 @pytest.mark.parametrize("m,d", [(256, 64), (128, 128), (64, 16)])
