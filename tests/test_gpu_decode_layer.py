@@ -8,8 +8,9 @@ what the two separate calls give:
   attention half     within 1e-5 relative of ig_sparse_decode_attn on a copy (the lane groups
                      associate the float sums differently), and within the bf16/f32 attention tolerance
                      of the oracle on the selected rows.
-Covered: the fused shapes (bf16 and f32), an attention split into several workgroups with the
-combine, a shape outside the fused set (two launches), either half alone, and the aliasing check.
+Covered: the fused shapes (bf16 and f32, more than 16 batch rows), an attention split into several
+workgroups with the combine, a shape outside the fused set (two launches), either half alone, and the
+aliasing check.
 """
 
 import numpy as np
@@ -49,6 +50,11 @@ CASES = [
      lambda: _spec(gen.opt_6_7b(n=700, B=2), H=4, d=32, r=8, seed=2005), dict(mode="topk", k=40, max_out=40)),
     ("opt6.7b-full", lambda: gen.opt_6_7b(), lambda: _spec(gen.opt_6_7b(), seed=2006),
      dict(mode="topk", k=128, max_out=128)),
+    # more than 16 batch rows (two 16-row blocks in the projection workgroups) and r = 16 (a 32-column
+    # block spans two heads)
+    ("bf16-batch20-r16", lambda: _spec(gen.opt_6_7b(n=600, B=20), H=3, r=16, heavy=12, topk=50),
+     lambda: _spec(gen.opt_6_7b(n=640, B=20), H=3, r=16, heavy=12, topk=50, seed=2007),
+     dict(mode="topk", k=50, max_out=50)),
 ]
 
 
