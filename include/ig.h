@@ -57,8 +57,8 @@ const char* ig_last_error(void);
  * 4: ig_decode_layer; 5: ig_partial_weight_index_dev; 6: the speculation
  * workspace starts with its arrival words; 7: the INT4 pool calls; 8: the
  * speculation's partial query comes from projection workgroups of the same
- * launch, whose arrival words follow the sequences' in the workspace;
- * 9: ig_select takes a workspace for rows longer than 32768 keys). */
+ * launch, whose split partial sums follow the sequences' arrival words in
+ * the workspace; 9: ig_select takes a workspace for rows longer than 32768 keys). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
