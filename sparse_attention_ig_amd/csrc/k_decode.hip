@@ -31,10 +31,11 @@ union DecodeShared {
 
 // Two 1024-thread workgroups per CU (8 waves per SIMD, at most 64 VGPRs each), so that one workgroup
 // of each role fits on a CU at once (the second launch bound is the minimum number of waves per SIMD).
-// Rows in flight per lane that keep the registers there without spills: 4 partial-key rows (double
-// buffered) and 2 K/V rows (64 lane groups x 2 = 128 rows per pass).
+// Rows in flight per lane: 4 partial-key rows (double buffered; the most that keep the registers
+// without spills) and 1 K/V row (64 lane groups, 64 rows per pass): the attention then takes less of
+// the memory system while the rows stream their partial keys, which measured faster than 2 K/V rows.
 constexpr int kDecodeSpecBatch = 4;
-constexpr int kDecodeAttnRows = 2;
+constexpr int kDecodeAttnRows = 1;
 
 template <typename T, int LPR_S, int LPR_A>
 __global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int bh_attn) {
