@@ -32,12 +32,13 @@ union DecodeShared {
 // Two 1024-thread workgroups per CU (8 waves per SIMD, at most 64 VGPRs each), so that one workgroup
 // of each role fits on a CU at once (the second launch bound is the minimum number of waves per SIMD).
 // Rows in flight per lane: 4 partial-key rows (double buffered; the most that keep the registers
-// without spills) and 1 K/V row (64 lane groups, 64 rows per pass): the attention then takes less of
-// the memory system while the rows stream their partial keys, which measured faster than 2 K/V rows.
+// without spills) and ROWS K/V rows per attention lane group: 1 when an attention item's rows fit
+// two passes of one row per lane group (the attention then takes less of the memory system while
+// the rows stream their partial keys: measured faster at 128 rows per item), else 2 (measured
+// faster at 205-218 rows per item).
 constexpr int kDecodeSpecBatch = 4;
-constexpr int kDecodeAttnRows = 1;
 
-template <typename T, int LPR_S, int LPR_A>
+template <typename T, int LPR_S, int LPR_A, int ROWS>
 __global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int bh_attn) {
     extern __shared__ __align__(16) uint32_t keys[];  // staged x (projection) or the speculation's score keys
     __shared__ DecodeShared<LPR_S * Vec<T>::N, LPR_A, Vec<T>::N> sm;
@@ -49,22 +50,22 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p
         spec_row<T, LPR_S, kDecodeSpecBatch>(p, wg - p.proj_wgs, keys, sm.spec);
     } else {
         const int item = wg - n_spec;
-        attn_item<T, LPR_A, kDecodeThreads, kDecodeAttnRows>(a, item % bh_attn, item / bh_attn, sm.attn);
+        attn_item<T, LPR_A, kDecodeThreads, ROWS>(a, item % bh_attn, item / bh_attn, sm.attn);
     }
 }
 
-template <typename T, int LPR_S, int LPR_A>
+template <typename T, int LPR_S, int LPR_A, int ROWS>
 static int launch_fused(const SpecParams& p, const AttnArgs& a, int bh_attn, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_layer<T, LPR_S, LPR_A>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_layer<T, LPR_S, LPR_A, ROWS>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  static_cast<int>(speculate_lds_bytes(kDecodeMaxRows)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
     const int grid = p.proj_wgs + p.row_wgs + a.nsplit * bh_attn;
-    hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A>), dim3(grid), dim3(kDecodeThreads),
+    hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A, ROWS>), dim3(grid), dim3(kDecodeThreads),
                        speculate_lds_bytes(p.n), s, p, a, bh_attn);
     return static_cast<int>(hipGetLastError());
 }
@@ -79,12 +80,19 @@ bool decode_fusable(const AttnCall& a, const SpecCall& s) {
            (ls == 2 || ls == 4 || ls == 8) && (la == 8 || la == 16 || la == 32);
 }
 
+template <typename T, int LPR_S, int LPR_A>
+static int launch_fused_r(const SpecParams& p, const AttnArgs& a, int bh_attn, hipStream_t s) {
+    // one K/V row per lane group when an item's rows fit two passes of that, else two
+    if (a.rows_per_split <= 2 * (kDecodeThreads / LPR_A)) return launch_fused<T, LPR_S, LPR_A, 1>(p, a, bh_attn, s);
+    return launch_fused<T, LPR_S, LPR_A, 2>(p, a, bh_attn, s);
+}
+
 template <typename T, int LPR_S>
 static int launch_fused_s(const SpecParams& p, const AttnArgs& a, int la, int bh_attn, hipStream_t s) {
     switch (la) {
-        case 8: return launch_fused<T, LPR_S, 8>(p, a, bh_attn, s);
-        case 16: return launch_fused<T, LPR_S, 16>(p, a, bh_attn, s);
-        case 32: return launch_fused<T, LPR_S, 32>(p, a, bh_attn, s);
+        case 8: return launch_fused_r<T, LPR_S, 8>(p, a, bh_attn, s);
+        case 16: return launch_fused_r<T, LPR_S, 16>(p, a, bh_attn, s);
+        case 32: return launch_fused_r<T, LPR_S, 32>(p, a, bh_attn, s);
         default: return static_cast<int>(hipErrorInvalidValue);
     }
 }
