@@ -49,6 +49,9 @@ enum { IG_F32 = 0, IG_BF16 = 1 };
 enum { IG_SEL_THRESHOLD = 0, IG_SEL_TOPK = 1, IG_SEL_HEADAVG = 2 };
 enum { IG_OP_REHEARSE = 0, IG_OP_SELECT = 1, IG_OP_ATTN = 2, IG_OP_SPECULATE = 3, IG_OP_TOUCH = 4,
        IG_OP_SETUP = 5 };
+/* Sticky status bits of a speculation workspace (ig_workspace_status). */
+enum { IG_WS_TIMEOUT = 1,   /* a row's partial query did not arrive within the poll limit */
+       IG_WS_SHAPE = 2 };   /* a call's (B, H, D, r) differs from the one the workspace was claimed for */
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* ig_last_error(void);
@@ -58,7 +61,9 @@ const char* ig_last_error(void);
  * workspace starts with its arrival words; 7: the INT4 pool calls; 8: the
  * speculation's partial query comes from projection workgroups of the same
  * launch, whose split partial sums follow the sequences' arrival words in
- * the workspace; 9: ig_select takes a workspace for rows longer than 32768 keys). */
+ * the workspace; 9: ig_select takes a workspace for rows longer than 32768 keys;
+ * 10: the speculation workspace starts with a status word and a shape stamp,
+ * ig_workspace_status, ig_set_handover_test_mode). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -151,9 +156,33 @@ size_t ig_workspace_size(int op, int B, int H, int D, int d, int r, int n, int m
 /*
  * Zero-fill a workspace on `stream` (a fill kernel, so it may be captured in a
  * graph).  Required once after allocating the workspace of ig_speculate, whose
- * calls then leave it zero-filled; harmless for the others.
+ * calls then leave it zero-filled (status and stamp aside); required again
+ * before a speculation call of another (B, H, D, r), and after a failure (a
+ * nonzero status).  Harmless for the other calls' workspaces.
  */
 int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Status word of a speculation workspace (ig_speculate, the speculation half
+ * of ig_decode_layer): 0, or IG_WS_* bits set by a call that ran on it.  The
+ * bits are sticky: a workspace with a nonzero status gives count = -1 for
+ * every row of later calls until ig_workspace_init clears it.  Waits for the
+ * work enqueued on `stream` (hipStreamSynchronize) and copies the word to
+ * *status; not for use under graph capture.  IG_EINVAL when ws or status is
+ * NULL or ws_bytes is below 16.
+ */
+int ig_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, hipStream_t stream);
+
+/*
+ * Failure-path testing of the speculation's in-launch hand-over, process-wide,
+ * read when a call is launched: spin_limit = polls of a row workgroup before it
+ * stops waiting for its partial query (0: the default, 2^22 polls of a few
+ * hundred ns each); withhold != 0 makes the projection workgroups store no
+ * partial sums, so that every row reaches its poll limit and fails as
+ * ig_speculate describes.  ig_set_handover_test_mode(0, 0) restores normal
+ * operation.  Returns IG_OK.
+ */
+int ig_set_handover_test_mode(uint32_t spin_limit, int withhold);
 
 /*
  * Speculation for the next layer (section 3.4, "Decoding Stage", steps 1-2):
@@ -187,15 +216,24 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * one workgroup per (b, h) (or per slice), which adds its head's split
  * partial sums in split order, then scores, selects and updates the counters;
  * with slices, a merge launch follows.  The workspace (IG_OP_SPECULATE bytes,
- * required) starts with one uint32 arrival word per sequence ([B] at offset
- * 0), then the projection's arrival words and split partial sums, then the
- * slices' candidates (when there are slices); it must have been zero-filled
- * once with ig_workspace_init, and every call returns the arrival words, the
- * counts and the partial-sum slots to zero.  Calls sharing a workspace must
- * not overlap and must agree on B, H, D and r (the places of those regions
- * depend on them; n, max_out and the mode may change from call to call): run
- * ig_workspace_init again before a call with other B, H, D or r.
- * H <= 65535.
+ * required) starts with a 256-byte region holding the status word (uint32 at
+ * offset 0, see ig_workspace_status) and the shape stamp (uint64 at offset 8),
+ * then one uint32 arrival word per sequence ([B] at offset 256), the slices'
+ * per-row counts and the projection's split partial sums, then the slices'
+ * candidates (when there are slices); it must have been zero-filled once with
+ * ig_workspace_init, and every call returns the arrival words, the counts and
+ * the partial-sum slots to zero.  The first call after the zero-fill stamps
+ * the workspace with its (B, H, D, r) (the places of those regions depend on
+ * them; n, max_out and the mode may change from call to call); a call of
+ * another (B, H, D, r) sets IG_WS_SHAPE instead of running: run
+ * ig_workspace_init before it.  Calls sharing a workspace must not overlap.
+ * Failures (not reported by the return value, which covers the launch only):
+ * a row workgroup that finds a nonzero status or a foreign stamp, or whose
+ * partial query is still missing after the poll limit (IG_WS_TIMEOUT; it then
+ * leaves every partial-sum slot as it is, since a late producer may still
+ * store into one), writes count = -1 for its row (idx, q_part and scores of
+ * that row unspecified) and touches no counter of it; the rows that completed
+ * are valid.  H <= 65535, B <= 65535, D < 2^22.
  */
 int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
                  int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,

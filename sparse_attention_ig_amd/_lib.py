@@ -61,6 +61,8 @@ _SIGS = {
     "ig_partial_weight_index": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _i]),
     "ig_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "ig_workspace_init": (_i, [_vp, _sz, _vp]),
+    "ig_workspace_status": (_i, [_vp, _sz, ctypes.POINTER(_u32), _vp]),
+    "ig_set_handover_test_mode": (_i, [_u32, _i]),
     "ig_speculate": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _i, _i, _vp, _vp, _i,
                           _vp, _u32, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "ig_rehearse": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -233,6 +235,22 @@ def ig_rehearse(x, Wq_part, Kp, n: int, scale: float, *, bq_part=None, q_part=No
 def ig_workspace_init(ws, *, stream=None):
     _check(load().ig_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "ig_workspace_init")
     return ws
+
+
+def ig_workspace_status(ws, *, stream=None) -> int:
+    """The status word of a speculation workspace (0, or IG_WS_* bits); waits for ``stream``."""
+    v = ctypes.c_uint32(0)
+    _check(load().ig_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(v), _stream(stream)),
+           "ig_workspace_status")
+    return int(v.value)
+
+
+def ig_set_handover_test_mode(spin_limit: int = 0, withhold: bool = False):
+    """Failure-path testing of the speculation hand-over (0, False: normal operation)."""
+    _check(load().ig_set_handover_test_mode(spin_limit, 1 if withhold else 0), "ig_set_handover_test_mode")
+
+
+IG_WS_TIMEOUT, IG_WS_SHAPE = 1, 2
 
 
 def ig_speculate(x, Wq_part, Kp, n: int, scale: float, mode: str, max_out: int, *, alpha: float = math.inf,

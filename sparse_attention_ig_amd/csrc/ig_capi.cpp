@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 9; }
+int ig_version(void) { return 10; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 
@@ -128,6 +128,22 @@ int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
     return hip_status(launch_zero(ws, ws_bytes, stream), "ig_workspace_init");
 }
 
+int ig_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, hipStream_t stream) {
+    IG_REQUIRE(ws && status && ws_bytes >= 16, "ig_workspace_status: NULL workspace or status, or fewer than 16 "
+               "bytes");
+    uint32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(static_cast<int>(e), "ig_workspace_status");
+    *status = v;
+    return ok();
+}
+
+int ig_set_handover_test_mode(uint32_t spin_limit, int withhold) {
+    set_handover_test_mode(spin_limit, withhold);
+    return ok();
+}
+
 // Validation of a speculation call (ig_speculate, and the speculation half of ig_decode_layer).
 static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes) {
     const int dtype = c.dtype, B = c.B, D = c.D, H = c.H, r = c.r, n = c.n, n_cap = c.n_cap, max_out = c.max_out;
@@ -156,7 +172,8 @@ static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes) {
         return fail(IG_EUNSUPPORTED, "%s: n = %d needs more than %d slices of %d rows; use ig_rehearse + "
                     "ig_select", fn, n, kSpecMaxSlices, kSpecMaxRows);
     IG_REQUIRE(!c.counters || c.cmax >= 2, "%s: cmax must be >= 2", fn);
-    IG_REQUIRE(H <= 0xFFFF, "%s: at most 65535 heads", fn);
+    IG_REQUIRE(H <= 0xFFFF && B <= 0xFFFF && D < (1 << 22), "%s: at most 65535 heads and batch rows and "
+               "D < 2^22 (the workspace stamp)", fn);
     const size_t need = plan.ws_bytes;
     IG_REQUIRE(c.ws && ws_bytes >= need, "%s: workspace of %zu bytes needed", fn, need);
     IG_REQUIRE(aligned16(c.ws), "%s: workspace must be 16-byte aligned", fn);

@@ -63,11 +63,13 @@ struct SpecPlan {
     int proj_blocks, splits, proj_wgs;  // projection workgroups: column blocks x splits of the D inputs
     bool bits;                        // the merge leaves bitmaps and a counter kernel applies them
     bool ok;                          // false: rows too long for the candidates to fit one merge
-    size_t off_arrive, off_pdone, off_part, off_cnt, off_key, off_idx, off_bits, off_flags, ws_bytes;
+    size_t off_status, off_arrive, off_pdone, off_part, off_cnt, off_key, off_idx, off_bits, off_flags, ws_bytes;
 };
 SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_lds_bytes(int n);
+void set_handover_test_mode(uint32_t spin_limit, int withhold);
+unsigned long long spec_shape_key(int B, int H, int D, int r);
 
 // kernel launchers (return hipError_t as int)
 int launch_rehearse(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,

@@ -80,7 +80,18 @@ struct SpecParams {
     // splits); row_wgs: the row workgroups; pdone [B*H]: slices of a row done reading its partial sums
     int proj_wgs, proj_blocks, row_wgs;
     uint32_t* pdone;
+    // workspace status word (sticky failure bits) and shape stamp (the (B, H, D, r) key of the calls the
+    // workspace serves; 0 until the first call claims it).  NULL: no checks (the standalone selection).
+    uint32_t* status;
+    unsigned long long* stamp;
+    unsigned long long key;
+    uint32_t spin_limit;  // polls of a row workgroup before it stops waiting for its partial query
+    int withhold;         // failure-path testing: the projection workgroups store no partial sums
 };
+
+// Sticky status bits of a speculation workspace (the public IG_WS_* values).
+constexpr uint32_t kWsTimeout = IG_WS_TIMEOUT;
+constexpr uint32_t kWsShape = IG_WS_SHAPE;
 
 // Fills the launch parameters of a speculation call (projection and row workgroups).
 int begin_speculate(const SpecCall& c, SpecParams* p);
@@ -116,7 +127,7 @@ constexpr int kProjTiles = 2;     // 16-column tiles per projection workgroup
 constexpr int kProjCols = 16 * kProjTiles;
 constexpr int kProjSlices = kSpecThreads / kWave / kProjTiles;  // input slices (one wave per tile and slice)
 constexpr int kProjLdsWords = kProjSlices * kProjTiles * 256;   // the slices' results (also the least `keys` size)
-constexpr uint32_t kProjSpinLimit = 1u << 22;  // polls before a row workgroup stops waiting
+constexpr uint32_t kProjSpinLimit = 1u << 22;  // default polls before a row workgroup stops waiting
 
 __device__ __forceinline__ void coherent_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -166,7 +177,7 @@ __device__ __forceinline__ void proj_role(const SpecParams& p, int pw, uint32_t*
         const int t = threadIdx.x;
         if (t < kProjTiles * 256) {
             const int tl = t / 256, row = (t / 16) % 16, c = blk * kProjCols + tl * 16 + t % 16;
-            if (b0 + row < B && c < N) {
+            if (b0 + row < B && c < N && !p.withhold) {
                 float v = 0.f;
 #pragma unroll
                 for (int sl = 0; sl < kProjSlices; ++sl) v += red[(sl * kProjTiles + tl) * 256 + row * 16 + t % 16];
@@ -178,12 +189,38 @@ __device__ __forceinline__ void proj_role(const SpecParams& p, int pw, uint32_t*
     }
 }
 
+// Admission of a row workgroup to the workspace (thread 0; the caller makes the result block-wide):
+// the status word must be clear (a failure of an earlier call poisons the workspace until it is
+// zero-filled again) and the shape stamp must be this call's key -- a zero stamp is claimed with a
+// compare-and-swap (the first call after the zero-fill).  A stamp of another shape sets kWsShape.
+// Returns true when the row may proceed.  Both words are read with device-coherent loads, issued
+// together.
+__device__ __forceinline__ bool ws_admit(const SpecParams& p) {
+    if (!p.status) return true;
+    const uint32_t st = __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long s = __hip_atomic_load(p.stamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (s == 0ull) {
+        unsigned long long e = 0ull;
+        __hip_atomic_compare_exchange_strong(p.stamp, &e, p.key, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        s = e == 0ull ? p.key : e;
+    }
+    if (s != p.key) {
+        atomicOr(p.status, kWsShape);
+        return false;
+    }
+    return st == 0u;
+}
+
 // Row workgroup: the partial query q[c] (c < R) of row b, columns [col0, col0 + R): poll the split
 // partials until every slot is filled, add them in a fixed order (thread (c, i) adds splits i, i + P,
 // .. in turn, then the P threads of column c are added by DPP; bias last), and return the slots to
-// empty.  Writes q (and q_out when not NULL); ends with a barrier.
+// empty.  Writes q (and q_out when not NULL); ends with a barrier.  Returns false (block-uniform) when
+// the row may not use the workspace (ws_admit) or when some slot is still empty after spin_limit
+// polls: then nothing is added and no slot is touched (a producer may still be about to store into
+// one), the timeout sets kWsTimeout, and the workspace stays unusable until it is zero-filled again.
 template <int R>
-__device__ __forceinline__ void wait_partial_query(const SpecParams& p, int b, int bh, int col0, float* q,
+__device__ __forceinline__ bool wait_partial_query(const SpecParams& p, int b, int bh, int col0, float* q,
                                                    float* q_out) {
     constexpr int P = kSpecThreads / R < 64 ? kSpecThreads / R : 64;  // threads per column
     const int tid = threadIdx.x;
@@ -191,6 +228,7 @@ __device__ __forceinline__ void wait_partial_query(const SpecParams& p, int b, i
     const int c = tid / P, i = tid % P;
     const int N = p.H * p.r;
     const bool sole = p.slices == 1;  // the only reader of these slots
+    if (__syncthreads_or(tid == 0 && !ws_admit(p))) return false;
     float acc = 0.f;
     for (int s0 = 0; s0 < p.splits; s0 += P) {
         const int s = s0 + i;
@@ -200,12 +238,21 @@ __device__ __forceinline__ void wait_partial_query(const SpecParams& p, int b, i
         uint32_t polls = 0;
         for (;;) {
             if (mine) v = coherent_load(src);
-            if (!__syncthreads_or(mine && __float_as_uint(v) == 0u) || ++polls >= kProjSpinLimit) break;
+            if (!__syncthreads_or(mine && __float_as_uint(v) == 0u)) break;
+            if (++polls >= p.spin_limit) {  // block-uniform: every thread counts the same polls
+                if (tid == 0 && p.status) atomicOr(p.status, kWsTimeout);
+                __syncthreads();
+                return false;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
-        if (mine) {
-            acc += v;
-            if (sole) coherent_store(src, 0.f);
+        // every slot of this round is filled: add them all at once, then return them to empty
+        if (mine) acc += v;
+    }
+    if (sole) {
+        for (int s0 = 0; s0 < p.splits; s0 += P) {
+            const int s = s0 + i;
+            if (on && s < p.splits) coherent_store(p.part + (static_cast<size_t>(s) * p.B + b) * N + col0 + c, 0.f);
         }
     }
     acc = group_sum<P>(acc);
@@ -227,6 +274,7 @@ __device__ __forceinline__ void wait_partial_query(const SpecParams& p, int b, i
         }
     }
     __syncthreads();
+    return true;
 }
 
 // (b, h) of a row workgroup index: with xcd_heads, groups of adjacent heads go to one XCD with all
@@ -244,6 +292,9 @@ __device__ __forceinline__ void spec_bh(const SpecParams& p, int row_wg, int* b,
         *h = row_wg - *b * p.H;
     }
 }
+
+__device__ __forceinline__ void seq_arrive(const SpecParams& p, int b, bool sat, uint32_t* lds, SelScratch& sh,
+                                           int& s_last);
 
 // Row index of key j for a whole row (the key's own position).
 struct IdentityIdx {
@@ -385,25 +436,52 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
             }
         }
         }
-        sat = __syncthreads_or(sat);
-        // Every counter atomic of this workgroup has returned (its value was used) before the barrier,
-        // so it is performed before thread 0's arrival atomic below; atomics are coherent across XCDs,
-        // so no fence (an agent-scope fence writes back the XCD's whole L2) is needed.  One word per
-        // sequence carries the arrivals (high half) and the workgroups that saw a saturation (low half).
-        if (tid == 0) {
-            const uint32_t old = atomicAdd(&p.arrive[b], 0x10000u + (sat ? 1u : 0u));
-            const bool last = (old >> 16) == static_cast<uint32_t>(p.H - 1);
-            s_last = last ? (1 + (((old & 0xFFFFu) + (sat ? 1u : 0u)) != 0u ? 1 : 0)) : 0;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        const bool halve = s_last == 2;
-        const int v = pool_finish<kSpecThreads>(crow, n, cmax, halve, p.victim != nullptr, lds, &sh.wtot[0]);
-        if (tid == 0) {
-            if (p.victim) p.victim[b] = v;
-            __hip_atomic_store(&p.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        seq_arrive(p, b, __syncthreads_or(sat) != 0, lds, sh, s_last);
     }
+}
+
+// The arrival of a row of sequence b after its counter updates (sat: some increment of this workgroup
+// reached cmax).  Every counter atomic of this workgroup has returned (its value was used) before the
+// barrier inside __syncthreads_or that produced `sat`, so it is performed before thread 0's arrival
+// atomic below; atomics are coherent across XCDs, so no fence (an agent-scope fence writes back the
+// XCD's whole L2) is needed.  One word per sequence carries the arrivals (high half) and the workgroups
+// that saw a saturation (low half); the last of the H rows halves the sequence's counters if any row
+// saturated, picks the victim and returns the word to zero.
+__device__ __forceinline__ void seq_arrive(const SpecParams& p, int b, bool sat, uint32_t* lds, SelScratch& sh,
+                                           int& s_last) {
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        const uint32_t old = atomicAdd(&p.arrive[b], 0x10000u + (sat ? 1u : 0u));
+        const bool last = (old >> 16) == static_cast<uint32_t>(p.H - 1);
+        s_last = last ? (1 + (((old & 0xFFFFu) + (sat ? 1u : 0u)) != 0u ? 1 : 0)) : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const bool halve = s_last == 2;
+    uint32_t* crow = p.counters + static_cast<size_t>(b) * p.n_cap;
+    const int v = pool_finish<kSpecThreads>(crow, p.n, p.cmax, halve, p.victim != nullptr, lds, &sh.wtot[0]);
+    if (tid == 0) {
+        if (p.victim) p.victim[b] = v;
+        __hip_atomic_store(&p.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// A whole row (or a merged row) that could not be computed: count = -1 marks it; its counters are not
+// touched, but the row still arrives so that the sequence's last row finishes as usual (with bitmaps,
+// the row's bitmap is all zero instead).
+__device__ __forceinline__ void spec_fail_row(const SpecParams& p, int b, int bh, uint32_t* lds, SelScratch& sh,
+                                              int& s_last) {
+    const int tid = threadIdx.x;
+    if (tid == 0) p.count[bh] = -1;
+    if (!p.counters) return;
+    if (p.bits) {
+        const int nw = (p.n + 31) / 32;
+        uint32_t* dst = p.bits + static_cast<size_t>(bh) * nw;
+        for (int i = tid; i < nw; i += kSpecThreads) dst[i] = 0u;
+        return;
+    }
+    __syncthreads();
+    seq_arrive(p, b, false, lds, sh, s_last);
 }
 
 // Row workgroup wg of the speculation launch (counted from the first row workgroup): one (b, h) row,
@@ -442,7 +520,15 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
         }
     }
     float* q_out = (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr;
-    wait_partial_query<R>(p, b, bh, h * R, s_q, q_out);
+    if (!wait_partial_query<R>(p, b, bh, h * R, s_q, q_out)) {
+        // no partial query: a slice marks its candidates invalid for the merge, a whole row fails
+        if (p.slices > 1) {
+            if (tid == 0) p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = -1;
+        } else {
+            spec_fail_row(p, b, bh, keys, sh, sm.last);
+        }
+        return;
+    }
     if constexpr (!PRE) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -516,6 +602,12 @@ __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t
     const uint32_t* ck = p.cand_key + base;
     const int32_t* ci = p.cand_idx + base;
     auto gidx = [&](int j) { return static_cast<int>(ci[j]); };
+    // a slice that could not compute its scores marks its count -1: the row fails
+    const int32_t* cc = p.cand_cnt + static_cast<size_t>(bh) * p.slices;
+    if (__syncthreads_or(tid < p.slices && cc[tid] < 0)) {
+        spec_fail_row(p, b, bh, keys, sh, sm.last);
+        return;
+    }
     fast_sel_init(fs);
     uint32_t kmax = 0;
     constexpr int U = 8;  // loads per lane in flight

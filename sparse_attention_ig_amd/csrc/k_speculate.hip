@@ -74,8 +74,9 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     sp.proj_blocks = (H * r + kProjCols - 1) / kProjCols;
     sp.splits = (D + kProjSplit - 1) / kProjSplit;
     sp.proj_wgs = sp.proj_blocks * sp.splits;
-    sp.off_arrive = 0;
-    sp.off_pdone = align256(static_cast<size_t>(B) * sizeof(uint32_t));
+    sp.off_status = 0;  // status word at 0, shape stamp at 8 (one 256-byte region)
+    sp.off_arrive = 256;
+    sp.off_pdone = sp.off_arrive + align256(static_cast<size_t>(B) * sizeof(uint32_t));
     sp.off_part = sp.off_pdone + align256(static_cast<size_t>(rows) * sizeof(uint32_t));
     sp.off_cnt = sp.off_part + align256(static_cast<size_t>(sp.splits) * B * H * r * sizeof(float));
     sp.off_key = sp.off_cnt + (S > 1 ? align256(static_cast<size_t>(rows) * S * sizeof(int32_t)) : 0);
@@ -143,6 +144,22 @@ int launch_spec_merge(const SpecParams& p, hipStream_t s) {
     return static_cast<int>(hipGetLastError());
 }
 
+// Failure-path testing (ig_set_handover_test_mode): the row workgroups' poll limit, and whether the
+// projection workgroups withhold their partial sums.  Process-wide; read when a call is launched.
+static uint32_t g_spin_limit = kProjSpinLimit;
+static int g_withhold = 0;
+
+void set_handover_test_mode(uint32_t spin_limit, int withhold) {
+    g_spin_limit = spin_limit ? spin_limit : kProjSpinLimit;
+    g_withhold = withhold ? 1 : 0;
+}
+
+unsigned long long spec_shape_key(int B, int H, int D, int r) {
+    // B < 2^16, H < 2^16, D < 2^22, r <= 256 (checked by the callers); the top bit keeps it nonzero
+    return (1ull << 63) | (static_cast<unsigned long long>(B) << 47) | (static_cast<unsigned long long>(H) << 31) |
+           (static_cast<unsigned long long>(D) << 9) | static_cast<unsigned long long>(r - 1);
+}
+
 int begin_speculate(const SpecCall& c, SpecParams* p) {
     const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
     char* ws = static_cast<char*>(c.ws);
@@ -158,6 +175,11 @@ int begin_speculate(const SpecCall& c, SpecParams* p) {
     p->proj_blocks = sp.proj_blocks;
     p->row_wgs = c.B * c.H * sp.slices;
     p->pdone = reinterpret_cast<uint32_t*>(ws + sp.off_pdone);
+    p->status = reinterpret_cast<uint32_t*>(ws + sp.off_status);
+    p->stamp = reinterpret_cast<unsigned long long*>(ws + sp.off_status + 8);
+    p->key = spec_shape_key(c.B, c.H, c.D, c.r);
+    p->spin_limit = g_spin_limit;
+    p->withhold = g_withhold;
     return 0;
 }
 

@@ -57,6 +57,17 @@ def ulp_mismatch(a: np.ndarray, b: np.ndarray) -> int:
                                 != b.view(np.uint32 if b.dtype == np.float32 else np.uint16)))
 
 
+def assert_setup_routes_agree(a: Inputs, b: Inputs) -> Dict[str, int]:
+    """The two setup routes give the same channel sets, x and V bit for bit, and the rotated K, q and
+    Wq_part bit for bit up to a handful of elements (a float64 rotation by the Jacobi and by the LAPACK
+    SVD may round an element to the neighbouring bfloat16 value); returns the mismatch counts."""
+    mism = compare_inputs(a, b)
+    assert mism["chan"] == 0 and mism["x"] == 0 and mism["V"] == 0, mism
+    total = a.K.size + a.q.size + a.Wq_part.size
+    assert mism["K"] + mism["q"] + mism["Wq_part"] <= max(2, total * 1e-5), mism
+    return mism
+
+
 def compare_inputs(a: Inputs, b: Inputs) -> Dict[str, int]:
     """Setup parity: bits of every derived input, and the channel sets."""
     return {
@@ -93,18 +104,50 @@ def oracle_step(inp: Inputs, *, mode: str, alpha: float = math.inf, k: int = 0, 
             C2, v = O.pool_touch(counters, idx, cnt, s.n, cmax, want_victim)
             res.update(counters=C2, victim=v)
         return res
+    return oracle_heads(inp, mode=mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out, heads=heads)[0]
+
+
+def oracle_heads(inp: Inputs, *, mode: str, alpha: float = math.inf, k: int = 0, max_sel: int = 0,
+                 max_out: int = 0, n: Optional[int] = None, x_bits=None, heads=None, attn: bool = True,
+                 Kp=None, q_layer: Optional[Inputs] = None):
+    """The oracle's layer-step one (b, h) at a time, decoding only that head's rows (the whole cache in
+    float64 would not fit at the long-context sizes): partial query, scores, selection and (attn) the
+    attention over the selected rows.  ``heads``: list of (b, h), default every head; ``x_bits``: the
+    attention input driving the speculation (default the layer's own x); ``n``: rows (default the
+    spec's); ``Kp``: partial key cache bits (default the layer's); ``q_layer``: the layer whose query,
+    K and V the attention uses (default ``inp``).  Returns (records per (b, h), idx [B][H][cap]
+    ascending, count [B][H]) -- the last two for the counters of every head."""
+    from oracle import oracle as O
+    s = inp.spec
+    dt = s.dtype
+    n = s.n if n is None else n
+    x = O.decode(inp.x if x_bits is None else x_bits, dt)
+    Wp = O.decode(inp.Wq_part, dt)
+    if Kp is None:
+        Kp = inp.extra.get("Kp")
+        if Kp is None:
+            Kp = O.partial_key_cache(inp.K, inp.chan)
+    ql = inp if q_layer is None else q_layer
+    if heads is None:
+        heads = [(b, h) for b in range(s.B) for h in range(s.H)]
+    cap = max_out if max_out > 0 else n
+    idx_all = np.zeros((s.B, s.H, cap), dtype=np.int32)
+    cnt_all = np.zeros((s.B, s.H), dtype=np.int32)
     out = {}
     for (b, h) in heads:
-        sub_x = x[b:b + 1]
-        qp, sc = O.rehearse(sub_x, Wp[:, h * s.r:(h + 1) * s.r], O.decode(Kp[b:b + 1, h:h + 1], dt), s.n, 1, s.r,
-                            s.softmax_scale)
+        qp, sc = O.rehearse(x[b:b + 1], Wp[:, h * s.r:(h + 1) * s.r], O.decode(Kp[b:b + 1, h:h + 1, :n], dt), n, 1,
+                            s.r, s.softmax_scale)
         idx, cnt = _oracle_select(sc, mode, alpha, k, max_sel, max_out)
         c = int(cnt[0, 0])
         rows = idx[0, 0, :c].astype(np.int64)
-        o, lse = O.attention_rows(O.decode(inp.q[b, h], dt), O.decode(inp.K[b, h, rows], dt),
-                                  O.decode(inp.V[b, h, rows], dt), s.softmax_scale)
-        out[(b, h)] = dict(q_part=qp[0, 0], scores=sc[0, 0], idx=rows, out=o, lse=lse)
-    return out
+        rec = dict(q_part=qp[0, 0], scores=sc[0, 0], idx=rows)
+        if attn:
+            rec["out"], rec["lse"] = O.attention_rows(O.decode(ql.q[b, h], dt), O.decode(ql.K[b, h, rows], dt),
+                                                      O.decode(ql.V[b, h, rows], dt), s.softmax_scale)
+        out[(b, h)] = rec
+        idx_all[b, h, :c] = rows
+        cnt_all[b, h] = c
+    return out, idx_all, cnt_all
 
 
 def _oracle_select(sc, mode, alpha, k, max_sel, max_out):
@@ -132,6 +175,60 @@ def cut_of(ref_scores: np.ndarray, ref_sel: np.ndarray, mode: str, alpha: float)
         if kept_all == len(ref_sel):
             return cut
     return float(ref_scores[ref_sel].min()) if len(ref_sel) else math.inf
+
+
+def check_heads(g_idx, g_cnt, ref: dict, mode: str, alpha: float, g_q_part=None, g_scores=None, g_out=None,
+                g_lse=None, tol: Optional[float] = None, n: Optional[int] = None):
+    """Every (b, h) of ``ref`` (oracle_heads records) against the GPU's arrays: q_part and scores within
+    1e-3 row-normwise, the index set equal outside the 1e-4 band (ascending, distinct), and where the
+    sets are equal the attention within ``tol``.  Returns the heads whose sets differ inside the band."""
+    inexact = []
+    for (b, h), r in ref.items():
+        if g_q_part is not None:
+            assert score_error(g_q_part[b, h], r["q_part"]) <= SCORE_RTOL, ("q_part", b, h)
+        if g_scores is not None:
+            sc = g_scores[b, h, :len(r["scores"])]
+            assert score_error(sc, r["scores"]) <= SCORE_RTOL, ("scores", b, h)
+        gs = g_idx[b, h, :g_cnt[b, h]]
+        assert np.all(np.diff(gs) > 0), ("not ascending", b, h)
+        ok, exact, band = compare_sets(gs, r["idx"], r["scores"], mode, alpha)
+        assert ok, ("set", b, h, sorted(set(gs.tolist()) ^ set(r["idx"].tolist())))
+        if not exact:
+            inexact.append((b, h))
+            continue
+        if g_out is not None and "out" in r:
+            err = np.abs(g_out[b, h] - r["out"]).max()
+            assert err <= tol, ("attention", b, h, err)
+            if g_lse is not None:
+                assert abs(g_lse[b, h] - r["lse"]) <= max(tol, 1e-5 * abs(r["lse"])), ("lse", b, h)
+    return inexact
+
+
+def check_counters(g_C, ref_C, g_idx, g_cnt, ref_idx, ref_cnt, n: int, g_victim=None, ref_victim=None):
+    """Counters slot by slot.  A head whose set differs from the oracle's inside the 1e-4 band moves the
+    counters of exactly those slots, by at most the number of such heads: every other slot must be equal,
+    and the victim too where no slot moved.  (No halving may differ: callers keep counters below cmax.)
+    Returns the sequences with moved slots."""
+    B = g_C.shape[0]
+    H = g_cnt.shape[1]
+    moved = []
+    for b in range(B):
+        diff = np.zeros(n, dtype=np.int64)
+        for h in range(H):
+            gs = set(int(v) for v in g_idx[b, h, :g_cnt[b, h]])
+            rs = set(int(v) for v in ref_idx[b, h, :ref_cnt[b, h]])
+            for j in gs ^ rs:
+                diff[j] += 1
+        free = diff == 0
+        assert np.array_equal(g_C[b, n:], ref_C[b, n:]), ("counters past n", b)
+        assert np.array_equal(g_C[b, :n][free], ref_C[b, :n][free]), ("counters", b)
+        gd = np.abs(g_C[b, :n].astype(np.int64) - ref_C[b, :n].astype(np.int64))
+        assert (gd[~free] <= diff[~free]).all(), ("counters in the band", b)
+        if (~free).any():
+            moved.append(b)
+        elif g_victim is not None:
+            assert g_victim[b] == ref_victim[b], ("victim", b)
+    return moved
 
 
 def band_rows(ref_scores: np.ndarray, cut: float) -> np.ndarray:

@@ -1,14 +1,19 @@
-"""GPU parity at the full sizes the benchmarks time, on sampled heads (the oracle computes those heads
-one by one on its own inputs):
+"""GPU parity at the full sizes the benchmarks time, on every (b, h) head (the oracle computes each head
+on its own, decoding only that head's rows):
 
   * the 40-layer Llama-2-13B pipeline's layer pair (B16 H40 d128 D5120 r32, n = 4096, top 5%): layer 0
     dense attention, layer 0's ig_decode_layer (the projection and speculation for layer 1 beside
-    layer 0's attention, one launch), layer 1's attention over the speculated rows;
-  * the OPT-30B pinned host pool (B16 H56 d128 D7168 r32, n = 2048 of 4096 slots, alpha 5, 20% cap),
-    with bf16 rows and with INT4 records: speculation in HBM, zero-copy gather, attention;
-  * the long-context Llama-2-7B layer at its largest benchmark size (B4, n = 131072, top 4%).
+    layer 0's attention, one launch), layer 1's attention over the speculated rows, layer 1's counters;
+  * the OPT-30B pinned host pool (B16 H56 d128 D7168 r32, alpha 5, 20% cap, 4096 slots), with bf16
+    rows and with INT4 records, at the sampled layers {0, 1, 24, 47} and the sampled steps of the growth
+    from 2048 to 4096 rows {first, middle, last} = n in {2048, 3072, 4096} (the first n rows of one
+    4096-row draw per layer; counters accumulate over the three steps): speculation in HBM, zero-copy
+    gather, attention;
+  * the long-context Llama-2-7B layer at its largest size (B4, n = 131072, top 4%, the benchmark's
+    workload).
 
-Selections must match outside the 1e-4 band; attention within 1e-2 (bf16) where the sets are equal.
+Selections must match outside the 1e-4 band; attention within 1e-2 (bf16) where the sets are equal;
+counters slot by slot (only slots of band-differing heads may move, by at most that many).
 """
 import math
 
@@ -33,18 +38,7 @@ def gpu():
     yield
 
 
-def _spec_head(ins, x_bits, b, h, n, mode, **kw):
-    """Oracle speculation for head (b, h) of the layer `ins` from the attention input x_bits[b]."""
-    s = ins.spec
-    dt = s.dtype
-    Wp = O.decode(ins.Wq_part, dt)[:, h * s.r:(h + 1) * s.r]
-    Kp = O.decode(ins.extra["Kp"][b:b + 1, h:h + 1], dt)
-    _, sc = O.rehearse(O.decode(x_bits[b:b + 1], dt), Wp, Kp, n, 1, s.r, s.softmax_scale)
-    idx, cnt = O.select(sc, mode, **kw)
-    return sc[0, 0], idx[0, 0, :cnt[0, 0]].astype(np.int64)
-
-
-def test_pipeline_layer_pair_full_size_sampled():
+def test_pipeline_layer_pair_full_size():
     import torch
     from sparse_attention_ig_amd.pipeline import DecodePipeline
     from sparse_attention_ig_amd.runtime import to_device
@@ -54,7 +48,7 @@ def test_pipeline_layer_pair_full_size_sampled():
     xs, lib_in, _ = harness.pipeline_setup(spec, 2, 1, harness.lib_inputs)
     _, ora_in, _ = harness.pipeline_setup(spec, 2, 1, harness.oracle_inputs)
     for a, b in zip(lib_in, ora_in):
-        assert harness.compare_inputs(a, b)["chan"] == 0
+        harness.assert_setup_routes_agree(a, b)
     pipe = DecodePipeline(lib_in, max_out=max_out)
     k = pipe.topk()
     pipe.step([to_device(xs[0, l]) for l in range(2)], append=False)
@@ -62,82 +56,95 @@ def test_pipeline_layer_pair_full_size_sampled():
     say("[full pipeline] gpu step done")
     out0, out1 = host(pipe.layers[0].out), host(pipe.layers[1].out)
     gi, gc = host(pipe.layers[1].idx), host(pipe.layers[1].count)
+    gC = host(pipe.layers[1].counters).view(np.uint32)
     dt = spec.dtype
     tol = harness.ATTN_TOL[dt]
-    exact_heads = 0
-    for (b, h) in [(0, 0), (7, 13), (15, 39)]:
-        L0 = ora_in[0]
-        o, _ = O.attention_rows(O.decode(L0.q[b, h], dt), O.decode(L0.K[b, h, :spec.n], dt),
-                                O.decode(L0.V[b, h, :spec.n], dt), spec.softmax_scale)
-        assert np.abs(out0[b, h] - o).max() <= tol, ("layer 0", b, h)
-        sc, rows = _spec_head(ora_in[1], xs[0, 0], b, h, spec.n, "topk", k=k, max_out=max_out)
-        ok, exact, _ = harness.compare_sets(gi[b, h, :gc[b, h]], rows, sc, "topk", 0.0)
-        assert ok and gc[b, h] == len(rows), ("layer 1 set", b, h)
-        if exact:
-            exact_heads += 1
-            L1 = ora_in[1]
-            o, _ = O.attention_rows(O.decode(L1.q[b, h], dt), O.decode(L1.K[b, h, rows], dt),
-                                    O.decode(L1.V[b, h, rows], dt), spec.softmax_scale)
-            assert np.abs(out1[b, h] - o).max() <= tol, ("layer 1", b, h)
-    assert exact_heads >= 1
+    L0 = ora_in[0]
+    for b in range(spec.B):
+        for h in range(spec.H):
+            o, _ = O.attention_rows(O.decode(L0.q[b, h], dt), O.decode(L0.K[b, h, :spec.n], dt),
+                                    O.decode(L0.V[b, h, :spec.n], dt), spec.softmax_scale)
+            assert np.abs(out0[b, h] - o).max() <= tol, ("layer 0", b, h)
+    say("[full pipeline] layer 0 dense attention: every head within tolerance")
+    ref, ri, rc = harness.oracle_heads(ora_in[1], mode="topk", k=k, max_out=max_out, x_bits=xs[0, 0])
+    inexact = harness.check_heads(gi, gc, ref, "topk", 0.0, g_out=out1, tol=tol)
+    assert len(inexact) <= spec.B * spec.H // 50, inexact
+    rC, _ = O.pool_touch(np.zeros((spec.B, spec.cap), np.uint32), ri, rc, spec.n, 65535)
+    moved = harness.check_counters(gC, rC, gi, gc, ri, rc, spec.n)
+    say(f"[full pipeline] layer 1: {spec.B * spec.H} heads checked, {len(inexact)} band-affected, "
+        f"counters moved in {len(moved)} sequences")
 
 
-@pytest.mark.parametrize("int4", [False, True], ids=["bf16-rows", "int4-records"])
-def test_pool_full_size_sampled(int4):
+@pytest.mark.parametrize("layer", [0, 1, 24, 47])
+def test_pool_full_size_sampled_layers_and_steps(layer):
     import torch
     from sparse_attention_ig_amd.runtime import PoolLayer
-    spec = gen.opt_30b(n=2048, B=16, n_cap=4096)
-    say(f"[full pool int4={int4}] B={spec.B} H={spec.H} n={spec.n} cap={spec.cap}")
-    li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
-    assert harness.compare_inputs(li, oi)["chan"] == 0
-    lay = PoolLayer(li, max_out=spec.max_sel, int4=int4)
-    lay.speculate(alpha=spec.alpha, max_sel=spec.max_sel)
-    lay.gather()
-    lay.attend()
-    torch.cuda.synchronize()
-    say("[full pool] gpu step done")
-    gi, gc, out = host(lay.idx), host(lay.count), host(lay.out)
+    spec = gen.opt_30b(n=4096, B=16, n_cap=4096)
+    say(f"[full pool layer {layer}] B={spec.B} H={spec.H} cap={spec.cap}: setup")
+    lay = gen.draw_layer(spec, layer, with_wk=False)
+    li, oi = harness.lib_inputs(spec, layer, lay=lay), harness.oracle_inputs(spec, layer, lay=lay)
+    harness.assert_setup_routes_agree(li, oi)
+    max_out = spec.max_sel                    # 20% of the largest n
+    pools = {"bf16": PoolLayer(li, max_out=max_out), "int4": PoolLayer(li, max_out=max_out, int4=True)}
     dt = spec.dtype
-    exact_heads = 0
-    for (b, h) in [(0, 0), (9, 27), (15, 55)]:
-        sc, rows = _spec_head(oi, oi.x, b, h, spec.n, "threshold", alpha=spec.alpha, max_sel=spec.max_sel,
-                              max_out=spec.max_sel)
-        ok, exact, _ = harness.compare_sets(gi[b, h, :gc[b, h]], rows, sc, "threshold", spec.alpha)
-        assert ok, (b, h)
-        if not exact:
-            continue
-        exact_heads += 1
-        K, V = oi.K[b, h, rows], oi.V[b, h, rows]
-        if int4:
-            K = O.store(O.dequantize_int4(*O.quantize_int4(K, dt)), dt)
-            V = O.store(O.dequantize_int4(*O.quantize_int4(V, dt)), dt)
-        o, _ = O.attention_rows(O.decode(oi.q[b, h], dt), O.decode(K, dt), O.decode(V, dt), spec.softmax_scale)
-        assert np.abs(out[b, h] - o).max() <= harness.ATTN_TOL[dt], (b, h)
-    assert exact_heads >= 1
+    tol = harness.ATTN_TOL[dt]
+    rC = np.zeros((spec.B, spec.cap), np.uint32)
+    diverged = set()
+    for n in (2048, 3072, 4096):
+        max_sel = max(1, int(math.floor(0.2 * n)))
+        for kind, pool in pools.items():
+            pool.speculate(alpha=spec.alpha, max_sel=max_sel, n=n, want_victim=True)
+            pool.gather()
+            pool.attend()
+        torch.cuda.synchronize()
+        say(f"[full pool layer {layer}] n={n} gpu done")
+        ref, ri, rc = harness.oracle_heads(oi, mode="threshold", alpha=spec.alpha, max_sel=max_sel, max_out=max_out,
+                                           n=n, attn=False)
+        rC, rv = O.pool_touch(rC, ri, rc, n, 65535, want_victim=True)
+        for kind, pool in pools.items():
+            gi, gc, out = host(pool.idx), host(pool.count), host(pool.out)
+            inexact = harness.check_heads(gi, gc, ref, "threshold", spec.alpha)
+            assert len(inexact) <= spec.B * spec.H // 50, (kind, inexact)
+            for (b, h), r in ref.items():
+                if (b, h) in inexact:
+                    continue
+                rows = r["idx"]
+                K, V = oi.K[b, h, rows], oi.V[b, h, rows]
+                if kind == "int4":
+                    K = O.store(O.dequantize_int4(*O.quantize_int4(K, dt)), dt)
+                    V = O.store(O.dequantize_int4(*O.quantize_int4(V, dt)), dt)
+                o, _ = O.attention_rows(O.decode(oi.q[b, h], dt), O.decode(K, dt), O.decode(V, dt),
+                                        spec.softmax_scale)
+                assert np.abs(out[b, h] - o).max() <= tol, (kind, n, b, h)
+            gC = host(pool.counters).view(np.uint32)
+            keep = [b for b in range(spec.B) if b not in diverged]
+            moved = harness.check_counters(gC[keep], rC[keep], gi[keep], gc[keep], ri[keep], rc[keep], n,
+                                           host(pool.victim)[keep], rv[keep])
+            diverged.update(keep[i] for i in moved)
+            say(f"[full pool layer {layer}] n={n} {kind}: {spec.B * spec.H} heads, {len(inexact)} band-affected, "
+                f"mean count {gc.mean():.1f}")
+    assert len(diverged) <= 2, diverged
 
 
-def test_long_context_b4_full_size_sampled():
+def test_long_context_b4_full_size():
     """Llama-2-7B-shaped layer at 131072 rows, batch 4, top 4% (5243 rows per head), the fused path:
-    the projection workgroups, 4 slices of 32768 rows per row, a merge of 20972 candidates per row; then the
-    attention split over the selected rows.  Sampled heads against the oracle, every head's counters."""
+    the projection workgroups, 4 slices of 32768 rows per row, a merge of the slices' candidates per row,
+    counters from the rows' bitmaps; then the attention split over the selected rows.  Every head
+    against the oracle, counters slot by slot."""
     from sparse_attention_ig_amd.runtime import DeviceLayer
     from tests.gpu_util import to_host
     spec = gen.llama2_7b_long(n=131072, B=4, frac=0.04)
     say(f"[long b4 full] n={spec.n} k={spec.topk}")
     li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
-    assert harness.compare_inputs(li, oi)["chan"] == 0
+    harness.assert_setup_routes_agree(li, oi)
     layer = DeviceLayer(li, max_out=spec.topk)
-    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, parts=DeviceLayer.FUSED))
+    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, want_victim=True, parts=DeviceLayer.FUSED))
     say("[long b4 full] gpu step done")
-    heads = [(0, 0), (1, 17), (3, 31)]
-    ref = harness.oracle_step(oi, mode="topk", k=spec.topk, max_out=spec.topk, heads=heads)
-    exact_heads = 0
-    for (b, h), r in ref.items():
-        assert harness.score_error(g["scores"][b, h, :spec.n], r["scores"]) <= harness.SCORE_RTOL
-        ok, exact, _ = harness.compare_sets(g["idx"][b, h, :g["count"][b, h]], r["idx"], r["scores"], "topk", 0.0)
-        assert ok and g["count"][b, h] == len(r["idx"]), (b, h)
-        if exact:
-            exact_heads += 1
-            assert np.abs(g["out"][b, h] - r["out"]).max() <= harness.ATTN_TOL["bf16"], (b, h)
-    assert exact_heads >= 1
-    assert int(g["counters"].sum()) == spec.B * spec.H * spec.topk
+    ref, ri, rc = harness.oracle_heads(oi, mode="topk", k=spec.topk, max_out=spec.topk)
+    inexact = harness.check_heads(g["idx"], g["count"], ref, "topk", 0.0, g_q_part=g["q_part"], g_scores=g["scores"],
+                                  g_out=g["out"], g_lse=g["lse"], tol=harness.ATTN_TOL["bf16"])
+    assert len(inexact) <= 3, inexact
+    assert (g["count"] == spec.topk).all()
+    rC, rv = O.pool_touch(np.zeros((spec.B, spec.cap), np.uint32), ri, rc, spec.n, 65535, want_victim=True)
+    moved = harness.check_counters(g["counters"], rC, g["idx"], g["count"], ri, rc, spec.n, g["victim"], rv)
+    say(f"[long b4 full] {spec.B * spec.H} heads, {len(inexact)} band-affected, counters moved in {len(moved)}")

@@ -84,8 +84,7 @@ def check_step(name, spec, mode, kw, lib_in=None, ora_in=None, path="unfused"):
     say(f"[case {name}] {path} B={spec.B} H={spec.H} d={spec.d} n={spec.n} r={spec.r} {spec.dtype} mode={mode} {kw}")
     lib_in = lib_in or harness.lib_inputs(spec)
     ora_in = ora_in or harness.oracle_inputs(spec)
-    mism = harness.compare_inputs(lib_in, ora_in)
-    assert mism["chan"] == 0, mism
+    harness.assert_setup_routes_agree(lib_in, ora_in)
     cmax = kw.get("cmax", 65535)
     C0 = gen.draw_counters(spec, cmax) if kw.get("counters") == "random" else np.zeros((spec.B, spec.cap), np.uint32)
     max_out = _max_out(spec, mode, kw)
@@ -99,8 +98,10 @@ def check_step(name, spec, mode, kw, lib_in=None, ora_in=None, path="unfused"):
     g = to_host(layer.step(mode=mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out, cmax=cmax,
                            want_victim=want_victim, parts=parts))
     if path == "fused":
-        # the arrival words (the first B words of the workspace) are back to zero
-        assert not host(layer.ws_spec)[:4 * spec.B].any(), "arrival words must return to zero"
+        # the arrival words (B words from byte 256 of the workspace) are back to zero, the status is clear
+        from sparse_attention_ig_amd import _lib as L
+        assert not host(layer.ws_spec)[256:256 + 4 * spec.B].any(), "arrival words must return to zero"
+        assert L.ig_workspace_status(layer.ws_spec) == 0
     say(f"[case {name}] gpu step done")
     ref = harness.oracle_step(ora_in, mode=mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out, cmax=cmax,
                               counters=C0, want_victim=want_victim)
@@ -310,29 +311,25 @@ def test_determinism():
 
 
 @pytest.mark.parametrize("path", ["unfused", "fused"])
-def test_long_context_full_size_sampled(path):
-    """Llama-2-7B-shaped layer at 131072 rows, top 1%: every head's scores and the sampled heads'
-    selection and attention against the oracle.  The fused speculation cuts each row into slices
-    (one workgroup each, candidates merged per row)."""
+def test_long_context_full_size(path):
+    """Llama-2-7B-shaped layer at 131072 rows, top 1%: every head's scores, selection and attention
+    against the oracle, counters slot by slot.  The fused speculation cuts each row into slices (one
+    workgroup each, candidates merged per row)."""
     spec = gen.llama2_7b_long(n=131072, B=1, frac=0.01)
     say(f"[long full {path}] n={spec.n} k={spec.topk}")
     li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
-    assert harness.compare_inputs(li, oi)["chan"] == 0
+    harness.assert_setup_routes_agree(li, oi)
     layer = DeviceLayer(li, max_out=spec.topk)
     parts = DeviceLayer.FUSED if path == "fused" else DeviceLayer.PARTS
-    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, parts=parts))
+    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, want_victim=True, parts=parts))
     say("[long full] gpu step done")
-    heads = [(0, 0), (0, 13), (0, 31)]
-    ref = harness.oracle_step(oi, mode="topk", k=spec.topk, max_out=spec.topk, heads=heads)
-    for (b, h), r in ref.items():
-        assert harness.score_error(g["scores"][b, h], r["scores"]) <= harness.SCORE_RTOL
-        gs = g["idx"][b, h, :g["count"][b, h]]
-        ok, exact, band = harness.compare_sets(gs, r["idx"], r["scores"], "topk", 0.0)
-        assert ok and g["count"][b, h] == len(r["idx"])
-        if exact:
-            assert np.abs(g["out"][b, h] - r["out"]).max() <= harness.ATTN_TOL["bf16"]
-    # counters: each head adds exactly k increments
-    assert int(g["counters"].sum()) == spec.H * spec.topk
+    ref, ri, rc = harness.oracle_heads(oi, mode="topk", k=spec.topk, max_out=spec.topk)
+    inexact = harness.check_heads(g["idx"], g["count"], ref, "topk", 0.0, g_q_part=g["q_part"], g_scores=g["scores"],
+                                  g_out=g["out"], g_lse=g["lse"], tol=harness.ATTN_TOL["bf16"])
+    assert len(inexact) <= 1, inexact
+    assert (g["count"] == spec.topk).all()
+    rC, rv = O.pool_touch(np.zeros((spec.B, spec.cap), np.uint32), ri, rc, spec.n, 65535, want_victim=True)
+    harness.check_counters(g["counters"], rC, g["idx"], g["count"], ri, rc, spec.n, g["victim"], rv)
 
 
 def test_graph_replay_matches_eager():
@@ -370,23 +367,19 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(got["idx"], eager["idx"]), rep
 
 
-def test_long_context_32k_fused_sampled():
-    """Llama-2-7B-shaped layer at 32768 rows (the fused path's LDS limit), batch 4, top 4%: sampled
-    heads' selection and attention against the oracle, every head's counters summed."""
+def test_long_context_32k_fused():
+    """Llama-2-7B-shaped layer at 32768 rows (the fused path's LDS limit), batch 4, top 4%: every head's
+    scores, selection and attention against the oracle, counters slot by slot."""
     spec = gen.llama2_7b_long(n=32768, B=4, frac=0.04)
     say(f"[long 32k fused] n={spec.n} k={spec.topk}")
     li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
-    assert harness.compare_inputs(li, oi)["chan"] == 0
+    harness.assert_setup_routes_agree(li, oi)
     layer = DeviceLayer(li, max_out=spec.topk)
-    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, parts=DeviceLayer.FUSED))
+    g = to_host(layer.step(mode="topk", k=spec.topk, max_out=spec.topk, want_victim=True, parts=DeviceLayer.FUSED))
     say("[long 32k fused] gpu step done")
-    heads = [(0, 0), (1, 17), (3, 31)]
-    ref = harness.oracle_step(oi, mode="topk", k=spec.topk, max_out=spec.topk, heads=heads)
-    for (b, h), r in ref.items():
-        assert harness.score_error(g["scores"][b, h, :spec.n], r["scores"]) <= harness.SCORE_RTOL
-        gs = g["idx"][b, h, :g["count"][b, h]]
-        ok, exact, band = harness.compare_sets(gs, r["idx"], r["scores"], "topk", 0.0)
-        assert ok and g["count"][b, h] == len(r["idx"])
-        if exact:
-            assert np.abs(g["out"][b, h] - r["out"]).max() <= harness.ATTN_TOL["bf16"]
-    assert int(g["counters"].sum()) == spec.B * spec.H * spec.topk
+    ref, ri, rc = harness.oracle_heads(oi, mode="topk", k=spec.topk, max_out=spec.topk)
+    inexact = harness.check_heads(g["idx"], g["count"], ref, "topk", 0.0, g_q_part=g["q_part"], g_scores=g["scores"],
+                                  g_out=g["out"], g_lse=g["lse"], tol=harness.ATTN_TOL["bf16"])
+    assert len(inexact) <= 3, inexact
+    rC, rv = O.pool_touch(np.zeros((spec.B, spec.cap), np.uint32), ri, rc, spec.n, 65535, want_victim=True)
+    harness.check_counters(g["counters"], rC, g["idx"], g["count"], ri, rc, spec.n, g["victim"], rv)

@@ -1,9 +1,9 @@
 """Speculation workspaces reused across calls, as the ABI allows: calls on one workspace agree on B,
 H, D and r while n, max_out and the mode change (whole rows, sliced rows whose slices all read each
-row's partial query, the fused decode layer), and a workspace that only whole-row calls used is all
-zero again, so it may serve another shape.  Every call must leave the workspace as it found it (the
-projection's partial-sum slots empty, the per-row slice counts and the arrival words at zero), so
-each result equals, bit for bit, that of the same call on a fresh workspace."""
+row's partial query, the fused decode layer); a call of another (B, H, D, r) follows
+ig_workspace_init.  Every call must leave the workspace as it found it (the projection's partial-sum
+slots empty, the per-row slice counts and the arrival words at zero, the status word clear), so each
+result equals, bit for bit, that of the same call on a fresh workspace."""
 import numpy as np
 import pytest
 
@@ -52,7 +52,9 @@ def lib():
 
 
 def test_whole_row_calls_of_different_shapes(lib):
-    """Whole-row calls leave the whole workspace zero: shapes may alternate on it."""
+    """Calls of one (B, H, D, r) share a workspace with no re-initialisation; a call of another shape
+    needs ig_workspace_init first (the workspace is stamped with the shape of its first call), after
+    which every result equals, bit for bit, the same call on a fresh workspace."""
     import torch
     from sparse_attention_ig_amd.runtime import DeviceLayer, decode_layer, prepare_layer
     specs = [_spec(gen.opt_6_7b(n=1500, B=4), H=8, topk=100),
@@ -62,9 +64,14 @@ def test_whole_row_calls_of_different_shapes(lib):
     ref = [_run(l, kw) for l, kw in zip(layers, kws)]
     shared = lib.ig_workspace_init(torch.empty(max(int(l.ws_spec.numel()) for l in layers), dtype=torch.uint8,
                                                device="cuda"))
-    for i in (0, 1, 0, 1, 1, 0):
+    prev = None
+    for i in (0, 0, 1, 1, 1, 0, 1, 0, 0):
+        if prev is not None and prev != i:
+            lib.ig_workspace_init(shared)   # another (B, H, D, r): the stamp must be cleared first
+        prev = i
         say(f"[shared workspace] ig_speculate B={specs[i].B} H={specs[i].H} r={specs[i].r} n={specs[i].n}")
         _same(_run(layers[i], kws[i], shared), ref[i], f"speculate {i}")
+        assert lib.ig_workspace_status(shared) == 0
     say("[shared workspace] ig_decode_layer")
     attn = layers[0].clone()
     attn.keep_scores = False
@@ -74,7 +81,8 @@ def test_whole_row_calls_of_different_shapes(lib):
     spec.ws_spec = shared
     decode_layer(attn, spec, kws[0])
     _same(_outputs(spec, dict(count=spec.count, idx=spec.idx)), ref[0], "decode layer")
-    _same(_run(layers[1], kws[1], shared), ref[1], "speculate after the decode layer")
+    _same(_run(layers[0], kws[0], shared), ref[0], "speculate after the decode layer")
+    assert lib.ig_workspace_status(shared) == 0
 
 
 def test_sliced_rows_changing_n_and_mode(lib):
@@ -93,3 +101,4 @@ def test_sliced_rows_changing_n_and_mode(lib):
         for i, kw in enumerate(calls):
             say(f"[shared workspace] sliced rows, call {i} {kw}")
             _same(_run(layer, kw, shared), ref[i], f"sliced call {i} rep {rep}")
+            assert lib.ig_workspace_status(shared) == 0
