@@ -244,6 +244,29 @@ int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const
                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * ig_speculate without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments (minus ws, ws_bytes), results and
+ * failure rule (count = -1) as ig_speculate; this call allocates nothing.  Its
+ * workspace is a static device array of 64 MiB (IG_NOALLOC_SCRATCH_BYTES) that
+ * each GPU the library runs on holds until the process ends; IG_EINVAL when
+ * ig_workspace_size(IG_OP_SPECULATE, ...) of the call exceeds it (B4 H32
+ * D4096 r32 n131072 top-5243 needs 33 MiB).  Every call first clears the
+ * regions that must start at zero (a fill kernel on `stream`, capturable) and
+ * stamps them with its shape, so shapes may change freely from call to call
+ * and a failed call leaves nothing behind.  All calls on one GPU share that
+ * GPU's array: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give unspecified results.
+ */
+#define IG_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ig_speculate_noalloc(const void* x, const void* Wq_part, const float* bq_part, const void* Kp,
+                         int B, int D, int H, int r, int n, int n_cap, int dtype, float scale,
+                         int mode, float alpha, int k, int max_sel,
+                         int32_t* idx, int32_t* count, int max_out,
+                         uint32_t* counters, uint32_t cmax, int32_t* victim,
+                         float* q_part, float* scores, int ld, hipStream_t stream);
+
+/*
  * One decode layer (section 3.2, "Big-Picture Architecture": the KV Selection
  * Controller speculates layer i's tokens from layer i-1's attention input
  * while layer i-1 computes; section 3.4, "Decoding Stage"): the attention of

@@ -65,6 +65,8 @@ _SIGS = {
     "ig_set_handover_test_mode": (_i, [_u32, _i]),
     "ig_speculate": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _i, _i, _vp, _vp, _i,
                           _vp, _u32, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
+    "ig_speculate_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _i, _i, _vp, _vp, _i,
+                                  _vp, _u32, _vp, _vp, _vp, _i, _vp]),
     "ig_rehearse": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp, _sz, _vp]),
     "ig_select": (_i, [_vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "ig_gather_kv": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
@@ -276,6 +278,27 @@ def ig_speculate(x, Wq_part, Kp, n: int, scale: float, mode: str, max_out: int, 
                                max_out, _ptr(counters), int(cmax), _ptr(victim), _ptr(q_part), _ptr(scores), ld,
                                _ptr(ws), wsb, _stream(stream)), "ig_speculate")
     return idx, count
+
+
+def ig_speculate_noalloc(x, Wq_part, Kp, n: int, scale: float, mode: str, max_out: int, *, alpha: float = math.inf,
+                         k: int = 0, max_sel: int = 0, bq_part=None, idx=None, count=None, counters=None,
+                         cmax: int = 65535, victim=None, q_part=None, scores=None, ld=None, stream=None):
+    """ig_speculate with the library's static device scratch as its workspace (allocates nothing;
+    ``idx`` and ``count`` must be given)."""
+    B, D = x.shape
+    Bk, H, n_cap, r = Kp.shape
+    if idx is None or count is None:
+        raise ValueError("ig_speculate_noalloc: idx and count must be preallocated")
+    if ld is None:
+        ld = scores.shape[2] if scores is not None else n
+    _check(load().ig_speculate_noalloc(_ptr(x), _ptr(Wq_part), _ptr(bq_part), _ptr(Kp), B, D, H, r, n, n_cap,
+                                       _dtype_of(x), float(scale), _MODES[mode], float(alpha), int(k), int(max_sel),
+                                       _ptr(idx), _ptr(count), max_out, _ptr(counters), int(cmax), _ptr(victim),
+                                       _ptr(q_part), _ptr(scores), ld, _stream(stream)), "ig_speculate_noalloc")
+    return idx, count
+
+
+IG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def ig_select(scores, mode: str, max_out: int, *, n=None, alpha: float = math.inf, k: int = 0, max_sel: int = 0,

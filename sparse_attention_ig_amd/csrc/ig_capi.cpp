@@ -145,7 +145,8 @@ int ig_set_handover_test_mode(uint32_t spin_limit, int withhold) {
 }
 
 // Validation of a speculation call (ig_speculate, and the speculation half of ig_decode_layer).
-static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes) {
+// noalloc: the workspace is the library's static scratch (ig_speculate_noalloc).
+static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes, bool noalloc = false) {
     const int dtype = c.dtype, B = c.B, D = c.D, H = c.H, r = c.r, n = c.n, n_cap = c.n_cap, max_out = c.max_out;
     IG_REQUIRE(dtype == IG_F32 || dtype == IG_BF16, "%s: unknown dtype %d", fn, dtype);
     IG_REQUIRE(c.x && c.Wq_part && c.Kp && c.idx && c.count, "%s: NULL required pointer", fn);
@@ -175,6 +176,11 @@ static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes) {
     IG_REQUIRE(H <= 0xFFFF && B <= 0xFFFF && D < (1 << 22), "%s: at most 65535 heads and batch rows and "
                "D < 2^22 (the workspace stamp)", fn);
     const size_t need = plan.ws_bytes;
+    if (noalloc) {
+        IG_REQUIRE(need <= kNoAllocScratchBytes, "%s: the call needs %zu bytes of scratch, more than the %zu "
+                   "bytes of the static scratch; use ig_speculate with a workspace", fn, need, kNoAllocScratchBytes);
+        return IG_OK;
+    }
     IG_REQUIRE(c.ws && ws_bytes >= need, "%s: workspace of %zu bytes needed", fn, need);
     IG_REQUIRE(aligned16(c.ws), "%s: workspace must be 16-byte aligned", fn);
     return IG_OK;
@@ -188,6 +194,16 @@ int ig_speculate(const void* x, const void* Wq_part, const float* bq_part, const
                      max_out, counters, cmax, victim, q_part, scores, ld, ws};
     if (const int e = check_spec("ig_speculate", c, ws_bytes)) return e;
     return hip_status(launch_decode_layer(nullptr, &c, stream), "ig_speculate");
+}
+
+int ig_speculate_noalloc(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D,
+                         int H, int r, int n, int n_cap, int dtype, float scale, int mode, float alpha, int k,
+                         int max_sel, int32_t* idx, int32_t* count, int max_out, uint32_t* counters, uint32_t cmax,
+                         int32_t* victim, float* q_part, float* scores, int ld, hipStream_t stream) {
+    const SpecCall c{x, Wq_part, bq_part, Kp, B, D, H, r, n, n_cap, dtype, scale, mode, alpha, k, max_sel, idx, count,
+                     max_out, counters, cmax, victim, q_part, scores, ld, nullptr};
+    if (const int e = check_spec("ig_speculate_noalloc", c, 0, true)) return e;
+    return hip_status(launch_speculate_noalloc(c, stream), "ig_speculate_noalloc");
 }
 
 int ig_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k, int max_sel,

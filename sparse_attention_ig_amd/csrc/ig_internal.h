@@ -69,6 +69,8 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_lds_bytes(int n);
 void set_handover_test_mode(uint32_t spin_limit, int withhold);
+// ig_speculate_noalloc: the speculation workspace in a static device array of this size per GPU
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(64) << 20;
 unsigned long long spec_shape_key(int B, int H, int D, int r);
 
 // kernel launchers (return hipError_t as int)
@@ -149,6 +151,7 @@ struct SpecCall {
 constexpr int kDecodeMaxRows = 16384;  // rows per (b, h) for the fused decode launch (LDS with two roles)
 bool decode_fusable(const AttnCall& a, const SpecCall& s);
 int launch_decode_layer(const AttnCall* a, const SpecCall* s, hipStream_t st);
+int launch_speculate_noalloc(const SpecCall& c, hipStream_t s);
 size_t int4_record_bytes(int d);
 int launch_quantize(const void* K, const void* V, int B, int H, int d, int ld_rows, int dtype, int row0, int nrows,
                     const int32_t* slot, void* KVq, int q_rows, hipStream_t s);

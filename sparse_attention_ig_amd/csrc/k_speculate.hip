@@ -6,6 +6,7 @@
 // workgroup per row selects among them.  InfiniGen, arXiv 2406.19707,
 // paper-graph-ui summary, section 3.4 "Decoding Stage" steps 1-3 and 5.
 #include <algorithm>
+#include <mutex>
 
 #include "ig_spec_dev.h"
 
@@ -198,6 +199,64 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     const SpecPlan sp = plan_speculate(B, H, D, r, n, max_out, dtype);
     return launch_touch_bits(counters, p.bits, B, H, n, n_cap, cmax,
                              reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), victim, s);
+}
+
+// ------------------------------------------------------------------ ig_speculate_noalloc
+// The speculation workspace of callers that cannot allocate: a file-scope device array, one copy per
+// GPU (each GPU the library runs on holds it until the process ends).  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol): the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (hipError_t as int).
+static int noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return static_cast<int>(e);
+        if (!ptr) return static_cast<int>(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return 0;
+}
+
+// Start of a no-allocation call: every word of [0, words) to zero except the shape stamp (words 2-3),
+// which gets this call's key, and the counter kernel's per-sequence flags (when the call has them).
+__global__ void k_scratch_reset(uint32_t* ws, size_t words, unsigned long long key, uint32_t* flags, int B) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < words) ws[i] = i == 2 ? static_cast<uint32_t>(key) : i == 3 ? static_cast<uint32_t>(key >> 32) : 0u;
+    if (flags && i < static_cast<size_t>(B)) flags[i] = 0u;
+}
+
+int launch_speculate_noalloc(const SpecCall& c, hipStream_t s) {
+    const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
+    if (sp.ws_bytes > kNoAllocScratchBytes) return static_cast<int>(hipErrorInvalidValue);  // checked before
+    void* ws = nullptr;
+    int e = noalloc_scratch(&ws);
+    if (e) return e;
+    // the status word, the stamp, the arrival words, the slices' per-row counts and the partial-sum slots
+    // come first (off_cnt is where the candidates start); the candidates and bitmaps are written before
+    // they are read in every call
+    const size_t words = sp.off_cnt / sizeof(uint32_t);
+    uint32_t* flags = sp.bits && c.counters ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags)
+                                            : nullptr;
+    const size_t span = std::max(words, static_cast<size_t>(c.B));
+    hipLaunchKernelGGL(k_scratch_reset, dim3(static_cast<unsigned>((span + 255) / 256)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ws), words, spec_shape_key(c.B, c.H, c.D, c.r), flags, c.B);
+    if ((e = static_cast<int>(hipGetLastError()))) return e;
+    return launch_speculate(c.x, c.Wq_part, c.bq_part, c.Kp, c.B, c.D, c.H, c.r, c.n, c.n_cap, c.dtype, c.scale,
+                            c.mode, c.alpha, c.k, c.max_sel, c.idx, c.count, c.max_out, c.counters, c.cmax, c.victim,
+                            c.q_part, c.scores, c.ld, ws, s);
 }
 
 __global__ void k_zero_words(uint32_t* p, size_t n) {
