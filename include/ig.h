@@ -166,12 +166,16 @@ int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
  * Status word of a speculation workspace (ig_speculate, the speculation half
  * of ig_decode_layer): 0, or IG_WS_* bits set by a call that ran on it.  The
  * bits are sticky: a workspace with a nonzero status gives count = -1 for
- * every row of later calls until ig_workspace_init clears it.  Waits for the
- * work enqueued on `stream` (hipStreamSynchronize) and copies the word to
- * *status; not for use under graph capture.  IG_EINVAL when ws or status is
- * NULL or ws_bytes is below 16.
+ * every row of later calls until ig_workspace_init clears it.  *recomputed
+ * (when not NULL) receives the number of sliced top-k rows, summed over the
+ * calls since ig_workspace_init (modulo 2^32), whose merge found the slices'
+ * tight candidates too few and recomputed the row's scores (exact, slower;
+ * see ig_speculate).  Waits for the work enqueued on `stream`
+ * (hipStreamSynchronize) and copies the words; not for use under graph
+ * capture.  IG_EINVAL when ws or status is NULL or ws_bytes is below 256.
  */
-int ig_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, hipStream_t stream);
+int ig_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, uint32_t* recomputed,
+                        hipStream_t stream);
 
 /*
  * Failure-path testing of the speculation's in-launch hand-over, process-wide,
@@ -218,11 +222,10 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * with slices, a merge launch follows.  The workspace (IG_OP_SPECULATE bytes,
  * required) starts with a 256-byte region holding the status word (uint32 at
  * offset 0, see ig_workspace_status) and the shape stamp (uint64 at offset 8),
- * then one uint32 arrival word per sequence ([B] at offset 256), the slices'
- * per-row counts and the projection's split partial sums, then the slices'
- * candidates (when there are slices); it must have been zero-filled once with
- * ig_workspace_init, and every call returns the arrival words, the counts and
- * the partial-sum slots to zero.  The first call after the zero-fill stamps
+ * then one uint32 arrival word per sequence ([B] at offset 256) and the
+ * projection's split partial sums, then the slices' candidates (when there
+ * are slices); it must have been zero-filled once with ig_workspace_init,
+ * and every call returns the arrival words and the partial-sum slots to zero.  The first call after the zero-fill stamps
  * the workspace with its (B, H, D, r) (the places of those regions depend on
  * them; n, max_out and the mode may change from call to call); a call of
  * another (B, H, D, r) sets IG_WS_SHAPE instead of running: run

@@ -424,11 +424,18 @@ def gather_kv_int4(Kq, Ks, Km, Vq, Vs, Vm, idx: np.ndarray, count: np.ndarray, m
 # ---------------------------------------------------------------- one decode layer-step
 def decode_step(x, Wq_part, Kp, q, K, V, C, *, n, H, r, scale, mode, alpha=math.inf, k=0,
                 max_sel=0, max_out=0, cmax=65535, bq_part=None, want_victim=False):
-    """One layer-step of the hot path, in the pages' order: partial query, speculated scores,
-    selection, attention over the selected rows, counter update (all inputs float64 values,
-    except C)."""
+    """One layer-step of the hot path, in the pages' order (section 3.4, "Decoding Stage" steps 1-5
+    and the pool paragraph): partial query, speculated scores, selection (mode "threshold" or "topk"
+    per head, or "headavg": step 4's multi-head averaging of the threshold counts), attention over
+    the selected rows, counter update.  Inputs are float64 values, except the counters C (uint32,
+    left unchanged when None: then no counters or victim are returned)."""
     qp, s = rehearse(x, Wq_part, Kp, n, H, r, scale, bq_part)
-    idx, cnt = select(s, mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out)
+    if mode == "headavg":
+        idx, cnt = select_head_average(s, alpha, max_sel=max_sel, max_out=max_out)
+    else:
+        idx, cnt = select(s, mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out)
     o, lse = sparse_decode_attn(q, K, V, idx, cnt, scale)
-    C2, victim = pool_touch(C, idx, cnt, n, cmax, want_victim)
+    C2 = victim = None
+    if C is not None:
+        C2, victim = pool_touch(C, idx, cnt, n, cmax, want_victim)
     return dict(q_part=qp, scores=s, idx=idx, count=cnt, out=o, lse=lse, counters=C2, victim=victim)

@@ -61,7 +61,7 @@ _SIGS = {
     "ig_partial_weight_index": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _i]),
     "ig_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "ig_workspace_init": (_i, [_vp, _sz, _vp]),
-    "ig_workspace_status": (_i, [_vp, _sz, ctypes.POINTER(_u32), _vp]),
+    "ig_workspace_status": (_i, [_vp, _sz, ctypes.POINTER(_u32), ctypes.POINTER(_u32), _vp]),
     "ig_set_handover_test_mode": (_i, [_u32, _i]),
     "ig_speculate": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _i, _i, _vp, _vp, _i,
                           _vp, _u32, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -239,12 +239,14 @@ def ig_workspace_init(ws, *, stream=None):
     return ws
 
 
-def ig_workspace_status(ws, *, stream=None) -> int:
-    """The status word of a speculation workspace (0, or IG_WS_* bits); waits for ``stream``."""
+def ig_workspace_status(ws, *, stream=None, recomputed: bool = False):
+    """The status word of a speculation workspace (0, or IG_WS_* bits); with ``recomputed``, also the
+    number of sliced top-k rows whose merge recomputed the row's scores.  Waits for ``stream``."""
     v = ctypes.c_uint32(0)
-    _check(load().ig_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(v), _stream(stream)),
-           "ig_workspace_status")
-    return int(v.value)
+    r = ctypes.c_uint32(0)
+    _check(load().ig_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(v), ctypes.byref(r),
+                                      _stream(stream)), "ig_workspace_status")
+    return (int(v.value), int(r.value)) if recomputed else int(v.value)
 
 
 def ig_set_handover_test_mode(spin_limit: int = 0, withhold: bool = False):

@@ -181,4 +181,33 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int bh, int split, 
     }
 }
 
+// The split-K combine of one (b, h): the splits' (m, l, acc) rescaled to the largest m and added, then
+// o = acc / l and lse = m + log l.  Run by the threads t < d of a workgroup (each owns output element t).
+struct CombineArgs {
+    const float* part;   // [B*H][nsplit][2 + d]; NULL: nothing to combine
+    int nsplit, d;
+    float* out;
+    float* lse;
+};
+
+__device__ __forceinline__ void combine_item(const CombineArgs& c, int bh) {
+    const int nsplit = c.nsplit, d = c.d;
+    const float* pp = c.part + static_cast<size_t>(bh) * nsplit * (2 + d);
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (2 + d)]);
+    for (int t = threadIdx.x; t < d; t += blockDim.x) {
+        float L = 0.f, A = 0.f;
+        if (M != -INFINITY) {
+            for (int s = 0; s < nsplit; ++s) {
+                const float ms = pp[s * (2 + d)];
+                const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+                L += pp[s * (2 + d) + 1] * w;
+                A += pp[s * (2 + d) + 2 + t] * w;
+            }
+        }
+        c.out[static_cast<size_t>(bh) * d + t] = L > 0.f ? A / L : 0.f;
+        if (c.lse && t == 0) c.lse[bh] = L > 0.f ? M + __logf(L) : -INFINITY;
+    }
+}
+
 }  // namespace ig

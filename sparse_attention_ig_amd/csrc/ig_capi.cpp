@@ -128,14 +128,16 @@ int ig_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
     return hip_status(launch_zero(ws, ws_bytes, stream), "ig_workspace_init");
 }
 
-int ig_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, hipStream_t stream) {
-    IG_REQUIRE(ws && status && ws_bytes >= 16, "ig_workspace_status: NULL workspace or status, or fewer than 16 "
+int ig_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, uint32_t* recomputed,
+                        hipStream_t stream) {
+    IG_REQUIRE(ws && status && ws_bytes >= 256, "ig_workspace_status: NULL workspace or status, or fewer than 256 "
                "bytes");
-    uint32_t v = 0;
-    hipError_t e = hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream);
+    uint32_t v[5] = {0, 0, 0, 0, 0};
+    hipError_t e = hipMemcpyAsync(v, ws, sizeof(v), hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_status(static_cast<int>(e), "ig_workspace_status");
-    *status = v;
+    *status = v[0];
+    if (recomputed) *recomputed = v[4];
     return ok();
 }
 
@@ -168,7 +170,7 @@ static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes, bool n
                                      "use ig_rehearse + ig_select", fn);
     else
         return fail(IG_EINVAL, "%s: unknown mode %d", fn, c.mode);
-    const SpecPlan plan = plan_speculate(B, H, D, r, n, max_out, dtype);
+    const SpecPlan plan = plan_speculate(B, H, D, r, n, max_out, dtype, c.mode);
     if (!plan.ok)
         return fail(IG_EUNSUPPORTED, "%s: n = %d needs more than %d slices of %d rows; use ig_rehearse + "
                     "ig_select", fn, n, kSpecMaxSlices, kSpecMaxRows);

@@ -56,16 +56,19 @@ struct SlicePlan {
     int slices, slice_rows, cap;
     bool ok;
 };
-SlicePlan plan_slices(int64_t rows, int n, int max_out);
+SlicePlan plan_slices(int64_t rows, int n, int max_out, bool topk = false);
+constexpr int kTopkSliceRows = 8192;  // rows per slice of a sliced top-k row
 
 struct SpecPlan {
     int slices, slice_rows, cand_cap;
     int proj_blocks, splits, proj_wgs;  // projection workgroups: column blocks x splits of the D inputs
     bool bits;                        // the merge leaves bitmaps and a counter kernel applies them
+    bool tight;                       // top-k slices with tight candidates (the merge checks, or recomputes)
     bool ok;                          // false: rows too long for the candidates to fit one merge
-    size_t off_status, off_arrive, off_pdone, off_part, off_cnt, off_key, off_idx, off_bits, off_flags, ws_bytes;
+    size_t off_status, off_arrive, off_part, off_cnt, off_lo, off_q, off_key, off_idx, off_bits,
+        off_flags, ws_bytes;
 };
-SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype);
+SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype, int mode);
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);
 size_t speculate_lds_bytes(int n);
 void set_handover_test_mode(uint32_t spin_limit, int withhold);

@@ -35,6 +35,7 @@
 #include <climits>
 #include <type_traits>
 
+#include "ig_attn_dev.h"
 #include "ig_internal.h"
 #include "ig_pool_dev.h"
 #include "ig_select_dev.h"
@@ -77,9 +78,8 @@ struct SpecParams {
     // kernel adds the heads' bits per slot (no atomics per selected slot); NULL: atomics in the merge
     uint32_t* bits;
     // projection workgroups: the first proj_wgs workgroups of the launch (proj_blocks column blocks x
-    // splits); row_wgs: the row workgroups; pdone [B*H]: slices of a row done reading its partial sums
+    // splits); row_wgs: the row workgroups
     int proj_wgs, proj_blocks, row_wgs;
-    uint32_t* pdone;
     // workspace status word (sticky failure bits) and shape stamp (the (B, H, D, r) key of the calls the
     // workspace serves; 0 until the first call claims it).  NULL: no checks (the standalone selection).
     uint32_t* status;
@@ -87,6 +87,13 @@ struct SpecParams {
     unsigned long long key;
     uint32_t spin_limit;  // polls of a row workgroup before it stops waiting for its partial query
     int withhold;         // failure-path testing: the projection workgroups store no partial sums
+    // top-k slices with tight candidates: a slice hands on about its share of the row's budget (plus a
+    // margin) and records in cand_lo [B*H][slices] the bound it used (every key of the slice at or above
+    // it was handed on); the first slice of a row stores the row's scaled partial query in q_rows
+    // [B*H][r], from which a merge whose candidates turn out too few recomputes the row's scores.
+    int tight;
+    uint32_t* cand_lo;
+    float* q_rows;
 };
 
 // Sticky status bits of a speculation workspace (the public IG_WS_* values).
@@ -96,7 +103,10 @@ constexpr uint32_t kWsShape = IG_WS_SHAPE;
 // Fills the launch parameters of a speculation call (projection and row workgroups).
 int begin_speculate(const SpecCall& c, SpecParams* p);
 // The merge launch of sliced rows: one workgroup per row over the slices' candidate slots.
-int launch_spec_merge(const SpecParams& p, hipStream_t s);
+int launch_spec_merge(const SpecParams& p, int dtype, hipStream_t s, const CombineArgs& cb = CombineArgs{});
+// After the launch of sliced rows: the merge (with the attention combine cb, if any), and the counter
+// kernels when the merge leaves bitmaps.
+int finish_speculate(const SpecParams& p, int dtype, void* ws, hipStream_t s, const CombineArgs& cb = CombineArgs{});
 
 template <int R>
 struct SpecShared {
@@ -215,20 +225,21 @@ __device__ __forceinline__ bool ws_admit(const SpecParams& p) {
 // Row workgroup: the partial query q[c] (c < R) of row b, columns [col0, col0 + R): poll the split
 // partials until every slot is filled, add them in a fixed order (thread (c, i) adds splits i, i + P,
 // .. in turn, then the P threads of column c are added by DPP; bias last), and return the slots to
-// empty.  Writes q (and q_out when not NULL); ends with a barrier.  Returns false (block-uniform) when
-// the row may not use the workspace (ws_admit) or when some slot is still empty after spin_limit
-// polls: then nothing is added and no slot is touched (a producer may still be about to store into
-// one), the timeout sets kWsTimeout, and the workspace stays unusable until it is zero-filled again.
+// empty (a whole row; the slices of a row leave that to the row's merge).  Writes q (and q_out when not
+// NULL); s_flag: one word of LDS scratch; ends with a barrier.  Returns false (block-uniform) when the
+// row may not use the workspace (ws_admit) or when some slot is still empty after spin_limit polls:
+// then nothing is added and no slot is touched (a producer may still be about to store into one), the
+// timeout sets kWsTimeout, and the workspace stays unusable until it is zero-filled again.
 template <int R>
-__device__ __forceinline__ bool wait_partial_query(const SpecParams& p, int b, int bh, int col0, float* q,
-                                                   float* q_out) {
+__device__ __forceinline__ bool wait_partial_query(const SpecParams& p, int b, int col0, float* q, float* q_out,
+                                                   int* s_flag) {
     constexpr int P = kSpecThreads / R < 64 ? kSpecThreads / R : 64;  // threads per column
     const int tid = threadIdx.x;
     const bool on = tid < R * P;
     const int c = tid / P, i = tid % P;
     const int N = p.H * p.r;
     const bool sole = p.slices == 1;  // the only reader of these slots
-    if (__syncthreads_or(tid == 0 && !ws_admit(p))) return false;
+    bool admitted = false;            // (block-uniform)
     float acc = 0.f;
     for (int s0 = 0; s0 < p.splits; s0 += P) {
         const int s = s0 + i;
@@ -238,7 +249,14 @@ __device__ __forceinline__ bool wait_partial_query(const SpecParams& p, int b, i
         uint32_t polls = 0;
         for (;;) {
             if (mine) v = coherent_load(src);
-            if (!__syncthreads_or(mine && __float_as_uint(v) == 0u)) break;
+            // the admission's loads travel with the first poll's (one round trip for both)
+            if (!admitted && tid == 0) *s_flag = ws_admit(p) ? 0 : 1;
+            const bool empty = __syncthreads_or(mine && __float_as_uint(v) == 0u);
+            if (!admitted) {
+                admitted = true;
+                if (*s_flag) return false;  // (published by the barrier above)
+            }
+            if (!empty) break;
             if (++polls >= p.spin_limit) {  // block-uniform: every thread counts the same polls
                 if (tid == 0 && p.status) atomicOr(p.status, kWsTimeout);
                 __syncthreads();
@@ -261,18 +279,7 @@ __device__ __forceinline__ bool wait_partial_query(const SpecParams& p, int b, i
         q[c] = v;
         if (q_out) q_out[c] = v;
     }
-    if (!sole) {
-        // slices of one row read the same slots: the last one to finish reading empties them
-        int last = 0;
-        if (tid == 0)
-            last = __hip_atomic_fetch_add(&p.pdone[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   static_cast<uint32_t>(p.slices - 1);
-        if (__syncthreads_or(last)) {
-            for (int k = tid; k < p.splits * R; k += kSpecThreads)
-                coherent_store(p.part + (static_cast<size_t>(k / R) * p.B + b) * N + col0 + k % R, 0.f);
-            if (tid == 0) __hip_atomic_store(&p.pdone[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    // (the slices of a row all read the same slots: the row's merge, a launch after them, empties them)
     __syncthreads();
     return true;
 }
@@ -300,46 +307,80 @@ __device__ __forceinline__ void seq_arrive(const SpecParams& p, int b, bool sat,
 struct IdentityIdx {
     __device__ __forceinline__ int operator()(int j) const { return j; }
 };
+// Row index of key j from an array in LDS (a merge's candidates copied there with their row indices).
+struct LdsIdx {
+    const int32_t* p;
+    __device__ __forceinline__ int operator()(int j) const { return p[j]; }
+};
 
-// Selection over the keys ks[0..m) (held in LDS, or a merge's candidates in global memory) and its
-// results.  `rows`: the row count the limit refers to (the slice's length in a slice workgroup, n
-// otherwise); gidx(j): the row index of key j; lds: at least 1024 words of LDS scratch (may be the
-// keys' own storage).  TO_CANDS: write the selected keys and row indices as this slice's candidates
-// (a superset of the slice's selection, at most cand_cap keys; the slice's unused candidate slots get
-// key 0, below every score key); otherwise write idx / count
-// and update the counters (one integer atomic per selected slot, all in flight together; the last
-// workgroup of sequence b halves if any slot saturated and picks the victim).
-template <bool TO_CANDS, class KS, typename GIdx>
-__device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, int slice, int m, int rows,
-                                            uint32_t kmax_all, KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs,
-                                            int& s_last, GIdx gidx) {
-    const int tid = threadIdx.x;
+constexpr int kSampledMin = 16384;  // keys from which a selection first tries the sampled bracket
+
+// The cut of a selection.  Selecting every key above kth and the first need_eq keys equal to it (of
+// eq_total equal keys; every key >= kth when need_eq >= eq_total) gives the selection.
+struct SelCut {
+    uint32_t kth;
+    int need_eq, eq_total;
+};
+
+// Keys a slice of `rows` of a row's n rows hands on for a top-kk selection of the row with tight
+// candidates: its expected share of the row's kk plus five standard deviations and 8 (a slice holding
+// more of the row's top kk than that makes the merge recompute the row), at most cap.
+__device__ __forceinline__ int tight_slice_k(int kk_row, int rows, int n, int cap) {
+    const float e = static_cast<float>(kk_row) * static_cast<float>(rows) / static_cast<float>(n);
+    const int want = static_cast<int>(ceilf(e + 5.f * sqrtf(e) + 8.f));
+    return min(min(want, rows), cap);
+}
+
+// The cut of the selection over the keys ks[0..m) (held in LDS, a merge's candidates in global memory,
+// or a row recomputed from its partial keys).  `rows`: the row count the limit refers to (the slice's
+// length in a slice workgroup, n otherwise).  TO_CANDS (a slice): the cut of a superset of the slice's
+// selection of at most cand_cap keys -- every key at or above a sampled lower bound of the slice's cut
+// when they fit; with tight top-k candidates, of the slice's share of the row's budget.
+template <bool TO_CANDS, class KS>
+__device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int m, int rows, uint32_t kmax_all, KS keys,
+                                           SelScratch& sh, FastSel& fs) {
     int limit = min(rows, p.max_out);
     bool done = false;
     int kk = 0;
-    uint32_t kth = 0;
-    int need_eq = INT_MAX, eq_total = INT_MAX;
+    SelCut c{0u, INT_MAX, INT_MAX};
     if (p.mode == IG_SEL_THRESHOLD) {
         const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
         const int cnt = count_ge<kSpecThreads>(keys, m, kc, sh);
         if (p.max_sel > 0) limit = min(limit, p.max_sel);
         if (cnt <= limit) {
-            kth = kc;
+            c.kth = kc;
             done = true;
         } else {
             kk = limit;
         }
     } else {
         kk = min(p.k, limit);
+        if constexpr (TO_CANDS) {
+            if (p.tight) kk = tight_slice_k(min(p.k, min(p.n, p.max_out)), rows, p.n, p.cand_cap);
+        }
     }
-    // a slice only has to hand on a superset of its own selection (its candidate slots hold more than
-    // max_out keys): every key at or above a sampled lower bound of its cut, when they fit
     if constexpr (TO_CANDS) {
-        if (!done && p.cand_cap > kk + kk / 8 && sampled_superset(keys, m, kk, p.cand_cap, fs, sh, &kth)) done = true;
+        if (!done && p.cand_cap > kk + kk / 8 && sampled_superset(keys, m, kk, p.cand_cap, fs, sh, &c.kth)) done = true;
     }
-    if (!done && !sampled_kth(keys, m, kk, fs, sh, &kth, &need_eq, &eq_total))
-        radix_kth_keys(keys, m, kk, fs, &kth, &need_eq, &eq_total);
+    // the sampled bracket pays off on long rows; below kSampledMin keys the radix over every key is faster
+    if (!done && (m < kSampledMin || !sampled_kth(keys, m, kk, fs, sh, &c.kth, &c.need_eq, &c.eq_total)))
+        radix_kth_keys(keys, m, kk, fs, &c.kth, &c.need_eq, &c.eq_total);
+    return c;
+}
 
+// The results of a selection with cut c over ks[0..m): gidx(j) is the row index of key j; lds: at least
+// 1024 words of LDS scratch (may be the keys' own storage).  TO_CANDS: write the selected keys and row
+// indices as this slice's candidates (at most cand_cap keys; the slice's unused candidate slots get key
+// 0, below every score key) and, with tight candidates, the slice's bound; otherwise write idx / count
+// and update the counters (one integer atomic per selected slot, all in flight together; the last
+// workgroup of sequence b halves if any slot saturated and picks the victim).
+template <bool TO_CANDS, class KS, typename GIdx>
+__device__ __forceinline__ void spec_emit(const SpecParams& p, int b, int bh, int slice, int m, const SelCut& c,
+                                          KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs, int& s_last,
+                                          GIdx gidx) {
+    const int tid = threadIdx.x;
+    const uint32_t kth = c.kth;
+    const int need_eq = c.need_eq, eq_total = c.eq_total;
     if constexpr (TO_CANDS) {
         const size_t base = (static_cast<size_t>(bh) * p.slices + slice) * p.cand_cap;
         uint32_t* ck = p.cand_key + base;
@@ -351,7 +392,12 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
         const int written = min(compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put),
                                 p.cand_cap);
         for (int i = written + tid; i < p.cand_cap; i += kSpecThreads) ck[i] = 0u;
-        if (tid == 0) p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = written;
+        if (tid == 0) {
+            p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = written;
+            // every key above kth was handed on, and every key equal to it unless only some of the ties
+            // were taken: the keys are integers, so the bound is kth or kth + 1
+            if (p.cand_lo) p.cand_lo[static_cast<size_t>(bh) * p.slices + slice] = need_eq >= eq_total ? kth : kth + 1u;
+        }
         return;
     } else {
         const int n = p.n;
@@ -360,10 +406,12 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
         uint32_t* stage = fs.stage();  // the select's scratch words are free by now
         int32_t* out = p.idx + static_cast<size_t>(bh) * p.max_out;
         int written;
-        if constexpr (std::is_same<GIdx, IdentityIdx>::value) {
+        if constexpr (std::is_same<GIdx, IdentityIdx>::value || std::is_same<GIdx, LdsIdx>::value) {
+            // the row index of each selected key is at hand: written as the key is placed
             auto keep = [&](int pos, int j) {
-                out[pos] = j;
-                if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(j);
+                const int g = gidx(j);
+                out[pos] = g;
+                if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(g);
             };
             written = compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
         } else {
@@ -439,6 +487,53 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
         seq_arrive(p, b, __syncthreads_or(sat) != 0, lds, sh, s_last);
     }
 }
+
+// Selection over ks[0..m) and its results (spec_cut, then spec_emit).
+template <bool TO_CANDS, class KS, typename GIdx>
+__device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, int slice, int m, int rows,
+                                            uint32_t kmax_all, KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs,
+                                            int& s_last, GIdx gidx) {
+    const SelCut c = spec_cut<TO_CANDS>(p, m, rows, kmax_all, keys, sh, fs);
+    spec_emit<TO_CANDS>(p, b, bh, slice, m, c, keys, lds, sh, fs, s_last, gidx);
+}
+
+// Score keys of a whole row recomputed from its partial keys (the exact fallback of a merge whose tight
+// candidates turn out too few): the same float32 products in the same order as the row workgroups'
+// stream -- per lane group member the fused multiply-adds over its VEC channels, then the members'
+// partial sums added pairwise as the cross-lane reduction adds them -- so every key equals the one the
+// slice held.  q: the scaled partial query [R] in LDS.
+template <typename T, int LPR>
+struct RowKeys {
+    static constexpr int kE = LPR >= 8 ? 1 : 4;  // keys per lane per step (each a row of LPR 16-byte loads)
+    static constexpr int VEC = Vec<T>::N;
+    static constexpr int R = LPR * VEC;
+    const T* kp;     // the row's partial keys [n][R]
+    const float* q;
+    __device__ __forceinline__ uint32_t at(int j) const {
+        const T* row = kp + static_cast<size_t>(j) * R;
+        float part[LPR];
+#pragma unroll
+        for (int l = 0; l < LPR; ++l) {
+            float kv[VEC];
+            unpack_raw(load_raw16(row + l * VEC), kv);
+            float s = 0.f;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) s = fmaf(q[l * VEC + v], kv[v], s);
+            part[l] = s;
+        }
+#pragma unroll
+        for (int w = 1; w < LPR; w *= 2) {
+#pragma unroll
+            for (int i = 0; i < LPR; i += 2 * w) part[i] = part[i] + part[i + w];
+        }
+        return score_key(part[0]);
+    }
+    template <int E>
+    __device__ __forceinline__ void load(int j, int end, uint32_t (&k)[E]) const {
+#pragma unroll
+        for (int e = 0; e < E; ++e) k[e] = j + e < end ? at(j + e) : 0u;
+    }
+};
 
 // The arrival of a row of sequence b after its counter updates (sat: some increment of this workgroup
 // reached cmax).  Every counter atomic of this workgroup has returned (its value was used) before the
@@ -520,7 +615,7 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
         }
     }
     float* q_out = (p.q_part && slice == 0) ? p.q_part + static_cast<size_t>(bh) * R : nullptr;
-    if (!wait_partial_query<R>(p, b, bh, h * R, s_q, q_out)) {
+    if (!wait_partial_query<R>(p, b, h * R, s_q, q_out, &sm.last)) {
         // no partial query: a slice marks its candidates invalid for the merge, a whole row fails
         if (p.slices > 1) {
             if (tid == 0) p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = -1;
@@ -539,6 +634,8 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
     float q[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) q[v] = s_q[li * VEC + v] * p.scale;
+    // the scaled partial query, for a merge that may have to recompute this row's scores
+    if (p.q_rows && slice == 0 && tid < R) p.q_rows[static_cast<size_t>(bh) * R + tid] = s_q[tid] * p.scale;
 
     // 2. scores -> LDS keys, double-buffered row batches (the first batch is already in flight)
     float* srow = p.scores ? p.scores + static_cast<size_t>(bh) * p.ld + r0 : nullptr;
@@ -583,13 +680,21 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
         spec_select<false>(p, b, bh, 0, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last, IdentityIdx());
 }
 
-// Merge workgroup of a sliced row.  Slice sl left its selection in candidate slots [sl * cap, +cap) of
-// the row (unused slots hold key 0, below every score key), so the m = slices * cap slots are in row
-// order and together hold the row's selection: a key among the row's top c is among its slice's top c,
-// and a key at or above the row's threshold cut is at or above its slice's.  The selection runs again
-// over them with the row's rules: on a copy in LDS when m <= kSpecMaxRows, else straight from the
-// candidate arrays (L2-resident: the slices wrote them just before).
-template <int R>
+// Merge workgroup of a sliced row.  Slice sl left its candidates in slots [sl * cap, +cap) of the row
+// (unused slots hold key 0, below every score key), so the m = slices * cap slots are in row order.
+// Without tight candidates they hold the row's selection: a key among the row's top c is among its
+// slice's top c, and a key at or above the row's threshold cut is at or above its slice's.  The
+// selection runs again over them with the row's rules: on a copy in LDS when m <= kSpecMaxRows, else
+// straight from the candidate arrays (L2-resident: the slices wrote them just before).
+//
+// With tight top-k candidates a slice handed on only about its share of the row's budget, every key of
+// it at or above its bound E_s.  The row's kk-th largest candidate T' is then checked: when T' >= E_s for
+// every slice, every key of the row at or above T' is a candidate, so the kk-th largest key of the row is
+// T' and the row's top kk (ties to the lower index) are the candidates' top kk -- the selection is exact.
+// Otherwise (a slice held more of the row's top kk than its share) the row's scores are recomputed from
+// its partial keys (RowKeys, the same float32 arithmetic as the slices) and the selection runs over
+// them: exact as well, only slower.
+template <typename T, int LPR, int R>
 __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t* keys, SpecShared<R>& sm) {
     SelScratch& sh = sm.sh;
     FastSel& fs = sm.fs;
@@ -597,48 +702,115 @@ __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t
     int b, h;
     spec_bh(p, wg, &b, &h);
     const int bh = b * p.H + h;
+    // every slice of the row has read its partial-sum slots (they ran in the launch before): empty them
+    if (p.part) {
+        const int N = p.H * p.r;
+        for (int k = tid; k < p.splits * p.r; k += kSpecThreads)
+            coherent_store(p.part + (static_cast<size_t>(k / p.r) * p.B + b) * N + h * p.r + k % p.r, 0.f);
+    }
     const int m = p.slices * p.cand_cap;
     const size_t base = static_cast<size_t>(bh) * m;
     const uint32_t* ck = p.cand_key + base;
     const int32_t* ci = p.cand_idx + base;
     auto gidx = [&](int j) { return static_cast<int>(ci[j]); };
-    // a slice that could not compute its scores marks its count -1: the row fails
+    // the slices' candidate counts (a slice that could not compute its scores marks its count -1: the row
+    // fails) and, with tight candidates, their bounds
+    const bool checked = p.tight && p.mode == IG_SEL_TOPK;
     const int32_t* cc = p.cand_cnt + static_cast<size_t>(bh) * p.slices;
-    if (__syncthreads_or(tid < p.slices && cc[tid] < 0)) {
+    int cnt = 0;
+    uint32_t lo = 0;
+    if (tid < p.slices) {
+        cnt = cc[tid];
+        if (checked) lo = p.cand_lo[static_cast<size_t>(bh) * p.slices + tid];
+    }
+    if (__syncthreads_or(cnt < 0)) {
         spec_fail_row(p, b, bh, keys, sh, sm.last);
         return;
     }
+    // where each slice's candidates go when only the used slots are copied: a prefix sum over the slices
+    int* s_off = reinterpret_cast<int*>(sm.q);  // (kSpecMaxSlices + 1 words, free until a recompute)
+    if (tid < p.slices) s_off[tid + 1] = min(cnt, p.cand_cap);
+    const uint32_t emax = checked ? block_max_u32(lo, sh) : 0u;
+    __syncthreads();
+    if (tid == 0) {
+        s_off[0] = 0;
+        for (int sl = 1; sl <= p.slices; ++sl) s_off[sl] += s_off[sl - 1];
+    }
     fast_sel_init(fs);
+    __syncthreads();
+    const int mu = s_off[p.slices];  // used candidate slots, in row order slice by slice
     uint32_t kmax = 0;
     constexpr int U = 8;  // loads per lane in flight
-    if (m <= kSpecMaxRows) {
-        for (int i0 = tid; i0 < m; i0 += kSpecThreads * U) {
-            uint32_t v[U];
+    bool exact = true;
+    if (mu <= kSpecMaxRows) {
+        // the used slots' keys to LDS [0, mu), and their row indices to [mu, 2 mu) when they fit too
+        const bool with_idx = 2 * mu <= kSpecMaxRows;
+        int32_t* lidx = reinterpret_cast<int32_t*>(keys + mu);
+        // thread t copies used slot t (t + 1024, ..) of every slice, the loads of all the slices in flight
+        // together: slot i of slice sl goes to s_off[sl] + i
+        for (int i = tid; i < p.cand_cap; i += kSpecThreads) {
+            uint32_t v[kSpecMaxSlices];
+            int32_t x[kSpecMaxSlices];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < m ? ck[i0 + u * kSpecThreads] : 0u;
+            for (int sl = 0; sl < kSpecMaxSlices; ++sl) {
+                const bool on = sl < p.slices && i < s_off[sl + 1] - s_off[sl];
+                const size_t g = static_cast<size_t>(sl) * p.cand_cap + i;
+                v[sl] = on ? ck[g] : 0u;
+                x[sl] = on && with_idx ? ci[g] : 0;
+            }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (i0 + u * kSpecThreads < m) {
-                    keys[i0 + u * kSpecThreads] = v[u];
-                    kmax = v[u] > kmax ? v[u] : kmax;
+            for (int sl = 0; sl < kSpecMaxSlices; ++sl) {
+                if (sl < p.slices && i < s_off[sl + 1] - s_off[sl]) {
+                    keys[s_off[sl] + i] = v[sl];
+                    if (with_idx) lidx[s_off[sl] + i] = x[sl];
+                    kmax = v[sl] > kmax ? v[sl] : kmax;
                 }
             }
         }
         const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
-        spec_select<false>(p, b, bh, 0, m, p.n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last, gidx);
-        return;
-    }
-    if (p.mode == IG_SEL_THRESHOLD) {
-        for (int i0 = tid; i0 < m; i0 += kSpecThreads * U) {
-            uint32_t v[U];
+        const SelCut c = spec_cut<false>(p, mu, p.n, kmax_all, LdsKeys{keys}, sh, fs);
+        exact = !checked || (c.kth != 0u && c.kth >= emax);
+        if (exact) {
+            if (with_idx) {
+                spec_emit<false>(p, b, bh, 0, mu, c, LdsKeys{keys}, keys, sh, fs, sm.last, LdsIdx{lidx});
+            } else {
+                // the row index of used slot j: slot j - s_off[sl] of the slice sl holding it
+                auto used_idx = [&](int j) {
+                    int sl = 0;
+                    while (sl + 1 < p.slices && s_off[sl + 1] <= j) ++sl;
+                    return static_cast<int>(ci[static_cast<size_t>(sl) * p.cand_cap + (j - s_off[sl])]);
+                };
+                spec_emit<false>(p, b, bh, 0, mu, c, LdsKeys{keys}, keys, sh, fs, sm.last, used_idx);
+            }
+            return;
+        }
+    } else {
+        if (p.mode == IG_SEL_THRESHOLD) {
+            for (int i0 = tid; i0 < m; i0 += kSpecThreads * U) {
+                uint32_t v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < m ? ck[i0 + u * kSpecThreads] : 0u;
+                for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < m ? ck[i0 + u * kSpecThreads] : 0u;
 #pragma unroll
-            for (int u = 0; u < U; ++u) kmax = v[u] > kmax ? v[u] : kmax;
+                for (int u = 0; u < U; ++u) kmax = v[u] > kmax ? v[u] : kmax;
+            }
+        }
+        const uint32_t kmax_all = block_max_u32(kmax, sh);  // (also the barrier after fast_sel_init)
+        const SelCut c = spec_cut<false>(p, m, p.n, kmax_all, GlobalKeys{ck}, sh, fs);
+        exact = !checked || (c.kth != 0u && c.kth >= emax);
+        if (exact) {
+            spec_emit<false>(p, b, bh, 0, m, c, GlobalKeys{ck}, keys, sh, fs, sm.last, gidx);
+            return;
         }
     }
-    const uint32_t kmax_all = block_max_u32(kmax, sh);  // (also the barrier after fast_sel_init)
-    spec_select<false>(p, b, bh, 0, m, p.n, kmax_all, GlobalKeys{ck}, keys, sh, fs, sm.last, gidx);
+    // the recompute (top-k only): the row's n keys from its partial keys and the scaled partial query;
+    // the workspace counts the rows recomputed (word 4 of the status region)
+    if (tid == 0 && p.status) atomicAdd(p.status + 4, 1u);
+    __syncthreads();  // every wave is done with the candidate cut's scratch
+    if (tid < R) sm.q[tid] = p.q_rows[static_cast<size_t>(bh) * R + tid];
+    fast_sel_init(fs);
+    __syncthreads();
+    const RowKeys<T, LPR> rk{static_cast<const T*>(p.Kp) + static_cast<size_t>(bh) * p.n_cap * R, sm.q};
+    spec_select<false>(p, b, bh, 0, p.n, p.n, 0u, rk, keys, sh, fs, sm.last, IdentityIdx());
 }
 
 }  // namespace ig

@@ -19,23 +19,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
 
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part, int nsplit, int d,
                                                       float* __restrict__ out, float* __restrict__ lse) {
-    const int bh = blockIdx.x;
-    const float* pp = part + static_cast<size_t>(bh) * nsplit * (2 + d);
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (2 + d)]);
-    for (int t = threadIdx.x; t < d; t += blockDim.x) {
-        float L = 0.f, A = 0.f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < nsplit; ++s) {
-                const float ms = pp[s * (2 + d)];
-                const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
-                L += pp[s * (2 + d) + 1] * w;
-                A += pp[s * (2 + d) + 2 + t] * w;
-            }
-        }
-        out[static_cast<size_t>(bh) * d + t] = L > 0.f ? A / L : 0.f;
-        if (lse && t == 0) lse[bh] = L > 0.f ? M + __logf(L) : -INFINITY;
-    }
+    combine_item(CombineArgs{part, nsplit, d, out, lse}, blockIdx.x);
 }
 
 AttnPlan plan_attn(int B, int H, int d, int max_out) {

@@ -5,12 +5,14 @@
 // the attention of layer l over the rows its speculation selected, beside the
 // speculation for layer l+1 (scores, selection and counters).
 //
-// One grid holds three roles, in this order: the partial-query projection
-// workgroups for layer l+1, one spec_row workgroup per (b, h) for layer l+1,
-// which waits only for the projection workgroups (lower indices, never waiting
-// themselves), then the attention items of layer l (one (b, h, split) each,
-// all 1024 threads of the workgroup on it), which take the slots the
-// projection leaves.  The row workgroups are resident from the start, with
+// One grid holds three roles: the partial-query projection workgroups for
+// layer l+1 first, then one spec_row workgroup per (b, h) (or per slice of a
+// long row) for layer l+1, which waits only for the projection workgroups
+// (lower indices, never waiting themselves), and the attention items of layer
+// l (one (b, h, split) each, all 1024 threads of the workgroup on it): whole
+// rows all before the attention items, which take the slots the projection
+// leaves; slices interleaved with them (a merge launch then selects among the
+// slices' candidates).  The row workgroups are resident from the start, with
 // their first partial-key loads in flight while the partial sums are made.  The attention and the
 // speculation touch disjoint buffers; a CU holds two workgroups, and the
 // attention's K/V gathers fill the memory pipeline while the speculation is in
@@ -38,20 +40,49 @@ union DecodeShared {
 // faster at 205-218 rows per item).
 constexpr int kDecodeSpecBatch = 4;
 
+// The roles of the nr + na workgroups after the projection's (nr row workgroups, na attention items):
+// with a_per > 0 (sliced rows, whose many slice workgroups come in several waves), blocks of a_per row
+// workgroups and one attention item, until one kind runs out, then the rest of the other, so that the
+// attention's gathers run beside the slices' streams; else every row workgroup first.  Row and item
+// indices each count up from 0 in position order.
+__device__ __forceinline__ void decode_role(int c, int nr, int na, int a_per, int* row, int* item) {
+    *row = -1;
+    *item = -1;
+    if (a_per <= 0) {
+        if (c < nr) *row = c; else *item = c - nr;
+        return;
+    }
+    const int64_t per = a_per + 1;
+    // the position where the pattern runs out of one kind: the end of the last attention item's block,
+    // or just after the last row's slot
+    const bool items_first = static_cast<int64_t>(na) * a_per <= nr;
+    const int64_t c_end = items_first ? na * per : (nr / a_per) * per + nr % a_per;
+    if (c < c_end) {
+        const int blk = static_cast<int>(c / per), off = static_cast<int>(c - blk * per);
+        if (off < a_per) *row = blk * a_per + off; else *item = blk;
+    } else if (items_first) {
+        *row = static_cast<int>(static_cast<int64_t>(na) * a_per + (c - c_end));
+    } else {
+        *item = static_cast<int>(nr / a_per + (c - c_end));
+    }
+}
+
 template <typename T, int LPR_S, int LPR_A, int ROWS>
-__global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int bh_attn) {
+__global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int bh_attn,
+                                                                     int a_per) {
     extern __shared__ __align__(16) uint32_t keys[];  // staged x (projection) or the speculation's score keys
     __shared__ DecodeShared<LPR_S * Vec<T>::N, LPR_A, Vec<T>::N> sm;
     const int wg = blockIdx.x;
-    const int n_spec = p.proj_wgs + p.row_wgs;
     if (wg < p.proj_wgs) {
         proj_role<T>(p, wg, keys);
-    } else if (wg < n_spec) {
-        spec_row<T, LPR_S, kDecodeSpecBatch>(p, wg - p.proj_wgs, keys, sm.spec);
-    } else {
-        const int item = wg - n_spec;
-        attn_item<T, LPR_A, kDecodeThreads, ROWS>(a, item % bh_attn, item / bh_attn, sm.attn);
+        return;
     }
+    int row, item;
+    decode_role(wg - p.proj_wgs, p.row_wgs, a.nsplit * bh_attn, a_per, &row, &item);
+    if (row >= 0)
+        spec_row<T, LPR_S, kDecodeSpecBatch>(p, row, keys, sm.spec);
+    else
+        attn_item<T, LPR_A, kDecodeThreads, ROWS>(a, item % bh_attn, item / bh_attn, sm.attn);
 }
 
 template <typename T, int LPR_S, int LPR_A, int ROWS>
@@ -64,9 +95,11 @@ static int launch_fused(const SpecParams& p, const AttnArgs& a, int bh_attn, hip
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
-    const int grid = p.proj_wgs + p.row_wgs + a.nsplit * bh_attn;
+    const int items = a.nsplit * bh_attn;
+    const int grid = p.proj_wgs + p.row_wgs + items;
+    const int a_per = p.slices > 1 ? (p.row_wgs + items - 1) / items : 0;
     hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A, ROWS>), dim3(grid), dim3(kDecodeThreads),
-                       speculate_lds_bytes(p.n), s, p, a, bh_attn);
+                       speculate_lds_bytes(p.slice_rows), s, p, a, bh_attn, a_per);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -75,9 +108,11 @@ static int lpr_of(int len, int dtype) { return len / (dtype == IG_BF16 ? 8 : 4);
 
 bool decode_fusable(const AttnCall& a, const SpecCall& s) {
     const int ls = lpr_of(s.r, s.dtype), la = lpr_of(a.d, a.dtype);
-    return a.dtype == s.dtype && s.n <= kDecodeMaxRows &&
-           plan_speculate(s.B, s.H, s.D, s.r, s.n, s.max_out, s.dtype).slices == 1 &&
-           (ls == 2 || ls == 4 || ls == 8) && (la == 8 || la == 16 || la == 32);
+    const SpecPlan sp = plan_speculate(s.B, s.H, s.D, s.r, s.n, s.max_out, s.dtype, s.mode);
+    // whole rows up to kDecodeMaxRows keys, or slices small enough for two workgroups per CU
+    const bool rows_ok = sp.slices == 1 ? s.n <= kDecodeMaxRows : sp.slice_rows <= kTopkSliceRows;
+    return a.dtype == s.dtype && sp.ok && rows_ok && (ls == 2 || ls == 4 || ls == 8) &&
+           (la == 8 || la == 16 || la == 32);
 }
 
 template <typename T, int LPR_S, int LPR_A>
@@ -134,7 +169,13 @@ int launch_decode_layer(const AttnCall* a, const SpecCall* sc, hipStream_t s) {
     const int bh = a->B * a->H;
     e = a->dtype == IG_BF16 ? launch_fused_t<uint16_t>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s)
                             : launch_fused_t<float>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s);
-    if (e || ap.nsplit == 1) return e;
+    if (e) return e;
+    if (p.slices > 1) {
+        // the merge (whose workgroups also combine the attention's splits), then the counters
+        const CombineArgs cb{ap.nsplit > 1 ? aa.part : nullptr, ap.nsplit, a->d, a->out, a->lse};
+        return finish_speculate(p, sc->dtype, sc->ws, s, cb);
+    }
+    if (ap.nsplit == 1) return 0;
     return launch_attn_combine(aa.part, ap.nsplit, a->d, bh, a->out, a->lse, s);
 }
 

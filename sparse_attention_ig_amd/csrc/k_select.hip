@@ -208,7 +208,7 @@ static int launch_select_sliced(const SelectPlan& sp, const float* scores, int B
     hipLaunchKernelGGL(k_select_slice, dim3(B * H * sp.sl.slices), dim3(kSpecThreads),
                        speculate_lds_bytes(sp.sl.slice_rows), s, p, scores, ld);
     const int e = static_cast<int>(hipGetLastError());
-    return e ? e : launch_spec_merge(p, s);
+    return e ? e : launch_spec_merge(p, IG_F32, s);
 }
 
 int launch_select(const float* scores, int B, int H, int n, int ld, int mode, float alpha, int k, int max_sel,

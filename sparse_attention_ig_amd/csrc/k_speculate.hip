@@ -23,35 +23,56 @@ __global__ __launch_bounds__(kSpecThreads, 8) void k_speculate(SpecParams p) {
         spec_row<T, LPR, 4>(p, wg - p.proj_wgs, keys, sm);
 }
 
-__global__ __launch_bounds__(kSpecThreads) void k_spec_merge(SpecParams p) {
+// One workgroup per row: the merge of the row's slices; in a decode layer whose attention is split, the
+// same workgroup index also combines that attention's splits of (b, h) = blockIdx.x (B and H are shared).
+template <typename T, int LPR>
+__global__ __launch_bounds__(kSpecThreads) void k_spec_merge(SpecParams p, CombineArgs cb) {
     extern __shared__ __align__(16) uint32_t keys[];  // the candidates' keys (up to kSpecMaxRows), or scratch
-    __shared__ SpecShared<kSpecMaxSlices + 1> sm;
-    spec_merge(p, blockIdx.x, keys, sm);
+    __shared__ SpecShared<LPR * Vec<T>::N> sm;
+    spec_merge<T, LPR>(p, blockIdx.x, keys, sm);
+    if (cb.part) combine_item(cb, blockIdx.x);
 }
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-SlicePlan plan_slices(int64_t rows, int n, int max_out) {
+// Candidate slots of a slice of `rows` of a row's n rows for a top-k selection of up to max_out rows
+// with tight candidates: twice the slice's share of the budget with its margin (tight_slice_k on the
+// device), and 64 more, so that a sampled bound of the slice's cut usually fits.
+static int tight_cap(int max_out, int rows, int n) {
+    const double e = static_cast<double>(max_out) * rows / n;
+    const int want = static_cast<int>(std::ceil(e + 5.0 * std::sqrt(e) + 8.0));
+    return std::min(rows, 2 * want + 64);
+}
+
+SlicePlan plan_slices(int64_t rows, int n, int max_out, bool topk) {
     // slices per row: enough for every row to fit in LDS, more (up to 16, at least 2048 rows each) when
     // there are too few rows to fill the chip; fewer while the merge's candidates would not fit its LDS,
-    // down to what the occupancy needs (a merge over more candidates reads them from global memory)
+    // down to what the occupancy needs (a merge over more candidates reads them from global memory).
+    // Top-k rows that are sliced at all get slices of at most kTopkSliceRows rows (two workgroups per
+    // CU, also beside attention workgroups) with tight candidates, whose merge stays small.
     const int s_min = (n + kSpecMaxRows - 1) / kSpecMaxRows;
     int S = static_cast<int>(std::min<int64_t>(kSpecMaxSlices, (256 + rows - 1) / rows));
     S = std::min(S, std::max(1, n / 2048));
     S = std::max(S, s_min);
     int slice_rows = 0, cap = 0;
-    // candidate slots per slice: for large selections max_out and half again, so that a slice can hand
-    // on every key above a sampled bound of its cut instead of finding the exact cut (small selections
-    // find the exact cut cheaply, and more slots would only grow the merge)
-    const int slack = max_out >= kSliceSlackMin
-                          ? static_cast<int>(std::min<int64_t>(static_cast<int64_t>(max_out) + max_out / 2 + 64,
-                                                               INT32_MAX))
-                          : max_out;
-    for (;;) {
+    if (topk && S > 1) {
+        S = std::max(S, std::min(kSpecMaxSlices, (n + kTopkSliceRows - 1) / kTopkSliceRows));
         slice_rows = (n + S - 1) / S;
-        cap = std::min(slice_rows, slack);
-        if (S == 1 || static_cast<int64_t>(S) * cap <= kSpecMaxRows || S == s_min) break;
-        --S;
+        cap = tight_cap(max_out, slice_rows, n);
+    } else {
+        // candidate slots per slice: for large selections max_out and half again, so that a slice can hand
+        // on every key above a sampled bound of its cut instead of finding the exact cut (small selections
+        // find the exact cut cheaply, and more slots would only grow the merge)
+        const int slack = max_out >= kSliceSlackMin
+                              ? static_cast<int>(std::min<int64_t>(static_cast<int64_t>(max_out) + max_out / 2 + 64,
+                                                                   INT32_MAX))
+                              : max_out;
+        for (;;) {
+            slice_rows = (n + S - 1) / S;
+            cap = std::min(slice_rows, slack);
+            if (S == 1 || static_cast<int64_t>(S) * cap <= kSpecMaxRows || S == s_min) break;
+            --S;
+        }
     }
     SlicePlan pl{};
     pl.slices = (n + slice_rows - 1) / slice_rows;
@@ -61,38 +82,49 @@ SlicePlan plan_slices(int64_t rows, int n, int max_out) {
     return pl;
 }
 
-SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype) {
+SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype, int mode) {
     SpecPlan sp{};
     const int64_t rows = static_cast<int64_t>(B) * H;
-    const SlicePlan pl = plan_slices(rows, n, max_out);
-    const int S = pl.slices;
+    // the workspace serves both modes (its size query knows no mode): regions sized for the larger plan
+    const SlicePlan thr = plan_slices(rows, n, max_out, false);
+    const SlicePlan tk = plan_slices(rows, n, max_out, true);
+    const SlicePlan& pl = mode == IG_SEL_TOPK ? tk : thr;
     sp.ok = pl.ok;
-    sp.slices = S;
+    sp.slices = pl.slices;
     sp.slice_rows = pl.slice_rows;
     sp.cand_cap = pl.cap;
-    const size_t cands = static_cast<size_t>(rows) * S * sp.cand_cap;
+    sp.tight = mode == IG_SEL_TOPK && pl.slices > 1;
+    const int s_max = std::max(thr.slices, tk.slices);
+    const size_t cands = static_cast<size_t>(rows) *
+                         std::max(static_cast<size_t>(thr.slices) * thr.cap, static_cast<size_t>(tk.slices) * tk.cap);
     // projection workgroups: column blocks x splits of the D inputs
     sp.proj_blocks = (H * r + kProjCols - 1) / kProjCols;
     sp.splits = (D + kProjSplit - 1) / kProjSplit;
     sp.proj_wgs = sp.proj_blocks * sp.splits;
     sp.off_status = 0;  // status word at 0, shape stamp at 8 (one 256-byte region)
     sp.off_arrive = 256;
-    sp.off_pdone = sp.off_arrive + align256(static_cast<size_t>(B) * sizeof(uint32_t));
-    sp.off_part = sp.off_pdone + align256(static_cast<size_t>(rows) * sizeof(uint32_t));
+    sp.off_part = sp.off_arrive + align256(static_cast<size_t>(B) * sizeof(uint32_t));
     sp.off_cnt = sp.off_part + align256(static_cast<size_t>(sp.splits) * B * H * r * sizeof(float));
-    sp.off_key = sp.off_cnt + (S > 1 ? align256(static_cast<size_t>(rows) * S * sizeof(int32_t)) : 0);
-    sp.off_idx = sp.off_key + (S > 1 ? align256(cands * sizeof(uint32_t)) : 0);
+    const bool sliced = s_max > 1;
+    sp.off_lo = sp.off_cnt + (sliced ? align256(static_cast<size_t>(rows) * s_max * sizeof(int32_t)) : 0);
+    sp.off_q = sp.off_lo + (sliced ? align256(static_cast<size_t>(rows) * s_max * sizeof(uint32_t)) : 0);
+    sp.off_key = sp.off_q + (tk.slices > 1 ? align256(static_cast<size_t>(rows) * r * sizeof(float)) : 0);
+    sp.off_idx = sp.off_key + (sliced ? align256(cands * sizeof(uint32_t)) : 0);
     // many selected slots per sequence: counter atomics in the merge would be throughput-bound
-    sp.bits = S > 1 && H <= 128 && rows * std::min(max_out, n) >= kBitsTouchMin;
+    auto uses_bits = [&](const SlicePlan& q) {
+        return q.slices > 1 && H <= 128 && rows * std::min(max_out, n) >= kBitsTouchMin;
+    };
+    sp.bits = uses_bits(pl);
+    const bool any_bits = uses_bits(thr) || uses_bits(tk);
     const size_t nw = (static_cast<size_t>(n) + 31) / 32;
-    sp.off_bits = sp.off_idx + (S > 1 ? align256(cands * sizeof(int32_t)) : 0);
-    sp.off_flags = sp.off_bits + (sp.bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
-    sp.ws_bytes = sp.off_flags + (sp.bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
+    sp.off_bits = sp.off_idx + (sliced ? align256(cands * sizeof(int32_t)) : 0);
+    sp.off_flags = sp.off_bits + (any_bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
+    sp.ws_bytes = sp.off_flags + (any_bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
     return sp;
 }
 
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype) {
-    return plan_speculate(B, H, D, r, n, max_out, dtype).ws_bytes;
+    return plan_speculate(B, H, D, r, n, max_out, dtype, IG_SEL_TOPK).ws_bytes;  // the same for every mode
 }
 
 // keys for the rows of a workgroup; at least the projection workgroups' slice results (which also
@@ -130,19 +162,45 @@ static int launch_spec_t(const SpecParams& p, hipStream_t s) {
     }
 }
 
-int launch_spec_merge(const SpecParams& p, hipStream_t s) {
+template <typename T, int L>
+static int launch_merge_tl(const SpecParams& p, const CombineArgs& cb, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_spec_merge),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_spec_merge<T, L>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  static_cast<int>(speculate_lds_bytes(kSpecMaxRows)));
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
-    const int m = p.slices * p.cand_cap;
-    const int words = std::max(m <= kSpecMaxRows ? m : 0, p.bits ? (p.n + 31) / 32 : 0);  // keys or the bitmap
-    hipLaunchKernelGGL(k_spec_merge, dim3(p.B * p.H), dim3(kSpecThreads), speculate_lds_bytes(words), s, p);
+    // the used candidates' keys and row indices (at most twice the slots, at most the LDS key store), or
+    // the bitmap
+    const int64_t m = static_cast<int64_t>(p.slices) * p.cand_cap;
+    const int words = static_cast<int>(std::max<int64_t>(std::min<int64_t>(2 * m, kSpecMaxRows),
+                                                         p.bits ? (p.n + 31) / 32 : 0));
+    hipLaunchKernelGGL((k_spec_merge<T, L>), dim3(p.B * p.H), dim3(kSpecThreads), speculate_lds_bytes(words), s, p,
+                       cb);
     return static_cast<int>(hipGetLastError());
+}
+
+template <typename T>
+static int launch_merge_t(const SpecParams& p, const CombineArgs& cb, hipStream_t s) {
+    switch (p.r / Vec<T>::N) {
+        case 1: return launch_merge_tl<T, 1>(p, cb, s);
+        case 2: return launch_merge_tl<T, 2>(p, cb, s);
+        case 4: return launch_merge_tl<T, 4>(p, cb, s);
+        case 8: return launch_merge_tl<T, 8>(p, cb, s);
+        case 16: return launch_merge_tl<T, 16>(p, cb, s);
+        case 32: return launch_merge_tl<T, 32>(p, cb, s);
+        default: return static_cast<int>(hipErrorInvalidValue);
+    }
+}
+
+// The merge launch of sliced rows; dtype and p.r pick the instance whose recompute reads the partial keys
+// (a merge without tight candidates never recomputes: any instance serves it).  cb: an attention split
+// combine to run in the same workgroups (part NULL: none).
+int launch_spec_merge(const SpecParams& p, int dtype, hipStream_t s, const CombineArgs& cb) {
+    if (!p.tight) return launch_merge_tl<float, 1>(p, cb, s);
+    return dtype == IG_BF16 ? launch_merge_t<uint16_t>(p, cb, s) : launch_merge_t<float>(p, cb, s);
 }
 
 // Failure-path testing (ig_set_handover_test_mode): the row workgroups' poll limit, and whether the
@@ -162,7 +220,7 @@ unsigned long long spec_shape_key(int B, int H, int D, int r) {
 }
 
 int begin_speculate(const SpecCall& c, SpecParams* p) {
-    const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
+    const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype, c.mode);
     char* ws = static_cast<char*>(c.ws);
     // all batch rows of a head on one XCD when the heads split evenly over the 8 XCDs
     *p = SpecParams{c.x, c.Wq_part, c.D, reinterpret_cast<float*>(ws + sp.off_part), sp.splits, c.bq_part, c.Kp, c.B,
@@ -175,12 +233,14 @@ int begin_speculate(const SpecCall& c, SpecParams* p) {
     p->proj_wgs = sp.proj_wgs;
     p->proj_blocks = sp.proj_blocks;
     p->row_wgs = c.B * c.H * sp.slices;
-    p->pdone = reinterpret_cast<uint32_t*>(ws + sp.off_pdone);
     p->status = reinterpret_cast<uint32_t*>(ws + sp.off_status);
     p->stamp = reinterpret_cast<unsigned long long*>(ws + sp.off_status + 8);
     p->key = spec_shape_key(c.B, c.H, c.D, c.r);
     p->spin_limit = g_spin_limit;
     p->withhold = g_withhold;
+    p->tight = sp.tight ? 1 : 0;
+    if (sp.slices > 1) p->cand_lo = reinterpret_cast<uint32_t*>(ws + sp.off_lo);
+    if (sp.tight) p->q_rows = reinterpret_cast<float*>(ws + sp.off_q);
     return 0;
 }
 
@@ -195,10 +255,16 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     if (e) return e;
     e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
     if (e || p.slices == 1) return e;
-    if ((e = launch_spec_merge(p, s)) || !p.bits) return e;
-    const SpecPlan sp = plan_speculate(B, H, D, r, n, max_out, dtype);
-    return launch_touch_bits(counters, p.bits, B, H, n, n_cap, cmax,
-                             reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), victim, s);
+    return finish_speculate(p, dtype, ws, s);
+}
+
+// After the launch of sliced rows: the merge, and the counter kernels when the merge leaves bitmaps.
+int finish_speculate(const SpecParams& p, int dtype, void* ws, hipStream_t s, const CombineArgs& cb) {
+    int e = launch_spec_merge(p, dtype, s, cb);
+    if (e || !p.bits) return e;
+    const SpecPlan sp = plan_speculate(p.B, p.H, p.D, p.r, p.n, p.max_out, dtype, p.mode);
+    return launch_touch_bits(p.counters, p.bits, p.B, p.H, p.n, p.n_cap, p.cmax,
+                             reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), p.victim, s);
 }
 
 // ------------------------------------------------------------------ ig_speculate_noalloc
@@ -239,7 +305,7 @@ __global__ void k_scratch_reset(uint32_t* ws, size_t words, unsigned long long k
 }
 
 int launch_speculate_noalloc(const SpecCall& c, hipStream_t s) {
-    const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype);
+    const SpecPlan sp = plan_speculate(c.B, c.H, c.D, c.r, c.n, c.max_out, c.dtype, c.mode);
     if (sp.ws_bytes > kNoAllocScratchBytes) return static_cast<int>(hipErrorInvalidValue);  // checked before
     void* ws = nullptr;
     int e = noalloc_scratch(&ws);

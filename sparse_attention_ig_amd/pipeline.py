@@ -11,6 +11,12 @@ The speculation for layer l+1 runs at layer l from layer l's attention input
 both in one ig_decode_layer call (the two run side by side on the GPU),
 and after the last layer every layer appends the new token's key and value (ig_append_kv), which
 also writes the partial-key row and restarts the slot's counter.
+
+Once the cache is full (n = n_cap) an append overwrites each sequence's victim, the slot with the
+smallest access counter (the summary's counter-based eviction, section 3.4 "KV Cache Pool Management
+Under Memory Pressure"): layers 1.. take it from their speculation (which then asks for it); layer 0,
+which no speculation selects for (it attends to every row), takes the lowest slot among the minima of
+its counters, which only appends reset (ig_pool_touch with empty selections).
 """
 from __future__ import annotations
 
@@ -34,6 +40,7 @@ class DecodePipeline:
         self.max_out = max_out
         self.dense_count = torch.full((s.B, s.H), s.n, dtype=torch.int32, device="cuda")
         self.slot = torch.empty((s.B,), dtype=torch.int32, device="cuda")
+        self.no_count = torch.zeros((s.B, s.H), dtype=torch.int32, device="cuda")
 
     def topk(self) -> int:
         """Fixed budget of the pipeline workload: 5% of the current context."""
@@ -56,7 +63,7 @@ class DecodePipeline:
             spec = None
             if l + 1 < nl:
                 spec = spec_call(self.layers[l + 1], mode=mode, alpha=alpha, k=k, max_sel=max_sel, cmax=self.cmax,
-                                 n=n, x=x_layers[l])
+                                 n=n, x=x_layers[l], want_victim=n == s.cap)
             L.ig_decode_layer(attn, spec, stream=stream)
         if append:
             self.append(k_new, v_new, stream=stream)
@@ -64,7 +71,11 @@ class DecodePipeline:
     def append(self, k_new, v_new, *, stream=None):
         """Every layer appends the new token's key and value rows (slot n, or the victim when full)."""
         n = self.n
+        full = n == self.spec.cap
         for l, lay in enumerate(self.layers):
+            if full and l == 0:
+                L.ig_pool_touch(lay.counters, lay.idx, self.no_count, n, self.cmax, victim=lay.victim, ws=lay.ws,
+                                stream=stream)
             L.ig_append_kv(lay.K, lay.V, lay.Kp, lay.counters, lay.chan, k_new[l], v_new[l], n,
-                           slot_out=self.slot, stream=stream)
+                           victim=lay.victim if full else None, slot_out=self.slot, stream=stream)
         self.n = min(n + 1, self.spec.cap)

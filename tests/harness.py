@@ -95,15 +95,9 @@ def oracle_step(inp: Inputs, *, mode: str, alpha: float = math.inf, k: int = 0, 
     if Kp is None:
         Kp = O.partial_key_cache(inp.K, inp.chan)
     if heads is None:
-        qp, sc = O.rehearse(x, Wp, O.decode(Kp, dt), s.n, s.H, s.r, s.softmax_scale)
-        idx, cnt = _oracle_select(sc, mode, alpha, k, max_sel, max_out)
-        o, lse = O.sparse_decode_attn(O.decode(inp.q, dt), O.decode(inp.K, dt), O.decode(inp.V, dt), idx, cnt,
-                                      s.softmax_scale)
-        res = dict(q_part=qp, scores=sc, idx=idx, count=cnt, out=o, lse=lse)
-        if counters is not None:
-            C2, v = O.pool_touch(counters, idx, cnt, s.n, cmax, want_victim)
-            res.update(counters=C2, victim=v)
-        return res
+        return O.decode_step(x, Wp, O.decode(Kp, dt), O.decode(inp.q, dt), O.decode(inp.K, dt), O.decode(inp.V, dt),
+                             counters, n=s.n, H=s.H, r=s.r, scale=s.softmax_scale, mode=mode, alpha=alpha, k=k,
+                             max_sel=max_sel, max_out=max_out, cmax=cmax, want_victim=want_victim)
     return oracle_heads(inp, mode=mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out, heads=heads)[0]
 
 
@@ -267,6 +261,7 @@ def oracle_pipeline(spec: gen.Spec, xs, ins, new, max_out: int, cmax: int = 6553
     C = [np.zeros((spec.B, spec.cap), np.uint32) for _ in ins]
     idx = [None] * L
     cnt = [None] * L
+    victim = [None] * L
     n = spec.n
     trace = []
     for t in range(xs.shape[0]):
@@ -284,11 +279,20 @@ def oracle_pipeline(spec: gen.Spec, xs, ins, new, max_out: int, cmax: int = 6553
                 _, sc = O.rehearse(O.decode(xs[t, l], dt), O.decode(ins[l + 1].Wq_part, dt),
                                    O.decode(Kp[l + 1], dt), n, spec.H, spec.r, spec.softmax_scale)
                 idx[l + 1], cnt[l + 1] = O.select(sc, "topk", k=k, max_out=max_out)
-                C[l + 1], _ = O.pool_touch(C[l + 1], idx[l + 1], cnt[l + 1], n, cmax)
+                C[l + 1], victim[l + 1] = O.pool_touch(C[l + 1], idx[l + 1], cnt[l + 1], n, cmax, want_victim=True)
                 rec["idx"][l + 1], rec["count"][l + 1], rec["scores"][l + 1] = idx[l + 1], cnt[l + 1], sc
+        full = n == spec.cap
+        if full:
+            # layer 0 attends to every row and no speculation selects for it: its victim is the lowest
+            # slot among the minima of counters that only appends reset
+            _, victim[0] = O.pool_touch(C[0], np.zeros((spec.B, spec.H, 1), np.int32),
+                                        np.zeros((spec.B, spec.H), np.int32), n, cmax, want_victim=True)
+        rec["victims"] = [None if v is None else v.copy() for v in victim] if full else None
         for l in range(L):
             kn, vn = new[t][l]
-            _, n2 = O.pool_append(K[l], V[l], Kp[l], C[l], ins[l].chan, kn, vn, n)
+            _, n2 = O.pool_append(K[l], V[l], Kp[l], C[l], ins[l].chan, kn, vn, n,
+                                  victim=victim[l] if full else None)
         n = n2
         trace.append(rec)
+    trace[-1]["K"] = K   # the caches after the last append
     return trace, C

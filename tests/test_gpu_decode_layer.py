@@ -4,13 +4,16 @@ The InfiniGen summary (arXiv 2406.19707, paper-graph-ui, section 3.2 "Big-Pictur
 runs the speculation for the next layer while the current layer computes.  The fused call must give
 what the two separate calls give:
   speculation half   idx, count, counters, q_part bit-exact against ig_speculate on a copy of the layer
-                     (same arithmetic per row; only the number of rows in flight differs);
+                     (same arithmetic per row; only the number of rows in flight differs), and against
+                     the oracle on its own inputs (q_part within 1e-3, every head's set outside the
+                     1e-4 band, counters slot by slot);
   attention half     within 1e-5 relative of ig_sparse_decode_attn on a copy (the lane groups
                      associate the float sums differently), and within the bf16/f32 attention tolerance
                      of the oracle on the selected rows.
-Covered: the fused shapes (bf16 and f32, more than 16 batch rows), an attention split into several
-workgroups with the combine, a shape outside the fused set (two launches), either half alone, and the
-aliasing check.
+Covered: the fused shapes (bf16 and f32, more than 16 batch rows), the benchmark's OPT-6.7B shape, an
+attention with two K/V rows per lane group in flight (256 items of 218 rows), an attention split into
+several workgroups with the combine, a shape outside the fused set (two launches), either half alone,
+and the aliasing check.
 """
 
 import numpy as np
@@ -55,6 +58,17 @@ CASES = [
     ("bf16-batch20-r16", lambda: _spec(gen.opt_6_7b(n=600, B=20), H=3, r=16, heavy=12, topk=50),
      lambda: _spec(gen.opt_6_7b(n=640, B=20), H=3, r=16, heavy=12, topk=50, seed=2007),
      dict(mode="topk", k=50, max_out=50)),
+    # 256 (b, h) items of 218 rows (the Llama-2-13B 5% budget): the attention role keeps two K/V rows
+    # per lane group in flight
+    ("bf16-rows2-218", lambda: _spec(gen.opt_6_7b(n=4352, B=8), topk=218),
+     lambda: _spec(gen.opt_6_7b(n=4352, B=8), topk=218, seed=2008), dict(mode="topk", k=218, max_out=218)),
+    # a long speculated row cut into 16 slices of 2500 rows (tight top-k candidates, a merge launch),
+    # its slice workgroups interleaved with the attention items in the one launch
+    ("bf16-sliced-topk", lambda: _spec(gen.opt_6_7b(n=3000, B=1), H=4, topk=400),
+     lambda: _spec(gen.llama2_7b_long(n=40000, B=1), H=4, topk=400, seed=2009), dict(mode="topk", k=400, max_out=400)),
+    # 128 rows of 65536 keys, top 2048: slices of 8192, counters from the merge's bitmaps
+    ("bf16-sliced-bitmaps", lambda: _spec(gen.opt_6_7b(n=4000, B=4), topk=2048),
+     lambda: _spec(gen.llama2_7b_long(n=65536, B=4), topk=2048, seed=2010), dict(mode="topk", k=2048, max_out=2048)),
 ]
 
 
@@ -92,6 +106,17 @@ def test_decode_layer_matches_separate_calls(name, attn_fn, spec_fn, kw):
             assert np.array_equal(g_b["idx"][b, h, :c], r_b["idx"][b, h, :c]), (b, h)
     assert np.array_equal(g_b["counters"], r_b["counters"])
     assert np.array_equal(g_b["q_part"].view(np.uint32), r_b["q_part"].view(np.uint32))
+    # ... and against the oracle on its own inputs: q_part, every head's set, the counters slot by slot
+    oi_b = harness.oracle_inputs(sb)
+    harness.assert_setup_routes_agree(li_b, oi_b)
+    mode = kw["mode"]
+    ref, ri, rc = harness.oracle_heads(oi_b, mode=mode, alpha=kw.get("alpha", np.inf), k=kw.get("k", 0),
+                                       max_sel=kw.get("max_sel", 0), max_out=kw["max_out"], attn=False)
+    inexact = harness.check_heads(g_b["idx"], g_b["count"], ref, mode, kw.get("alpha", np.inf),
+                                  g_q_part=g_b["q_part"])
+    assert len(inexact) <= max(1, sb.B * sb.H // 50), inexact
+    rC, _ = O.pool_touch(np.zeros((sb.B, sb.cap), np.uint32), ri, rc, sb.n, 65535)
+    harness.check_counters(g_b["counters"].view(np.uint32), rC, g_b["idx"], g_b["count"], ri, rc, sb.n)
 
     # attention half: against ig_sparse_decode_attn and against the oracle on the selected rows
     scale = np.abs(r_a["out"]).max(axis=-1, keepdims=True) + 1e-30

@@ -10,7 +10,8 @@ on its own, decoding only that head's rows):
     4096-row draw per layer; counters accumulate over the three steps): speculation in HBM, zero-copy
     gather, attention;
   * the long-context Llama-2-7B layer at its largest size (B4, n = 131072, top 4%, the benchmark's
-    workload).
+    workload): the fused speculation, and ig_decode_layer as the benchmark calls it (the speculation's
+    slices beside the attention of the layer before, in one launch).
 
 Selections must match outside the 1e-4 band; attention within 1e-2 (bf16) where the sets are equal;
 counters slot by slot (only slots of band-differing heads may move, by at most that many).
@@ -128,8 +129,8 @@ def test_pool_full_size_sampled_layers_and_steps(layer):
 
 def test_long_context_b4_full_size():
     """Llama-2-7B-shaped layer at 131072 rows, batch 4, top 4% (5243 rows per head), the fused path:
-    the projection workgroups, 4 slices of 32768 rows per row, a merge of the slices' candidates per row,
-    counters from the rows' bitmaps; then the attention split over the selected rows.  Every head
+    the projection workgroups, 16 slices of 8192 rows per row handing on tight candidates, a merge per
+    row, counters from the rows' bitmaps; then the attention split over the selected rows.  Every head
     against the oracle, counters slot by slot."""
     from sparse_attention_ig_amd.runtime import DeviceLayer
     from tests.gpu_util import to_host
@@ -148,3 +149,43 @@ def test_long_context_b4_full_size():
     rC, rv = O.pool_touch(np.zeros((spec.B, spec.cap), np.uint32), ri, rc, spec.n, 65535, want_victim=True)
     moved = harness.check_counters(g["counters"], rC, g["idx"], g["count"], ri, rc, spec.n, g["victim"], rv)
     say(f"[long b4 full] {spec.B * spec.H} heads, {len(inexact)} band-affected, counters moved in {len(moved)}")
+
+
+def test_long_context_b4_decode_layer_full_size():
+    """ig_decode_layer at the benchmark's workload (B4, n = 131072, top 4%): the attention of a layer
+    over its own speculated rows beside the speculation of a copy of it (16 slices of 8192 rows per row,
+    interleaved with the attention items; a merge and the bitmap counter kernels after).  Every head of
+    both halves against the oracle (one layer's draws serve both: a copy has the same caches)."""
+    import torch
+    from sparse_attention_ig_amd.runtime import DeviceLayer, decode_layer
+    from tests.gpu_util import to_host
+    spec = gen.llama2_7b_long(n=131072, B=4, frac=0.04)
+    kw = dict(mode="topk", k=spec.topk, max_out=spec.topk)
+    say(f"[long b4 decode layer] n={spec.n} k={spec.topk}")
+    li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
+    harness.assert_setup_routes_agree(li, oi)
+    A = DeviceLayer(li, max_out=spec.topk)
+    del li
+    A.keep_scores = False
+    A.step(**kw, parts=("speculate",))          # layer l's own selection, which its attention reads
+    S = A.clone()
+    S.counters.zero_()
+    S.idx.fill_(-1)
+    decode_layer(A, S, kw)
+    torch.cuda.synchronize()
+    say("[long b4 decode layer] gpu step done")
+    from sparse_attention_ig_amd import _lib as L
+    assert L.ig_workspace_status(S.ws_spec) == 0
+    ga = to_host(dict(idx=A.idx, count=A.count, out=A.out, lse=A.lse))
+    gs = to_host(dict(idx=S.idx, count=S.count, counters=S.counters, q_part=S.q_part))
+    ref, ri, rc = harness.oracle_heads(oi, mode="topk", k=spec.topk, max_out=spec.topk)
+    # the speculation half: every head's set, q_part, counters slot by slot
+    inexact = harness.check_heads(gs["idx"], gs["count"], ref, "topk", 0.0, g_q_part=gs["q_part"])
+    assert len(inexact) <= 3, inexact
+    rC, _ = O.pool_touch(np.zeros((spec.B, spec.cap), np.uint32), ri, rc, spec.n, 65535)
+    harness.check_counters(gs["counters"].view(np.uint32), rC, gs["idx"], gs["count"], ri, rc, spec.n)
+    # the attention half, over layer l's own selection (the same rule on the same layer)
+    inexact_a = harness.check_heads(ga["idx"], ga["count"], ref, "topk", 0.0, g_out=ga["out"], g_lse=ga["lse"],
+                                    tol=harness.ATTN_TOL["bf16"])
+    assert len(inexact_a) <= 3, inexact_a
+    say(f"[long b4 decode layer] {spec.B * spec.H} heads per half, band-affected {len(inexact)} / {len(inexact_a)}")

@@ -1,5 +1,6 @@
 """GPU parity of the cross-layer decode pipeline (speculation for layer l+1 at layer l, layer 0
-dense, one appended token per step) against the oracle running the same loop on its own inputs."""
+dense, one appended token per step, the victim slot overwritten once the cache is full) against the
+oracle running the same loop on its own inputs."""
 import math
 
 import numpy as np
@@ -13,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _spec():
-    base = gen.llama2_13b(n=300, B=2, n_cap=306)
+    # two appends fill the 302 slots; the last three steps evict each layer's victim
+    base = gen.llama2_13b(n=300, B=2, n_cap=302)
     return gen.Spec(**{**base.__dict__, "H": 8, "heavy": 6})
 
 
@@ -28,7 +30,7 @@ def test_pipeline_matches_oracle():
     xs, lib_in, new = harness.pipeline_setup(spec, layers, steps, harness.lib_inputs)
     _, ora_in, _ = harness.pipeline_setup(spec, layers, steps, harness.oracle_inputs)
     for a, b in zip(lib_in, ora_in):
-        assert harness.compare_inputs(a, b)["chan"] == 0
+        harness.assert_setup_routes_agree(a, b)
     pipe = DecodePipeline(lib_in, max_out=max_out)
     trace, C_ref = harness.oracle_pipeline(spec, xs, ora_in, new, max_out)
     exact_hist = np.ones((layers, spec.B), bool)
@@ -58,12 +60,23 @@ def test_pipeline_matches_oracle():
                         assert np.abs(out[b, h] - trace[t]["out"][l][b, h]).max() <= tol, (t, l, b, h)
                     else:
                         exact_hist[l, b] = False
+        if trace[t]["victims"] is not None:
+            for l in range(layers):
+                gv = host(pipe.layers[l].victim)
+                for b in range(spec.B):
+                    if exact_hist[l, b]:
+                        assert gv[b] == trace[t]["victims"][l][b], ("victim", t, l, b)
     for l in range(1, layers):
         C = host(pipe.layers[l].counters).view(np.uint32)
         for b in range(spec.B):
             if exact_hist[l, b]:
                 assert np.array_equal(C[b], C_ref[l][b]), (l, b)
-    assert pipe.n == spec.n + steps
-    # the appended rows landed in the caches
+    assert pipe.n == min(spec.n + steps, spec.cap)
+    # the appended rows landed in the caches, the evicting appends included
     K = host(pipe.layers[1].K)
     assert np.array_equal(K[:, :, spec.n], new[0][1][0])
+    for l in range(layers):
+        Kl = host(pipe.layers[l].K)
+        for b in range(spec.B):
+            if exact_hist[l, b]:
+                assert np.array_equal(Kl[b], trace[-1]["K"][l][b]), ("cache after eviction", l, b)

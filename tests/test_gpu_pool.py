@@ -19,20 +19,31 @@ def _spec():
     return gen.Spec(**{**base.__dict__, "H": 8, "heavy": 6})
 
 
-def test_pool_step_and_eviction_match_oracle():
+def _spec_80pct():
+    # the OPT-6.7B shape with a pool of 80% of the 2048 tokens of its full cache (the summary's Table 2
+    # limit), as the benchmark's eviction run
+    cap = int(0.8 * 2048)
+    return gen.Spec(**{**gen.opt_6_7b(n=cap, B=8).__dict__, "n_cap": cap})
+
+
+@pytest.mark.parametrize("spec_fn", [_spec, _spec_80pct], ids=["opt30b-h8", "opt6.7b-80pct"])
+def test_pool_step_and_eviction_match_oracle(spec_fn):
     import torch
     from sparse_attention_ig_amd import _lib as L
     from sparse_attention_ig_amd.runtime import PoolLayer, to_device
-    spec = _spec()                 # the pool is full: every append evicts the victim
+    spec = spec_fn()               # the pool is full: every append evicts the victim
     max_sel = spec.max_sel
     say(f"[pool] B={spec.B} H={spec.H} n={spec.n} cap={spec.cap} alpha={spec.alpha} max_sel={max_sel}")
     li, oi = harness.lib_inputs(spec), harness.oracle_inputs(spec)
-    assert harness.compare_inputs(li, oi)["chan"] == 0
+    harness.assert_setup_routes_agree(li, oi)
     pool = PoolLayer(li, max_out=max_sel)
     assert np.array_equal(host(pool.Kp), O.partial_key_cache(oi.K, oi.chan))    # built from the pinned pool
     K, V, Kp = oi.K.copy(), oi.V.copy(), O.partial_key_cache(oi.K, oi.chan)
     C = np.zeros((spec.B, spec.cap), np.uint32)
     slot = torch.empty(spec.B, dtype=torch.int32, device="cuda")
+    # a sequence whose set differs from the oracle's inside the 1e-4 band (or whose victim then differs)
+    # leaves the oracle's history: it is compared no further, the others step by step
+    in_sync = set(range(spec.B))
     for step in range(3):
         pool.speculate(alpha=spec.alpha, max_sel=max_sel, want_victim=True)
         pool.gather()
@@ -43,9 +54,10 @@ def test_pool_step_and_eviction_match_oracle():
         ref = harness.oracle_step(ins, mode="threshold", alpha=spec.alpha, max_sel=max_sel, max_out=max_sel,
                                   counters=C, want_victim=True)
         gi, gc = host(pool.idx), host(pool.count)
-        Kc, Vc = host(pool.Kc), host(pool.Vc)
-        all_exact = True
-        for b in range(spec.B):
+        Kc, Vc, out = host(pool.Kc), host(pool.Vc), host(pool.out)
+        gC, victim = host(pool.counters).view(np.uint32), host(pool.victim)
+        for b in sorted(in_sync):
+            exact_b = True
             for h in range(spec.H):
                 c = gc[b, h]
                 gs, rs = gi[b, h, :c], ref["idx"][b, h, :ref["count"][b, h]]
@@ -53,14 +65,14 @@ def test_pool_step_and_eviction_match_oracle():
                 assert ok, (step, b, h)
                 assert np.array_equal(Kc[b, h, :c], K[b, h, gs]) and np.array_equal(Vc[b, h, :c], V[b, h, gs])
                 if exact:
-                    assert np.abs(host(pool.out)[b, h] - ref["out"][b, h]).max() <= harness.ATTN_TOL["bf16"]
-                else:
-                    all_exact = False
-        if not all_exact:
-            pytest.skip("a row within 1e-4 of the cut diverged the histories; counters not comparable")
-        assert np.array_equal(host(pool.counters).view(np.uint32), ref["counters"])
-        victim = host(pool.victim)
-        assert np.array_equal(victim, ref["victim"])
+                    assert np.abs(out[b, h] - ref["out"][b, h]).max() <= harness.ATTN_TOL["bf16"]
+                exact_b = exact_b and exact
+            moved = harness.check_counters(gC[b:b + 1], ref["counters"][b:b + 1], gi[b:b + 1], gc[b:b + 1],
+                                           ref["idx"][b:b + 1], ref["count"][b:b + 1], spec.n, victim[b:b + 1],
+                                           ref["victim"][b:b + 1])
+            if moved or not exact_b or victim[b] != ref["victim"][b]:
+                in_sync.discard(b)
+                say(f"[pool] step {step}: sequence {b} left the oracle's history (a row within 1e-4 of the cut)")
         C = ref["counters"].copy()
         # append the new token: the pool is full, so it overwrites the victim slot (host pool + HBM partial keys)
         kn, vn = gen.draw_new_rows(spec, 0, step)
@@ -68,7 +80,11 @@ def test_pool_step_and_eviction_match_oracle():
                        victim=pool.victim, slot_out=slot)
         torch.cuda.synchronize()
         slots, _ = O.pool_append(K, V, Kp, C, oi.chan, kn, vn, spec.n, victim=ref["victim"])
-        assert np.array_equal(host(slot), slots)
-        assert np.array_equal(pool.Kh_host.view(torch.int16).numpy().view(np.uint16), K)
-        assert np.array_equal(host(pool.Kp), Kp)
-        assert np.array_equal(host(pool.counters).view(np.uint32), C)
+        gslot = host(slot)
+        Kh = pool.Kh_host.view(torch.int16).numpy().view(np.uint16)
+        gKp, gC = host(pool.Kp), host(pool.counters).view(np.uint32)
+        for b in sorted(in_sync):
+            assert gslot[b] == slots[b], (step, b)
+            assert np.array_equal(Kh[b], K[b]) and np.array_equal(gKp[b], Kp[b]), (step, b)
+            assert np.array_equal(gC[b], C[b]), (step, b)
+    assert len(in_sync) >= 1

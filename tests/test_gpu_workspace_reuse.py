@@ -2,7 +2,7 @@
 H, D and r while n, max_out and the mode change (whole rows, sliced rows whose slices all read each
 row's partial query, the fused decode layer); a call of another (B, H, D, r) follows
 ig_workspace_init.  Every call must leave the workspace as it found it (the projection's partial-sum
-slots empty, the per-row slice counts and the arrival words at zero, the status word clear), so each
+slots empty, the arrival words at zero, the status word clear), so each
 result equals, bit for bit, that of the same call on a fresh workspace."""
 import numpy as np
 import pytest

@@ -142,8 +142,8 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     assert lib.ig_speculate(p, p, None, p, 70000, 64, 1, 8, 40, 40, L.IG_BF16, f(1.0), L.IG_SEL_TOPK, f(0.0), 4, 0,
                             p, p, 4, None, 15, None, None, None, 40, p, 1 << 30, None) == L.IG_EINVAL
     # the status query needs a workspace and somewhere to put the word
-    assert lib.ig_workspace_status(None, 256, ctypes.byref(ctypes.c_uint32()), None) == L.IG_EINVAL
-    assert lib.ig_workspace_status(p, 8, ctypes.byref(ctypes.c_uint32()), None) == L.IG_EINVAL
+    assert lib.ig_workspace_status(None, 256, ctypes.byref(ctypes.c_uint32()), None, None) == L.IG_EINVAL
+    assert lib.ig_workspace_status(p, 8, ctypes.byref(ctypes.c_uint32()), None, None) == L.IG_EINVAL
     # INT4 pool: d not a multiple of 32, rows past the record array, NULL records
     assert L.ig_int4_record_bytes(128) == 160 and L.ig_int4_record_bytes(64) == 96 and L.ig_int4_record_bytes(48) == 0
     assert lib.ig_quantize_kv(p, p, 1, 1, 48, 8, L.IG_BF16, 0, 8, None, p, 8, None) == L.IG_EINVAL
@@ -168,13 +168,13 @@ def test_workspace_sizes(lib):
 
 def test_speculation_workspace_holds_its_documented_regions(lib):
     """The speculation workspace holds (in this order, each 256-byte aligned) the status word and the
-    shape stamp (256 bytes), one arrival word per sequence, one slice count per row, and the
-    projection's split partial sums [ceil(D/512)][B][H*r] float32, then the slices' candidates when
-    rows are sliced; its size only grows with n."""
+    shape stamp (256 bytes), one arrival word per sequence and the projection's split partial sums
+    [ceil(D/512)][B][H*r] float32, then the slices' candidates when rows are sliced; its size only
+    grows with n."""
     a256 = lambda v: (v + 255) // 256 * 256
     for B, H, D, r, n, max_out in [(8, 32, 4096, 32, 2048, 128), (16, 40, 5120, 32, 4352, 218),
                                    (1, 4, 256, 16, 256, 32), (20, 3, 384, 16, 600, 50), (4, 32, 4096, 32, 131072, 5243)]:
-        need = 256 + a256(4 * B) + a256(4 * B * H) + a256(-(-D // 512) * B * H * r * 4)
+        need = 256 + a256(4 * B) + a256(-(-D // 512) * B * H * r * 4)
         sizes = [L.ig_workspace_size(L.IG_OP_SPECULATE, B, H, D, 128, r, nn, max_out) for nn in (max(1, n // 4), n)]
         assert sizes[1] >= need, (B, H, D, r, n)
         assert sizes[1] >= sizes[0], (B, H, D, r, n)

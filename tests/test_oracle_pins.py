@@ -421,6 +421,43 @@ def test_pool_append_slots():
     assert slots.tolist() == [0, 1] and n3 == 3 and C[0, 0] == 0 and C[1, 1] == 0
 
 
+# ---------------------------------------------------------------- one whole layer-step
+def _step_inputs(case, common):
+    """Arrays of a decode_step golden case: x [1][D], Wq_part [D][H*r], Kp [1][H][n][r], q [1][H][d],
+    K, V [1][H][n][d], counters [1][n]."""
+    H = case["H"]
+    heads = ["head0", "head1"][:H]
+    def per_head(key):
+        return np.array([[case.get(f"{key}_{hd}", common.get(f"{key}_{hd}")) for hd in heads]], dtype=float)
+    x = np.array(common["x"], dtype=float)
+    W = np.array(case["Wq_part"], dtype=float)
+    bq = None if case["bq_part"] is None else np.array(case["bq_part"], dtype=float)
+    return x, W, bq, per_head("Kp"), per_head("q"), per_head("K"), per_head("V"), np.array(case["C"], dtype=np.uint32)
+
+
+def test_decode_step_golden_cases():
+    """decode_step chains the steps and forwards every argument (bias, cap, output capacity, mode,
+    cmax, victim): hand-computed layer-steps (tests/golden/decode_step_cases.json)."""
+    g = _load("decode_step_cases.json")
+    common = g["common"]
+    for case in g["cases"]:
+        x, W, bq, Kp, q, K, V, C = _step_inputs(case, common)
+        res = O.decode_step(x, W, Kp, q, K, V, C, n=common["n"], H=case["H"], r=2, scale=common["scale"],
+                            mode=case["mode"], alpha=case.get("alpha", math.inf), k=case.get("k", 0),
+                            max_sel=case["max_sel"], max_out=case["max_out"], cmax=case["cmax"], bq_part=bq,
+                            want_victim=True)
+        e = case["expect"]
+        name = case["name"]
+        for key in ("q_part", "scores", "out", "lse"):
+            assert np.allclose(res[key], np.array(e[key]), rtol=0, atol=1e-12), (name, key, res[key])
+        assert res["count"].tolist() == e["count"], (name, res["count"])
+        for h in range(case["H"]):
+            c = int(res["count"][0, h])
+            assert res["idx"][0, h, :c].tolist() == e["idx"][0][h], (name, h)
+        assert res["counters"].tolist() == e["counters"], (name, res["counters"])
+        assert res["victim"].tolist() == e["victim"], (name, res["victim"])
+
+
 # ---------------------------------------------------------------- the pins catch planted mistakes
 def test_pins_catch_planted_mistakes(monkeypatch):
     """Each planted mistake in a copy of an oracle step makes one of the pins above fail."""
@@ -447,10 +484,36 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         v = np.argmin(C[:, :n], axis=1).astype(np.int32) if want_victim else None
         return np.minimum(C, cmax).astype(np.uint32), v
 
+    real_step = mod.decode_step
+
+    def bias_dropped(*a, **kw):  # the bias is not forwarded to the partial query
+        return real_step(*a, **{**kw, "bq_part": None})
+
+    def cap_dropped(*a, **kw):  # the per-layer cap is not forwarded to the selection
+        return real_step(*a, **{**kw, "max_sel": 0})
+
+    def capacity_dropped(*a, **kw):  # the output capacity is not forwarded
+        return real_step(*a, **{**kw, "max_out": 0})
+
+    real_avg = mod.select_head_average
+
+    def avg_rounded_down(scores, alpha, max_sel=0, max_out=0):  # head average rounded down
+        B, H, n = scores.shape
+        counts = [len(mod.select_threshold(scores[0, h], alpha)) for h in range(H)]
+        if sum(counts) % H == 0:
+            return real_avg(scores, alpha, max_sel, max_out)
+        return real_avg(scores, alpha, max(1, sum(counts) // H), max_out)
+
     planted = [("rehearse", no_scale, test_rehearse_brute_force_loops),
                ("select_threshold", strict_cut, test_select_hand_cases),
                ("attention_rows", no_value_weighting, test_attention_hand_cases),
-               ("pool_touch", no_halving, test_counter_hand_cases)]
+               ("pool_touch", no_halving, test_counter_hand_cases),
+               ("rehearse", no_scale, test_decode_step_golden_cases),
+               ("pool_touch", no_halving, test_decode_step_golden_cases),
+               ("decode_step", bias_dropped, test_decode_step_golden_cases),
+               ("decode_step", cap_dropped, test_decode_step_golden_cases),
+               ("decode_step", capacity_dropped, test_decode_step_golden_cases),
+               ("select_head_average", avg_rounded_down, test_select_hand_cases)]
     for name, fake, pin in planted:
         monkeypatch.setattr(mod, name, fake)
         with pytest.raises(AssertionError):
