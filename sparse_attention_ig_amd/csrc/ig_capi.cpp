@@ -166,11 +166,13 @@ static int check_spec(const char* fn, const SpecCall& c, size_t ws_bytes, bool n
     else if (c.mode == IG_SEL_TOPK)
         IG_REQUIRE(c.k >= 1, "%s: k must be >= 1", fn);
     else if (c.mode == IG_SEL_HEADAVG)
-        return fail(IG_EUNSUPPORTED, "%s: the head-average mode needs every head's count first; "
-                                     "use ig_rehearse + ig_select", fn);
+        IG_REQUIRE(c.alpha >= 0.f && !std::isnan(c.alpha) && c.max_sel >= 0, "%s: alpha must be >= 0", fn);
     else
         return fail(IG_EINVAL, "%s: unknown mode %d", fn, c.mode);
     const SpecPlan plan = plan_speculate(B, H, D, r, n, max_out, dtype, c.mode);
+    if (!plan.ok && c.mode == IG_SEL_HEADAVG)
+        return fail(IG_EUNSUPPORTED, "%s: the head-average mode needs rows held whole by one workgroup (n <= %d "
+                    "and enough rows to fill the chip); use ig_rehearse + ig_select", fn, kSpecMaxRows);
     if (!plan.ok)
         return fail(IG_EUNSUPPORTED, "%s: n = %d needs more than %d slices of %d rows; use ig_rehearse + "
                     "ig_select", fn, n, kSpecMaxSlices, kSpecMaxRows);

@@ -94,6 +94,8 @@ struct SpecParams {
     int tight;
     uint32_t* cand_lo;
     float* q_rows;
+    // head average (whole rows): each row's threshold count [B*H], summed per sequence by the merge
+    int32_t* hcount;
 };
 
 // Sticky status bits of a speculation workspace (the public IG_WS_* values).
@@ -337,13 +339,34 @@ __device__ __forceinline__ int tight_slice_k(int kk_row, int rows, int n, int ca
 // selection of at most cand_cap keys -- every key at or above a sampled lower bound of the slice's cut
 // when they fit; with tight top-k candidates, of the slice's share of the row's budget.
 template <bool TO_CANDS, class KS>
-__device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int m, int rows, uint32_t kmax_all, KS keys,
-                                           SelScratch& sh, FastSel& fs) {
+__device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, int m, int rows, uint32_t kmax_all,
+                                           KS keys, SelScratch& sh, FastSel& fs) {
     int limit = min(rows, p.max_out);
     bool done = false;
     int kk = 0;
     SelCut c{0u, INT_MAX, INT_MAX};
-    if (p.mode == IG_SEL_THRESHOLD) {
+    if (p.mode == IG_SEL_HEADAVG) {
+        if constexpr (TO_CANDS) {
+            // a whole row of a head-average call: its threshold count for the sequence's average, and as
+            // candidates every key an averaged count could take, the row's top min(n, max_out, max_sel)
+            const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
+            const int cnt = count_ge<kSpecThreads>(keys, m, kc, sh);
+            if (threadIdx.x == 0) p.hcount[bh] = cnt;
+            kk = p.max_sel > 0 ? min(limit, p.max_sel) : limit;
+        } else {
+            // the merge: every head of sequence b takes ceil(mean_h count_h), then the cap and the output
+            if (threadIdx.x == 0) {
+                long long tot = 0;
+                for (int h = 0; h < p.H; ++h) tot += p.hcount[static_cast<size_t>(b) * p.H + h];
+                long long cb = (tot + p.H - 1) / p.H;
+                if (p.max_sel > 0) cb = min(cb, static_cast<long long>(p.max_sel));
+                sh.bc[0] = static_cast<int>(max(1ll, min(cb, static_cast<long long>(min(limit, m)))));
+            }
+            __syncthreads();
+            kk = sh.bc[0];
+            __syncthreads();
+        }
+    } else if (p.mode == IG_SEL_THRESHOLD) {
         const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
         const int cnt = count_ge<kSpecThreads>(keys, m, kc, sh);
         if (p.max_sel > 0) limit = min(limit, p.max_sel);
@@ -493,7 +516,7 @@ template <bool TO_CANDS, class KS, typename GIdx>
 __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, int slice, int m, int rows,
                                             uint32_t kmax_all, KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs,
                                             int& s_last, GIdx gidx) {
-    const SelCut c = spec_cut<TO_CANDS>(p, m, rows, kmax_all, keys, sh, fs);
+    const SelCut c = spec_cut<TO_CANDS>(p, b, bh, m, rows, kmax_all, keys, sh, fs);
     spec_emit<TO_CANDS>(p, b, bh, slice, m, c, keys, lds, sh, fs, s_last, gidx);
 }
 
@@ -672,8 +695,9 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
     }
     const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
 
-    // 3. selection (and, for a whole row, counters)
-    if (p.slices > 1)
+    // 3. selection (and, for a whole row, counters; a slice, or a row of a head-average call, hands on
+    // candidates to the merge instead)
+    if (p.slices > 1 || p.mode == IG_SEL_HEADAVG)
         spec_select<true>(p, b, bh, slice, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last,
                           [&](int j) { return r0 + j; });
     else
@@ -768,7 +792,7 @@ __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t
             }
         }
         const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
-        const SelCut c = spec_cut<false>(p, mu, p.n, kmax_all, LdsKeys{keys}, sh, fs);
+        const SelCut c = spec_cut<false>(p, b, bh, mu, p.n, kmax_all, LdsKeys{keys}, sh, fs);
         exact = !checked || (c.kth != 0u && c.kth >= emax);
         if (exact) {
             if (with_idx) {
@@ -795,7 +819,7 @@ __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t
             }
         }
         const uint32_t kmax_all = block_max_u32(kmax, sh);  // (also the barrier after fast_sel_init)
-        const SelCut c = spec_cut<false>(p, m, p.n, kmax_all, GlobalKeys{ck}, sh, fs);
+        const SelCut c = spec_cut<false>(p, b, bh, m, p.n, kmax_all, GlobalKeys{ck}, sh, fs);
         exact = !checked || (c.kth != 0u && c.kth >= emax);
         if (exact) {
             spec_emit<false>(p, b, bh, 0, m, c, GlobalKeys{ck}, keys, sh, fs, sm.last, gidx);

@@ -170,7 +170,7 @@ int launch_decode_layer(const AttnCall* a, const SpecCall* sc, hipStream_t s) {
     e = a->dtype == IG_BF16 ? launch_fused_t<uint16_t>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s)
                             : launch_fused_t<float>(p, aa, lpr_of(sc->r, sc->dtype), lpr_of(a->d, a->dtype), bh, s);
     if (e) return e;
-    if (p.slices > 1) {
+    if (p.slices > 1 || p.mode == IG_SEL_HEADAVG) {
         // the merge (whose workgroups also combine the attention's splits), then the counters
         const CombineArgs cb{ap.nsplit > 1 ? aa.part : nullptr, ap.nsplit, a->d, a->out, a->lse};
         return finish_speculate(p, sc->dtype, sc->ws, s, cb);

@@ -88,15 +88,23 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     // the workspace serves both modes (its size query knows no mode): regions sized for the larger plan
     const SlicePlan thr = plan_slices(rows, n, max_out, false);
     const SlicePlan tk = plan_slices(rows, n, max_out, true);
-    const SlicePlan& pl = mode == IG_SEL_TOPK ? tk : thr;
+    // the head average: whole rows only (the threshold count needs the row's maximum), each handing on its
+    // top min(n, max_out) as candidates
+    SlicePlan ha = thr;
+    ha.ok = thr.slices == 1;
+    ha.cap = std::min(n, max_out);
+    const SlicePlan& pl = mode == IG_SEL_TOPK ? tk : mode == IG_SEL_HEADAVG ? ha : thr;
     sp.ok = pl.ok;
     sp.slices = pl.slices;
     sp.slice_rows = pl.slice_rows;
     sp.cand_cap = pl.cap;
     sp.tight = mode == IG_SEL_TOPK && pl.slices > 1;
+    sp.headavg = mode == IG_SEL_HEADAVG;
     const int s_max = std::max(thr.slices, tk.slices);
-    const size_t cands = static_cast<size_t>(rows) *
-                         std::max(static_cast<size_t>(thr.slices) * thr.cap, static_cast<size_t>(tk.slices) * tk.cap);
+    const size_t ha_cands = ha.ok ? static_cast<size_t>(rows) * ha.cap : 0;
+    const size_t cands = std::max(static_cast<size_t>(rows) * std::max(static_cast<size_t>(thr.slices) * thr.cap,
+                                                                       static_cast<size_t>(tk.slices) * tk.cap),
+                                  ha_cands);
     // projection workgroups: column blocks x splits of the D inputs
     sp.proj_blocks = (H * r + kProjCols - 1) / kProjCols;
     sp.splits = (D + kProjSplit - 1) / kProjSplit;
@@ -105,7 +113,7 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     sp.off_arrive = 256;
     sp.off_part = sp.off_arrive + align256(static_cast<size_t>(B) * sizeof(uint32_t));
     sp.off_cnt = sp.off_part + align256(static_cast<size_t>(sp.splits) * B * H * r * sizeof(float));
-    const bool sliced = s_max > 1;
+    const bool sliced = s_max > 1 || ha.ok;  // (candidate regions: slices, or head-average rows)
     sp.off_lo = sp.off_cnt + (sliced ? align256(static_cast<size_t>(rows) * s_max * sizeof(int32_t)) : 0);
     sp.off_q = sp.off_lo + (sliced ? align256(static_cast<size_t>(rows) * s_max * sizeof(uint32_t)) : 0);
     sp.off_key = sp.off_q + (tk.slices > 1 ? align256(static_cast<size_t>(rows) * r * sizeof(float)) : 0);
@@ -119,7 +127,8 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     const size_t nw = (static_cast<size_t>(n) + 31) / 32;
     sp.off_bits = sp.off_idx + (sliced ? align256(cands * sizeof(int32_t)) : 0);
     sp.off_flags = sp.off_bits + (any_bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
-    sp.ws_bytes = sp.off_flags + (any_bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
+    sp.off_hcount = sp.off_flags + (any_bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
+    sp.ws_bytes = sp.off_hcount + (ha.ok ? align256(static_cast<size_t>(rows) * sizeof(int32_t)) : 0);
     return sp;
 }
 
@@ -241,6 +250,7 @@ int begin_speculate(const SpecCall& c, SpecParams* p) {
     p->tight = sp.tight ? 1 : 0;
     if (sp.slices > 1) p->cand_lo = reinterpret_cast<uint32_t*>(ws + sp.off_lo);
     if (sp.tight) p->q_rows = reinterpret_cast<float*>(ws + sp.off_q);
+    if (sp.headavg) p->hcount = reinterpret_cast<int32_t*>(ws + sp.off_hcount);
     return 0;
 }
 
@@ -254,7 +264,7 @@ int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, c
     int e = begin_speculate(c, &p);
     if (e) return e;
     e = dtype == IG_BF16 ? launch_spec_t<uint16_t>(p, s) : launch_spec_t<float>(p, s);
-    if (e || p.slices == 1) return e;
+    if (e || (p.slices == 1 && p.mode != IG_SEL_HEADAVG)) return e;
     return finish_speculate(p, dtype, ws, s);
 }
 

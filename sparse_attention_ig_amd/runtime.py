@@ -158,8 +158,6 @@ class DeviceLayer:
                 L.ig_sparse_decode_attn(self.q, self.K, self.V, idx, self.count, s.softmax_scale, out=self.out,
                                         lse=self.lse, ws=self.ws, stream=stream)
             elif part == "speculate":
-                if mode == "headavg":
-                    raise ValueError("the fused speculation has no head-average mode")
                 L.ig_speculate(self.x, self.Wq_part, self.Kp, n, s.softmax_scale, mode, max_out, alpha=alpha, k=k,
                                max_sel=max_sel, idx=idx, count=self.count, counters=self.counters, cmax=cmax,
                                victim=self.victim if want_victim else None, q_part=self.q_part,

@@ -66,6 +66,10 @@ CASES = [
     # its slice workgroups interleaved with the attention items in the one launch
     ("bf16-sliced-topk", lambda: _spec(gen.opt_6_7b(n=3000, B=1), H=4, topk=400),
      lambda: _spec(gen.llama2_7b_long(n=40000, B=1), H=4, topk=400, seed=2009), dict(mode="topk", k=400, max_out=400)),
+    # the head average (every head of a sequence takes the mean threshold count): whole rows hand on
+    # candidates, a merge launch after the fused one averages and selects
+    ("bf16-headavg", lambda: _spec(gen.opt_6_7b(n=1500, B=2), H=3, topk=100),
+     lambda: _spec(gen.opt_6_7b(n=1800, B=2), H=3, seed=2011), dict(mode="headavg", alpha=5.0, max_sel=300, max_out=300)),
     # 128 rows of 65536 keys, top 2048: slices of 8192, counters from the merge's bitmaps
     ("bf16-sliced-bitmaps", lambda: _spec(gen.opt_6_7b(n=4000, B=4), topk=2048),
      lambda: _spec(gen.llama2_7b_long(n=65536, B=4), topk=2048, seed=2010), dict(mode="topk", k=2048, max_out=2048)),
@@ -110,8 +114,18 @@ def test_decode_layer_matches_separate_calls(name, attn_fn, spec_fn, kw):
     oi_b = harness.oracle_inputs(sb)
     harness.assert_setup_routes_agree(li_b, oi_b)
     mode = kw["mode"]
-    ref, ri, rc = harness.oracle_heads(oi_b, mode=mode, alpha=kw.get("alpha", np.inf), k=kw.get("k", 0),
-                                       max_sel=kw.get("max_sel", 0), max_out=kw["max_out"], attn=False)
+    if mode == "headavg":
+        # the average couples a sequence's heads: the oracle runs the whole layer-step
+        full = harness.oracle_step(oi_b, mode=mode, alpha=kw["alpha"], max_sel=kw.get("max_sel", 0),
+                                   max_out=kw["max_out"], counters=np.zeros((sb.B, sb.cap), np.uint32))
+        ri, rc = full["idx"], full["count"]
+        ref = {(b, h): dict(q_part=full["q_part"][b, h], scores=full["scores"][b, h],
+                            idx=ri[b, h, :rc[b, h]].astype(np.int64))
+               for b in range(sb.B) for h in range(sb.H)}
+        assert np.array_equal(g_b["count"], rc), (g_b["count"], rc)
+    else:
+        ref, ri, rc = harness.oracle_heads(oi_b, mode=mode, alpha=kw.get("alpha", np.inf), k=kw.get("k", 0),
+                                           max_sel=kw.get("max_sel", 0), max_out=kw["max_out"], attn=False)
     inexact = harness.check_heads(g_b["idx"], g_b["count"], ref, mode, kw.get("alpha", np.inf),
                                   g_q_part=g_b["q_part"])
     assert len(inexact) <= max(1, sb.B * sb.H // 50), inexact

@@ -155,12 +155,13 @@ def test_decode_step_parity(name, factory, mode, kw):
     check_step(name, factory(), mode, kw)
 
 
-FUSED_CASES = [c for c in CASES if c[2] != "headavg"]
+FUSED_CASES = CASES
 
 
 @pytest.mark.parametrize("name,factory,mode,kw", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
 def test_fused_speculation_parity(name, factory, mode, kw):
-    """ig_speculate (partial query, scores, selection and counters in one launch) + attention."""
+    """ig_speculate (partial query, scores, selection and counters in one launch; the head average with
+    a merge launch after the rows) + attention."""
     check_step(name, factory(), mode, kw, path="fused")
 
 

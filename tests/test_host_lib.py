@@ -133,8 +133,9 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     # fused speculation: rows beyond 16 slices of 32768, or the head-average mode, are unsupported
     assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 600000, 600000, L.IG_BF16, f(1.0), L.IG_SEL_TOPK, f(0.0), 4,
                             0, p, p, 20000, None, 15, None, None, None, 600000, None, 0, None) == L.IG_EUNSUPPORTED
-    assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 40, 40, L.IG_BF16, f(1.0), L.IG_SEL_HEADAVG, f(1.0), 4, 0,
-                            p, p, 4, None, 15, None, None, None, 40, None, 0, None) == L.IG_EUNSUPPORTED
+    # (the head average needs whole rows: a 100000-key row is sliced)
+    assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 100000, 100000, L.IG_BF16, f(1.0), L.IG_SEL_HEADAVG, f(1.0), 4,
+                            0, p, p, 4, None, 15, None, None, None, 100000, None, 0, None) == L.IG_EUNSUPPORTED
     # no workspace
     assert lib.ig_speculate(p, p, None, p, 1, 64, 1, 8, 40, 40, L.IG_BF16, f(1.0), L.IG_SEL_TOPK, f(0.0), 4, 0,
                             p, p, 4, p, 15, None, None, None, 40, None, 0, None) == L.IG_EINVAL
