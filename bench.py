@@ -672,14 +672,14 @@ def kernel_sources_digest() -> str:
 
 
 # the kernels of a call (rocprofv3 kernel names start with these): ig_decode_layer is one fused launch plus,
-# for sliced rows, the merge and the counter kernels, and for a split attention the combine; where the
+# for sliced rows, the merge (which also combines a split attention) and the counter kernels; where the
 # two halves are not fused it is the speculation's kernels and the attention's
 CALL_KERNELS = {
-    "ig_decode_layer": ("void ig::k_decode_layer<", "ig::k_spec_merge", "ig::k_touch_bits", "ig::k_touch_finish",
-                        "ig::k_attn_combine"),
-    "ig_decode_layer/unfused": ("void ig::k_speculate<", "ig::k_spec_merge", "ig::k_touch_bits",
+    "ig_decode_layer": ("void ig::k_decode_layer<", "void ig::k_spec_merge<", "ig::k_touch_bits",
+                        "ig::k_touch_finish"),
+    "ig_decode_layer/unfused": ("void ig::k_speculate<", "void ig::k_spec_merge<", "ig::k_touch_bits",
                                 "ig::k_touch_finish", "void ig::k_attn_split<", "ig::k_attn_combine"),
-    "ig_speculate": ("void ig::k_speculate<", "ig::k_spec_merge", "ig::k_touch_bits", "ig::k_touch_finish"),
+    "ig_speculate": ("void ig::k_speculate<", "void ig::k_spec_merge<", "ig::k_touch_bits", "ig::k_touch_finish"),
 }
 
 
