@@ -209,10 +209,15 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * scores, selection and counter update of ig_rehearse + ig_select +
  * ig_pool_touch (section 3.4, "Decoding Stage" steps 1-3 and 5, and the pool
  * paragraph), with the scores kept on chip.  Same arguments and results as
- * those calls; modes IG_SEL_THRESHOLD and IG_SEL_TOPK.  A row's scores live in
- * LDS: when there are too few rows to fill the GPU, or n > 32768, each row is
- * cut into up to 16 slices that select locally, and a merge launch selects
- * among their candidates; IG_EUNSUPPORTED when n > 16 x 32768.
+ * those calls, in all three modes.  A row's scores live in LDS: when there are
+ * too few rows to fill the GPU, or n > 32768, each row is cut into up to 16
+ * slices that select locally, and a merge launch selects among their
+ * candidates; IG_EUNSUPPORTED when n > 16 x 32768, or in IG_SEL_HEADAVG when
+ * rows would have to be sliced (each whole row hands on its top candidates
+ * and its threshold count, and the merge launch gives every head of a
+ * sequence the averaged count).  When a sliced call selects many slots, the
+ * counters are updated from per-row bitmaps by two small kernels after the
+ * merge.
  * q_part [B][H][r] and scores [B][H][ld] are written only when not NULL.
  * counters (not NULL) are updated as by ig_pool_touch, victim [B] (not NULL)
  * receives the victim.  One launch: projection workgroups (each one block of
@@ -224,8 +229,9 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * offset 0, see ig_workspace_status) and the shape stamp (uint64 at offset 8),
  * then one uint32 arrival word per sequence ([B] at offset 256) and the
  * projection's split partial sums, then the slices' candidates (when there
- * are slices); it must have been zero-filled once with ig_workspace_init,
- * and every call returns the arrival words and the partial-sum slots to zero.  The first call after the zero-fill stamps
+ * are slices) and the counter kernels' bitmaps and per-sequence records; it
+ * must have been zero-filled once with ig_workspace_init, and every call
+ * returns the arrival words, the partial-sum slots and those records to zero.  The first call after the zero-fill stamps
  * the workspace with its (B, H, D, r) (the places of those regions depend on
  * them; n, max_out and the mode may change from call to call); a call of
  * another (B, H, D, r) sets IG_WS_SHAPE instead of running: run

@@ -210,4 +210,46 @@ __device__ __forceinline__ void combine_item(const CombineArgs& c, int bh) {
     }
 }
 
+// The same combine with the splits' partials loaded ahead (at most kCombinePre splits): combine_load
+// issues the loads into registers, combine_store adds them exactly as combine_item does (splits in
+// order), so a workgroup can start the loads before other work and finish the combine after it.
+constexpr int kCombinePre = 8;
+struct CombinePre {
+    float m[kCombinePre], l[kCombinePre], a[kCombinePre];
+};
+
+__device__ __forceinline__ void combine_load(const CombineArgs& c, int bh, CombinePre& pre) {
+    const int t = threadIdx.x, d = c.d;
+    const float* pp = c.part + static_cast<size_t>(bh) * c.nsplit * (2 + d);
+#pragma unroll
+    for (int s = 0; s < kCombinePre; ++s) {
+        const bool on = s < c.nsplit && t < d;
+        pre.m[s] = on ? pp[s * (2 + d)] : -INFINITY;
+        pre.l[s] = on ? pp[s * (2 + d) + 1] : 0.f;
+        pre.a[s] = on ? pp[s * (2 + d) + 2 + t] : 0.f;
+    }
+}
+
+__device__ __forceinline__ void combine_store(const CombineArgs& c, int bh, const CombinePre& pre) {
+    const int t = threadIdx.x, d = c.d;
+    if (t >= d) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kCombinePre; ++s) M = fmaxf(M, pre.m[s]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int s = 0; s < kCombinePre; ++s) {
+            if (s < c.nsplit) {
+                const float ms = pre.m[s];
+                const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+                L += pre.l[s] * w;
+                A += pre.a[s] * w;
+            }
+        }
+    }
+    c.out[static_cast<size_t>(bh) * d + t] = L > 0.f ? A / L : 0.f;
+    if (c.lse && t == 0) c.lse[bh] = L > 0.f ? M + __logf(L) : -INFINITY;
+}
+
 }  // namespace ig

@@ -292,18 +292,20 @@ struct GlobalKeys {
     }
 };
 
-// One radix pass: hist[digit] counts of the keys whose bits above `shift + 8` equal `prefix`.
+// One radix pass: hist[digit] counts of the keys k >= base whose offset k - base has the bits above
+// `shift + 8` equal to `prefix` (base 0: the keys themselves).
 template <int NT, int E, class KS>
 __device__ __forceinline__ void radix_hist(KS lk, int n, uint32_t* h, int shift, uint32_t prefix, uint32_t pmask,
-                                           bool first) {
+                                           bool first, uint32_t base) {
     const int lane = threadIdx.x % kWave;
     for (int j0 = E * static_cast<int>(threadIdx.x); j0 < n; j0 += E * NT) {
         uint32_t k[E];
         lk.template load<E>(j0, n, k);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const uint32_t bin = (k[e] >> shift) & 255u;
-            bool on = j0 + e < n && (k[e] & pmask) == prefix;
+            const uint32_t kb = k[e] - base;
+            const uint32_t bin = (kb >> shift) & 255u;
+            bool on = j0 + e < n && k[e] >= base && (kb & pmask) == prefix;
             if (first) {
                 // the first pass's keys crowd into the few bins of their sign and exponent bits, and
                 // LDS atomics to one address serialise: the bin of the first active lane is counted
@@ -328,23 +330,29 @@ __device__ __forceinline__ void radix_hist(KS lk, int n, uint32_t* h, int shift,
 // belongs to the top kk the search stops early: T is then the bin's lowest key value (its low bits
 // zero) and every key >= T is selected (*need_eq == *eq_total).  Ends after a barrier.
 //
+// With a known range base <= T <= hi (at least kk keys >= base, none above hi), only the keys >= base
+// take part, as offsets k - base, and the passes start at the digit of the highest bit of hi - base:
+// every offset of a key in range has the bits above it zero.  (base 0, hi ~0: every key, four passes.)
+//
 // Per pass: LDS atomics into that pass's histogram, one barrier, then every wave finds the digit on
 // its own: lane L holds bins 255-4L .. 252-4L, a DPP prefix sum over the lanes gives the keys above
 // each bin, and the lane holding the bin where the count reaches rem broadcasts it.
 template <int NT = kSelThreads, class KS>
 __device__ __forceinline__ void radix_kth_keys(KS lk, int n, int kk, FastSel& fs, uint32_t* T_out, int* need_eq_out,
-                                               int* eq_total_out) {
+                                               int* eq_total_out, uint32_t base = 0u, uint32_t hi = ~0u) {
     const int tid = threadIdx.x, lane = tid % kWave;
     constexpr int E = KS::kE;
     const bool wide = n >= E * NT;
-    uint32_t prefix = 0, pmask = 0;
+    const uint32_t span = hi - base;
+    const int top = span ? (31 - __clz(static_cast<int>(span))) / 8 * 8 : 0;  // shift of the first pass
+    uint32_t prefix = 0, pmask = top < 24 ? ~0u << (top + 8) : 0u;
     int rem = kk, dcount = 0;
-    for (int pass = 0, shift = 24; shift >= 0; ++pass, shift -= 8) {
+    for (int pass = 0, shift = top; shift >= 0; ++pass, shift -= 8) {
         uint32_t* h = fs.hist(pass % 3);
         if (wide)
-            radix_hist<NT, E>(lk, n, h, shift, prefix, pmask, pass == 0);
+            radix_hist<NT, E>(lk, n, h, shift, prefix, pmask, pass == 0, base);
         else
-            radix_hist<NT, 1>(lk, n, h, shift, prefix, pmask, pass == 0);
+            radix_hist<NT, 1>(lk, n, h, shift, prefix, pmask, pass == 0, base);
         __syncthreads();
         if (tid < 256) fs.hist((pass + 2) % 3)[tid] = 0u;
         const uint4 c4 = *reinterpret_cast<const uint4*>(h + 252 - 4 * lane);
@@ -372,7 +380,7 @@ __device__ __forceinline__ void radix_kth_keys(KS lk, int n, int kk, FastSel& fs
         pmask |= 255u << shift;
         if (dcount == rem) break;  // the whole bin is taken
     }
-    *T_out = prefix;
+    *T_out = base + prefix;
     *need_eq_out = rem;
     *eq_total_out = dcount;
 }

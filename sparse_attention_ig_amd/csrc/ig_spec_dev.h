@@ -704,52 +704,126 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
         spec_select<false>(p, b, bh, 0, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last, IdentityIdx());
 }
 
-// Merge workgroup of a sliced row.  Slice sl left its candidates in slots [sl * cap, +cap) of the row
-// (unused slots hold key 0, below every score key), so the m = slices * cap slots are in row order.
-// Without tight candidates they hold the row's selection: a key among the row's top c is among its
-// slice's top c, and a key at or above the row's threshold cut is at or above its slice's.  The
-// selection runs again over them with the row's rules: on a copy in LDS when m <= kSpecMaxRows, else
-// straight from the candidate arrays (L2-resident: the slices wrote them just before).
-//
-// With tight top-k candidates a slice handed on only about its share of the row's budget, every key of
-// it at or above its bound E_s.  The row's kk-th largest candidate T' is then checked: when T' >= E_s for
-// every slice, every key of the row at or above T' is a candidate, so the kk-th largest key of the row is
-// T' and the row's top kk (ties to the lower index) are the candidates' top kk -- the selection is exact.
-// Otherwise (a slice held more of the row's top kk than its share) the row's scores are recomputed from
-// its partial keys (RowKeys, the same float32 arithmetic as the slices) and the selection runs over
-// them: exact as well, only slower.
-template <typename T, int LPR, int R>
-__device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t* keys, SpecShared<R>& sm) {
+// The partial-sum slots of row (b, h): every slice of the row read them in the launch before, so the
+// merge returns them to empty for the next call.
+__device__ __forceinline__ void merge_empty_part(const SpecParams& p, int b, int h) {
+    if (!p.part) return;
+    const int N = p.H * p.r;
+    for (int k = threadIdx.x; k < p.splits * p.r; k += kSpecThreads)
+        coherent_store(p.part + (static_cast<size_t>(k / p.r) * p.B + b) * N + h * p.r + k % p.r, 0.f);
+}
+
+// A merge whose candidate slots fit in LDS twice over (keys and row indices) with at most one slot per
+// thread and slice.  One round trip reads every slot of every slice (an unused slot holds key 0: read,
+// then dropped) together with the slices' counts and bounds; the used slots go to LDS in row order.
+// With tight candidates the row's cut is searched among the keys at or above E = the largest slice
+// bound only: the merge is exact exactly when at least kk candidates reach E (then the kk-th largest
+// key T' >= E), and those keys lie in [E, the largest key].  Returns false when the row must be
+// recomputed (fewer than kk candidates reach E).
+template <int R>
+__device__ __forceinline__ bool merge_small(const SpecParams& p, int b, int h, int m, int cnt, uint32_t lo,
+                                            bool checked, uint32_t* keys, SpecShared<R>& sm) {
+    SelScratch& sh = sm.sh;
+    FastSel& fs = sm.fs;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int bh = b * p.H + h;
+    const size_t base = static_cast<size_t>(bh) * m;
+    const uint32_t* ck = p.cand_key + base;
+    const int32_t* ci = p.cand_idx + base;
+    uint32_t v[kSpecMaxSlices];
+    int32_t x[kSpecMaxSlices];
+#pragma unroll
+    for (int sl = 0; sl < kSpecMaxSlices; ++sl) {
+        const bool on = sl < p.slices && tid < p.cand_cap;
+        const size_t g = static_cast<size_t>(sl) * p.cand_cap + tid;
+        v[sl] = on ? ck[g] : 0u;
+        x[sl] = on ? ci[g] : 0;
+    }
+    merge_empty_part(p, b, h);
+    // wave 0: where each slice's used slots go (a prefix sum over the slices), whether a slice failed,
+    // and E
+    int* s_off = reinterpret_cast<int*>(sm.q);  // (kSpecMaxSlices + 1 words, free until a recompute)
+    if (wave == 0) {
+        const int c = tid < p.slices ? min(max(cnt, 0), p.cand_cap) : 0;
+        const int inc = wave_incl_scan(c);
+        if (tid < p.slices) s_off[tid + 1] = inc;
+        const bool bad = __ballot(tid < p.slices && cnt < 0) != 0;
+        const uint32_t em = wave_max_u32(lo);
+        if (tid == 0) {
+            s_off[0] = 0;
+            sh.bc[1] = bad ? 1 : 0;
+            sh.bc[2] = static_cast<int>(em);
+        }
+    }
+    fast_sel_init(fs);
+    __syncthreads();
+    if (sh.bc[1]) {
+        spec_fail_row(p, b, bh, keys, sh, sm.last);
+        return true;
+    }
+    const uint32_t emax = static_cast<uint32_t>(sh.bc[2]);
+    const int mu = s_off[p.slices];  // used candidate slots, in row order slice by slice
+    int32_t* lidx = reinterpret_cast<int32_t*>(keys + mu);
+    uint32_t kmax = 0;
+    int ge = 0;
+#pragma unroll
+    for (int sl = 0; sl < kSpecMaxSlices; ++sl) {
+        if (sl < p.slices) {
+            const int o = s_off[sl];
+            if (tid < s_off[sl + 1] - o) {
+                keys[o + tid] = v[sl];
+                lidx[o + tid] = x[sl];
+                kmax = max_u32(kmax, v[sl]);
+                ge += v[sl] >= emax ? 1 : 0;
+            }
+        }
+    }
+    // the largest key and the count at or above E in one barrier (which also publishes the LDS copy)
+    kmax = wave_max_u32(kmax);
+    ge = wave_sum_i32(ge);
+    if (lane == 0) {
+        fs.wtot[wave] = static_cast<int>(kmax);
+        fs.wtot2[wave] = ge;
+    }
+    __syncthreads();
+    uint32_t kmax_all = 0;
+    int ge_all = 0;
+#pragma unroll
+    for (int w = 0; w < kSpecThreads / kWave; ++w) {
+        kmax_all = max_u32(kmax_all, static_cast<uint32_t>(fs.wtot[w]));
+        ge_all += fs.wtot2[w];
+    }
+    SelCut c{0u, INT_MAX, INT_MAX};
+    if (checked) {
+        const int kk = min(p.k, min(p.n, p.max_out));
+        if (ge_all < kk) return false;
+        radix_kth_keys(LdsKeys{keys}, mu, kk, fs, &c.kth, &c.need_eq, &c.eq_total, emax, kmax_all);
+        if (c.kth == 0u) return false;
+    } else {
+        c = spec_cut<false>(p, b, bh, mu, p.n, kmax_all, LdsKeys{keys}, sh, fs);
+    }
+    spec_emit<false>(p, b, bh, 0, mu, c, LdsKeys{keys}, keys, sh, fs, sm.last, LdsIdx{lidx});
+    return true;
+}
+
+// Any other merge: the used slots are copied to LDS once the counts are known (keys, and row indices
+// when they fit too), or the selection runs straight on the candidate arrays.  Returns false when the
+// row must be recomputed (tight candidates whose cut T' is below a slice's bound).
+template <int R>
+__device__ __forceinline__ bool merge_large(const SpecParams& p, int b, int h, int m, int cnt, uint32_t lo,
+                                            bool checked, uint32_t* keys, SpecShared<R>& sm) {
     SelScratch& sh = sm.sh;
     FastSel& fs = sm.fs;
     const int tid = threadIdx.x;
-    int b, h;
-    spec_bh(p, wg, &b, &h);
     const int bh = b * p.H + h;
-    // every slice of the row has read its partial-sum slots (they ran in the launch before): empty them
-    if (p.part) {
-        const int N = p.H * p.r;
-        for (int k = tid; k < p.splits * p.r; k += kSpecThreads)
-            coherent_store(p.part + (static_cast<size_t>(k / p.r) * p.B + b) * N + h * p.r + k % p.r, 0.f);
-    }
-    const int m = p.slices * p.cand_cap;
     const size_t base = static_cast<size_t>(bh) * m;
     const uint32_t* ck = p.cand_key + base;
     const int32_t* ci = p.cand_idx + base;
     auto gidx = [&](int j) { return static_cast<int>(ci[j]); };
-    // the slices' candidate counts (a slice that could not compute its scores marks its count -1: the row
-    // fails) and, with tight candidates, their bounds
-    const bool checked = p.tight && p.mode == IG_SEL_TOPK;
-    const int32_t* cc = p.cand_cnt + static_cast<size_t>(bh) * p.slices;
-    int cnt = 0;
-    uint32_t lo = 0;
-    if (tid < p.slices) {
-        cnt = cc[tid];
-        if (checked) lo = p.cand_lo[static_cast<size_t>(bh) * p.slices + tid];
-    }
+    merge_empty_part(p, b, h);
     if (__syncthreads_or(cnt < 0)) {
         spec_fail_row(p, b, bh, keys, sh, sm.last);
-        return;
+        return true;
     }
     // where each slice's candidates go when only the used slots are copied: a prefix sum over the slices
     int* s_off = reinterpret_cast<int*>(sm.q);  // (kSpecMaxSlices + 1 words, free until a recompute)
@@ -765,7 +839,6 @@ __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t
     const int mu = s_off[p.slices];  // used candidate slots, in row order slice by slice
     uint32_t kmax = 0;
     constexpr int U = 8;  // loads per lane in flight
-    bool exact = true;
     if (mu <= kSpecMaxRows) {
         // the used slots' keys to LDS [0, mu), and their row indices to [mu, 2 mu) when they fit too
         const bool with_idx = 2 * mu <= kSpecMaxRows;
@@ -793,48 +866,84 @@ __device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t
         }
         const uint32_t kmax_all = block_max_u32(kmax, sh);  // also publishes the LDS keys
         const SelCut c = spec_cut<false>(p, b, bh, mu, p.n, kmax_all, LdsKeys{keys}, sh, fs);
-        exact = !checked || (c.kth != 0u && c.kth >= emax);
-        if (exact) {
-            if (with_idx) {
-                spec_emit<false>(p, b, bh, 0, mu, c, LdsKeys{keys}, keys, sh, fs, sm.last, LdsIdx{lidx});
-            } else {
-                // the row index of used slot j: slot j - s_off[sl] of the slice sl holding it
-                auto used_idx = [&](int j) {
-                    int sl = 0;
-                    while (sl + 1 < p.slices && s_off[sl + 1] <= j) ++sl;
-                    return static_cast<int>(ci[static_cast<size_t>(sl) * p.cand_cap + (j - s_off[sl])]);
-                };
-                spec_emit<false>(p, b, bh, 0, mu, c, LdsKeys{keys}, keys, sh, fs, sm.last, used_idx);
-            }
-            return;
+        if (checked && !(c.kth != 0u && c.kth >= emax)) return false;
+        if (with_idx) {
+            spec_emit<false>(p, b, bh, 0, mu, c, LdsKeys{keys}, keys, sh, fs, sm.last, LdsIdx{lidx});
+        } else {
+            // the row index of used slot j: slot j - s_off[sl] of the slice sl holding it
+            auto used_idx = [&](int j) {
+                int sl = 0;
+                while (sl + 1 < p.slices && s_off[sl + 1] <= j) ++sl;
+                return static_cast<int>(ci[static_cast<size_t>(sl) * p.cand_cap + (j - s_off[sl])]);
+            };
+            spec_emit<false>(p, b, bh, 0, mu, c, LdsKeys{keys}, keys, sh, fs, sm.last, used_idx);
         }
-    } else {
-        if (p.mode == IG_SEL_THRESHOLD) {
-            for (int i0 = tid; i0 < m; i0 += kSpecThreads * U) {
-                uint32_t v[U];
+        return true;
+    }
+    if (p.mode == IG_SEL_THRESHOLD) {
+        for (int i0 = tid; i0 < m; i0 += kSpecThreads * U) {
+            uint32_t v[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < m ? ck[i0 + u * kSpecThreads] : 0u;
+            for (int u = 0; u < U; ++u) v[u] = i0 + u * kSpecThreads < m ? ck[i0 + u * kSpecThreads] : 0u;
 #pragma unroll
-                for (int u = 0; u < U; ++u) kmax = v[u] > kmax ? v[u] : kmax;
-            }
-        }
-        const uint32_t kmax_all = block_max_u32(kmax, sh);  // (also the barrier after fast_sel_init)
-        const SelCut c = spec_cut<false>(p, b, bh, m, p.n, kmax_all, GlobalKeys{ck}, sh, fs);
-        exact = !checked || (c.kth != 0u && c.kth >= emax);
-        if (exact) {
-            spec_emit<false>(p, b, bh, 0, m, c, GlobalKeys{ck}, keys, sh, fs, sm.last, gidx);
-            return;
+            for (int u = 0; u < U; ++u) kmax = v[u] > kmax ? v[u] : kmax;
         }
     }
-    // the recompute (top-k only): the row's n keys from its partial keys and the scaled partial query;
-    // the workspace counts the rows recomputed (word 4 of the status region)
+    const uint32_t kmax_all = block_max_u32(kmax, sh);  // (also the barrier after fast_sel_init)
+    const SelCut c = spec_cut<false>(p, b, bh, m, p.n, kmax_all, GlobalKeys{ck}, sh, fs);
+    if (checked && !(c.kth != 0u && c.kth >= emax)) return false;
+    spec_emit<false>(p, b, bh, 0, m, c, GlobalKeys{ck}, keys, sh, fs, sm.last, gidx);
+    return true;
+}
+
+// The exact fallback of a tight top-k merge: the row's n keys recomputed from its partial keys and the
+// scaled partial query, and the selection over them; the workspace counts the rows recomputed (word 4
+// of the status region).
+template <typename T, int LPR, int R>
+__device__ __forceinline__ void merge_recompute(const SpecParams& p, int b, int bh, uint32_t* keys, SpecShared<R>& sm) {
+    const int tid = threadIdx.x;
     if (tid == 0 && p.status) atomicAdd(p.status + 4, 1u);
     __syncthreads();  // every wave is done with the candidate cut's scratch
     if (tid < R) sm.q[tid] = p.q_rows[static_cast<size_t>(bh) * R + tid];
-    fast_sel_init(fs);
+    fast_sel_init(sm.fs);
     __syncthreads();
     const RowKeys<T, LPR> rk{static_cast<const T*>(p.Kp) + static_cast<size_t>(bh) * p.n_cap * R, sm.q};
-    spec_select<false>(p, b, bh, 0, p.n, p.n, 0u, rk, keys, sh, fs, sm.last, IdentityIdx());
+    spec_select<false>(p, b, bh, 0, p.n, p.n, 0u, rk, keys, sm.sh, sm.fs, sm.last, IdentityIdx());
+}
+
+// Merge workgroup of a sliced row.  Slice sl left its candidates in slots [sl * cap, +cap) of the row
+// (unused slots hold key 0, below every score key), so the m = slices * cap slots are in row order.
+// Without tight candidates they hold the row's selection: a key among the row's top c is among its
+// slice's top c, and a key at or above the row's threshold cut is at or above its slice's.  The
+// selection runs again over them with the row's rules.
+//
+// With tight top-k candidates a slice handed on only about its share of the row's budget, every key of
+// it at or above its bound E_s.  The row's kk-th largest candidate T' is then checked: when T' >= E_s for
+// every slice, every key of the row at or above T' is a candidate, so the kk-th largest key of the row is
+// T' and the row's top kk (ties to the lower index) are the candidates' top kk -- the selection is exact.
+// Otherwise (a slice held more of the row's top kk than its share) the row's scores are recomputed from
+// its partial keys (RowKeys, the same float32 arithmetic as the slices) and the selection runs over
+// them: exact as well, only slower.
+template <typename T, int LPR, int R>
+__device__ __forceinline__ void spec_merge(const SpecParams& p, int wg, uint32_t* keys, SpecShared<R>& sm) {
+    const int tid = threadIdx.x;
+    int b, h;
+    spec_bh(p, wg, &b, &h);
+    const int bh = b * p.H + h;
+    const int m = p.slices * p.cand_cap;
+    // the slices' candidate counts (a slice that could not compute its scores marks its count -1: the row
+    // fails) and, with tight candidates, their bounds
+    const bool checked = p.tight && p.mode == IG_SEL_TOPK;
+    int cnt = 0;
+    uint32_t lo = 0;
+    if (tid < p.slices) {
+        cnt = p.cand_cnt[static_cast<size_t>(bh) * p.slices + tid];
+        if (checked) lo = p.cand_lo[static_cast<size_t>(bh) * p.slices + tid];
+    }
+    const bool done = 2 * m <= kSpecMaxRows && p.cand_cap <= kSpecThreads
+                          ? merge_small(p, b, h, m, cnt, lo, checked, keys, sm)
+                          : merge_large(p, b, h, m, cnt, lo, checked, keys, sm);
+    if (!done) merge_recompute<T, LPR>(p, b, bh, keys, sm);
 }
 
 }  // namespace ig

@@ -29,8 +29,15 @@ template <typename T, int LPR>
 __global__ __launch_bounds__(kSpecThreads) void k_spec_merge(SpecParams p, CombineArgs cb) {
     extern __shared__ __align__(16) uint32_t keys[];  // the candidates' keys (up to kSpecMaxRows), or scratch
     __shared__ SpecShared<LPR * Vec<T>::N> sm;
+    // the combine's loads go out with the merge's first reads; its sums are formed after the merge
+    CombinePre pre;
+    const bool ahead = cb.part && cb.nsplit <= kCombinePre;
+    if (ahead) combine_load(cb, blockIdx.x, pre);
     spec_merge<T, LPR>(p, blockIdx.x, keys, sm);
-    if (cb.part) combine_item(cb, blockIdx.x);
+    if (ahead)
+        combine_store(cb, blockIdx.x, pre);
+    else if (cb.part)
+        combine_item(cb, blockIdx.x);
 }
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -127,7 +134,7 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     const size_t nw = (static_cast<size_t>(n) + 31) / 32;
     sp.off_bits = sp.off_idx + (sliced ? align256(cands * sizeof(int32_t)) : 0);
     sp.off_flags = sp.off_bits + (any_bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
-    sp.off_hcount = sp.off_flags + (any_bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
+    sp.off_hcount = sp.off_flags + (any_bits ? align256(touch_bits_ws_bytes(B, n)) : 0);
     sp.ws_bytes = sp.off_hcount + (ha.ok ? align256(static_cast<size_t>(rows) * sizeof(int32_t)) : 0);
     return sp;
 }
@@ -274,7 +281,7 @@ int finish_speculate(const SpecParams& p, int dtype, void* ws, hipStream_t s, co
     if (e || !p.bits) return e;
     const SpecPlan sp = plan_speculate(p.B, p.H, p.D, p.r, p.n, p.max_out, dtype, p.mode);
     return launch_touch_bits(p.counters, p.bits, p.B, p.H, p.n, p.n_cap, p.cmax,
-                             reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), p.victim, s);
+                             static_cast<char*>(ws) + sp.off_flags, p.victim, s);
 }
 
 // ------------------------------------------------------------------ ig_speculate_noalloc
@@ -307,11 +314,13 @@ static int noalloc_scratch(void** out) {
 }
 
 // Start of a no-allocation call: every word of [0, words) to zero except the shape stamp (words 2-3),
-// which gets this call's key, and the counter kernel's per-sequence flags (when the call has them).
-__global__ void k_scratch_reset(uint32_t* ws, size_t words, unsigned long long key, uint32_t* flags, int B) {
+// which gets this call's key, and the counter kernels' per-sequence flags (flag_words words, when the
+// call has them).
+__global__ void k_scratch_reset(uint32_t* ws, size_t words, unsigned long long key, uint32_t* flags,
+                                size_t flag_words) {
     const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < words) ws[i] = i == 2 ? static_cast<uint32_t>(key) : i == 3 ? static_cast<uint32_t>(key >> 32) : 0u;
-    if (flags && i < static_cast<size_t>(B)) flags[i] = 0u;
+    if (flags && i < flag_words) flags[i] = 0u;
 }
 
 int launch_speculate_noalloc(const SpecCall& c, hipStream_t s) {
@@ -326,9 +335,10 @@ int launch_speculate_noalloc(const SpecCall& c, hipStream_t s) {
     const size_t words = sp.off_cnt / sizeof(uint32_t);
     uint32_t* flags = sp.bits && c.counters ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags)
                                             : nullptr;
-    const size_t span = std::max(words, static_cast<size_t>(c.B));
+    const size_t flag_words = static_cast<size_t>(c.B);  // the counter kernels' saturation flags
+    const size_t span = std::max(words, flag_words);
     hipLaunchKernelGGL(k_scratch_reset, dim3(static_cast<unsigned>((span + 255) / 256)), dim3(256), 0, s,
-                       static_cast<uint32_t*>(ws), words, spec_shape_key(c.B, c.H, c.D, c.r), flags, c.B);
+                       static_cast<uint32_t*>(ws), words, spec_shape_key(c.B, c.H, c.D, c.r), flags, flag_words);
     if ((e = static_cast<int>(hipGetLastError()))) return e;
     return launch_speculate(c.x, c.Wq_part, c.bq_part, c.Kp, c.B, c.D, c.H, c.r, c.n, c.n_cap, c.dtype, c.scale,
                             c.mode, c.alpha, c.k, c.max_sel, c.idx, c.count, c.max_out, c.counters, c.cmax, c.victim,
