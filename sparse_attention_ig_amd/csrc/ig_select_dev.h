@@ -418,11 +418,12 @@ __device__ __forceinline__ int count_ge_lds(const uint32_t* lk, int n, uint32_t 
 // row >= T when need_eq >= eq_total), ascending.  Each wave owns a contiguous chunk of whole groups of
 // 64*E keys (E consecutive keys per lane): it counts its rows in registers, one barrier shares the
 // per-wave counts, and a second pass places each group with DPP prefix sums over the lanes' counts,
-// writing out[pos] = j and calling visit(pos, j).  Returns the number selected (block-uniform).  lk is
-// read by other waves while visit runs, so a visitor must not write lk.
+// writing out[pos] = j and calling visit(pos, j).  Returns the number selected (block-uniform), or -1
+// without placing anything when that number lies outside [win_lo, win_hi].  lk is read by other waves
+// while visit runs, so a visitor must not write lk.
 template <int NT, int E, class KS, typename Visit>
 __device__ int compact_e(KS lk, int n, uint32_t T, int need_eq, int eq_total, int32_t* __restrict__ out, int max_out,
-                         FastSel& fs, Visit visit) {
+                         FastSel& fs, Visit visit, int win_lo = 0, int win_hi = INT_MAX) {
     constexpr int NW = NT / kWave, G = kWave * E;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const bool all_eq = need_eq >= eq_total;
@@ -451,6 +452,7 @@ __device__ int compact_e(KS lk, int n, uint32_t T, int need_eq, int eq_total, in
     int eq_before = wave > 0 ? read_lane(incl_eq, wave - 1) : 0;
     const int gt_tot = read_lane(incl_gt, NW - 1), eq_tot = read_lane(incl_eq, NW - 1);
     const int take = all_eq ? eq_tot : min(eq_tot, need_eq);
+    if (gt_tot + take < win_lo || gt_tot + take > win_hi) return -1;  // uniform: block-wide counts
     int pos = gt_before + min(eq_before, take);
     for (int g0 = lo; g0 < hi; g0 += G) {  // whole wave in step: the DPP scans need every lane
         const int j0 = g0 + lane * E;
@@ -500,9 +502,10 @@ __device__ int compact_e(KS lk, int n, uint32_t T, int need_eq, int eq_total, in
 
 template <int NT = kSelThreads, class KS, typename Visit = NoVisit>
 __device__ int compact_keys(KS lk, int n, uint32_t T, int need_eq, int eq_total, int32_t* __restrict__ out,
-                            int max_out, FastSel& fs, Visit visit) {
-    if (n >= KS::kE * NT) return compact_e<NT, KS::kE>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
-    return compact_e<NT, 1>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit);
+                            int max_out, FastSel& fs, Visit visit, int win_lo = 0, int win_hi = INT_MAX) {
+    if (n >= KS::kE * NT)
+        return compact_e<NT, KS::kE>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit, win_lo, win_hi);
+    return compact_e<NT, 1>(lk, n, T, need_eq, eq_total, out, max_out, fs, visit, win_lo, win_hi);
 }
 
 template <int NT = kSelThreads, typename Visit = NoVisit>
@@ -592,11 +595,14 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
     return true;
 }
 
-// A superset of the top kk of ks[0..n) of at most `cap` keys: every key >= L, for L the sample's
-// r-th largest key (r as in sampled_kth), when at least kk and at most cap keys are >= L (the top kk
-// are then among them).  Returns false (histograms cleared again) when that count is out of range.
+// A bound for a superset of the top kk of ks[0..n) of at most `cap` keys: L = the sample's r-th
+// largest key (r as in sampled_kth), so that about kk plus a margin keys are >= L.  Whether their count
+// really lies in [kk, cap] (the top kk are then among them) is for the caller to check, e.g. with the
+// window of compact_keys.  Returns false (nothing decided) when the row is too short to sample.  The
+// sample's passes leave counts in the histograms (waves may still be reading the last one): a select
+// that follows needs a barrier, then fast_sel_init and another barrier.
 template <int NT = kSelThreads, class KS>
-__device__ bool sampled_superset(KS lk, int n, int kk, int cap, FastSel& fs, SelScratch& sh, uint32_t* L_out) {
+__device__ bool sampled_bound(KS lk, int n, int kk, int cap, FastSel& fs, uint32_t* L_out) {
     const int tid = threadIdx.x;
     if (n < 8 * NT || cap < kk) return false;
     const double expect = static_cast<double>(kk) * NT / n;
@@ -605,14 +611,9 @@ __device__ bool sampled_superset(KS lk, int n, int kk, int cap, FastSel& fs, Sel
     uint32_t* sample = fs.words + kSampleBase;
     sample[tid] = lk.at(static_cast<int>(static_cast<int64_t>(tid) * n / NT));
     __syncthreads();
-    uint32_t L;
     int ne, et;
-    radix_kth_lds<NT>(sample, NT, r_lo, fs, &L, &ne, &et);
-    const int c = count_ge<NT>(lk, n, L, sh);
-    fast_sel_init(fs);  // (the compaction that follows needs no histograms; a fallback needs clean ones)
-    __syncthreads();
-    *L_out = L;
-    return c >= kk && c <= cap;  // uniform: c is a block sum
+    radix_kth_lds<NT>(sample, NT, r_lo, fs, L_out, &ne, &et);
+    return true;
 }
 
 template <int NT = kSelThreads>

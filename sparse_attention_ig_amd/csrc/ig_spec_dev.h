@@ -318,10 +318,13 @@ struct LdsIdx {
 constexpr int kSampledMin = 16384;  // keys from which a selection first tries the sampled bracket
 
 // The cut of a selection.  Selecting every key above kth and the first need_eq keys equal to it (of
-// eq_total equal keys; every key >= kth when need_eq >= eq_total) gives the selection.
+// eq_total equal keys; every key >= kth when need_eq >= eq_total) gives the selection.  A slice's cut
+// from a sampled bound (win_lo > 0) is good only when it selects between win_lo (its kk) and cand_cap
+// keys; the compaction checks that count before it places anything.
 struct SelCut {
     uint32_t kth;
     int need_eq, eq_total;
+    int kk, win_lo;
 };
 
 // Keys a slice of `rows` of a row's n rows hands on for a top-kk selection of the row with tight
@@ -333,18 +336,27 @@ __device__ __forceinline__ int tight_slice_k(int kk_row, int rows, int n, int ca
     return min(min(want, rows), cap);
 }
 
+// The exact cut of the top kk of ks[0..m) (fast_sel_init and a barrier before): the sampled bracket
+// pays off on long rows; below kSampledMin keys the radix over every key is faster.
+template <class KS>
+__device__ __forceinline__ void exact_cut(KS keys, int m, int kk, FastSel& fs, SelScratch& sh, SelCut& c) {
+    if (m < kSampledMin || !sampled_kth(keys, m, kk, fs, sh, &c.kth, &c.need_eq, &c.eq_total))
+        radix_kth_keys(keys, m, kk, fs, &c.kth, &c.need_eq, &c.eq_total);
+}
+
 // The cut of the selection over the keys ks[0..m) (held in LDS, a merge's candidates in global memory,
 // or a row recomputed from its partial keys).  `rows`: the row count the limit refers to (the slice's
 // length in a slice workgroup, n otherwise).  TO_CANDS (a slice): the cut of a superset of the slice's
-// selection of at most cand_cap keys -- every key at or above a sampled lower bound of the slice's cut
-// when they fit; with tight top-k candidates, of the slice's share of the row's budget.
+// selection of at most cand_cap keys -- every key at or above a sampled lower bound of the slice's cut,
+// to be checked by the compaction (win_lo); with tight top-k candidates, of the slice's share of the
+// row's budget.
 template <bool TO_CANDS, class KS>
 __device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, int m, int rows, uint32_t kmax_all,
                                            KS keys, SelScratch& sh, FastSel& fs) {
     int limit = min(rows, p.max_out);
     bool done = false;
     int kk = 0;
-    SelCut c{0u, INT_MAX, INT_MAX};
+    SelCut c{0u, INT_MAX, INT_MAX, 0, 0};
     if (p.mode == IG_SEL_HEADAVG) {
         if constexpr (TO_CANDS) {
             // a whole row of a head-average call: its threshold count for the sequence's average, and as
@@ -382,23 +394,27 @@ __device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, i
             if (p.tight) kk = tight_slice_k(min(p.k, min(p.n, p.max_out)), rows, p.n, p.cand_cap);
         }
     }
+    c.kk = kk;
     if constexpr (TO_CANDS) {
-        if (!done && p.cand_cap > kk + kk / 8 && sampled_superset(keys, m, kk, p.cand_cap, fs, sh, &c.kth)) done = true;
+        if (!done && p.cand_cap > kk + kk / 8 && sampled_bound(keys, m, kk, p.cand_cap, fs, &c.kth)) {
+            c.win_lo = kk;  // every key >= the bound, when there are kk to cand_cap of them
+            return c;
+        }
     }
-    // the sampled bracket pays off on long rows; below kSampledMin keys the radix over every key is faster
-    if (!done && (m < kSampledMin || !sampled_kth(keys, m, kk, fs, sh, &c.kth, &c.need_eq, &c.eq_total)))
-        radix_kth_keys(keys, m, kk, fs, &c.kth, &c.need_eq, &c.eq_total);
+    if (!done) exact_cut(keys, m, kk, fs, sh, c);
     return c;
 }
 
 // The results of a selection with cut c over ks[0..m): gidx(j) is the row index of key j; lds: at least
 // 1024 words of LDS scratch (may be the keys' own storage).  TO_CANDS: write the selected keys and row
-// indices as this slice's candidates (at most cand_cap keys; the slice's unused candidate slots get key
-// 0, below every score key) and, with tight candidates, the slice's bound; otherwise write idx / count
-// and update the counters (one integer atomic per selected slot, all in flight together; the last
-// workgroup of sequence b halves if any slot saturated and picks the victim).
+// indices as this slice's candidates (at most cand_cap keys; when the merge may read the candidate
+// arrays whole, the slice's unused slots get key 0, below every score key) and, with tight candidates,
+// the slice's bound; returns false, having written nothing, when a sampled cut selects a count outside
+// its window.  Otherwise write idx / count and update the counters (one integer atomic per selected
+// slot, all in flight together; the last workgroup of sequence b halves if any slot saturated and picks
+// the victim).
 template <bool TO_CANDS, class KS, typename GIdx>
-__device__ __forceinline__ void spec_emit(const SpecParams& p, int b, int bh, int slice, int m, const SelCut& c,
+__device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, int slice, int m, const SelCut& c,
                                           KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs, int& s_last,
                                           GIdx gidx) {
     const int tid = threadIdx.x;
@@ -412,16 +428,20 @@ __device__ __forceinline__ void spec_emit(const SpecParams& p, int b, int bh, in
             ck[pos] = keys.at(j);
             ci[pos] = gidx(j);
         };
-        const int written = min(compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put),
-                                p.cand_cap);
-        for (int i = written + tid; i < p.cand_cap; i += kSpecThreads) ck[i] = 0u;
+        const int got = compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put, c.win_lo,
+                                     c.win_lo > 0 ? p.cand_cap : INT_MAX);
+        if (got < 0) return false;
+        const int written = min(got, p.cand_cap);
+        // (a merge reads the candidate arrays whole only when they exceed its LDS)
+        if (static_cast<int64_t>(p.slices) * p.cand_cap > kSpecMaxRows)
+            for (int i = written + tid; i < p.cand_cap; i += kSpecThreads) ck[i] = 0u;
         if (tid == 0) {
             p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = written;
             // every key above kth was handed on, and every key equal to it unless only some of the ties
             // were taken: the keys are integers, so the bound is kth or kth + 1
             if (p.cand_lo) p.cand_lo[static_cast<size_t>(bh) * p.slices + slice] = need_eq >= eq_total ? kth : kth + 1u;
         }
-        return;
+        return true;
     } else {
         const int n = p.n;
         uint32_t* crow = p.counters ? p.counters + static_cast<size_t>(b) * p.n_cap : nullptr;
@@ -461,7 +481,7 @@ __device__ __forceinline__ void spec_emit(const SpecParams& p, int b, int bh, in
             }
         }
         if (tid == 0) p.count[bh] = min(written, p.max_out);
-        if (!crow) return;
+        if (!crow) return true;
         __syncthreads();
         if (p.bits) {
             // the row's selection as a bitmap of its n slots, built in LDS and written out whole
@@ -476,7 +496,7 @@ __device__ __forceinline__ void spec_emit(const SpecParams& p, int b, int bh, in
             __syncthreads();
             uint32_t* dst = p.bits + static_cast<size_t>(bh) * nw;
             for (int i = tid; i < nw; i += kSpecThreads) dst[i] = lds[i];
-            return;
+            return true;
         }
         int sat = 0;
         // (written <= max_out and every staged index is < n by construction; both are re-checked so
@@ -508,6 +528,7 @@ __device__ __forceinline__ void spec_emit(const SpecParams& p, int b, int bh, in
         }
         }
         seq_arrive(p, b, __syncthreads_or(sat) != 0, lds, sh, s_last);
+        return true;
     }
 }
 
@@ -517,7 +538,14 @@ __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, 
                                             uint32_t kmax_all, KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs,
                                             int& s_last, GIdx gidx) {
     const SelCut c = spec_cut<TO_CANDS>(p, b, bh, m, rows, kmax_all, keys, sh, fs);
-    spec_emit<TO_CANDS>(p, b, bh, slice, m, c, keys, lds, sh, fs, s_last, gidx);
+    if (spec_emit<TO_CANDS>(p, b, bh, slice, m, c, keys, lds, sh, fs, s_last, gidx)) return;
+    // a sampled bound whose superset held too few or too many keys: the exact cut of the slice's kk
+    __syncthreads();  // every wave is done with the sample's histograms
+    fast_sel_init(fs);
+    __syncthreads();
+    SelCut e{0u, INT_MAX, INT_MAX, c.kk, 0};
+    exact_cut(keys, m, c.kk, fs, sh, e);
+    spec_emit<TO_CANDS>(p, b, bh, slice, m, e, keys, lds, sh, fs, s_last, gidx);
 }
 
 // Score keys of a whole row recomputed from its partial keys (the exact fallback of a merge whose tight
@@ -714,8 +742,8 @@ __device__ __forceinline__ void merge_empty_part(const SpecParams& p, int b, int
 }
 
 // A merge whose candidate slots fit in LDS twice over (keys and row indices) with at most one slot per
-// thread and slice.  One round trip reads every slot of every slice (an unused slot holds key 0: read,
-// then dropped) together with the slices' counts and bounds; the used slots go to LDS in row order.
+// thread and slice.  One round trip reads every slot of every slice (an unused slot is read, then
+// dropped) together with the slices' counts and bounds; the used slots go to LDS in row order.
 // With tight candidates the row's cut is searched among the keys at or above E = the largest slice
 // bound only: the merge is exact exactly when at least kk candidates reach E (then the kk-th largest
 // key T' >= E), and those keys lie in [E, the largest key].  Returns false when the row must be
@@ -912,7 +940,8 @@ __device__ __forceinline__ void merge_recompute(const SpecParams& p, int b, int 
 }
 
 // Merge workgroup of a sliced row.  Slice sl left its candidates in slots [sl * cap, +cap) of the row
-// (unused slots hold key 0, below every score key), so the m = slices * cap slots are in row order.
+// (when the slots exceed the merge's LDS, unused ones hold key 0, below every score key), so the
+// m = slices * cap slots are in row order.
 // Without tight candidates they hold the row's selection: a key among the row's top c is among its
 // slice's top c, and a key at or above the row's threshold cut is at or above its slice's.  The
 // selection runs again over them with the row's rules.
