@@ -424,14 +424,31 @@ __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, in
         const size_t base = (static_cast<size_t>(bh) * p.slices + slice) * p.cand_cap;
         uint32_t* ck = p.cand_key + base;
         int32_t* ci = p.cand_idx + base;
+        // the candidates are staged in LDS (the select's scratch words are free by the compaction's
+        // placing pass) and written out coalesced, when they fit there
+        const bool staged = 2 * p.cand_cap <= kFastStage;
+        uint32_t* sk = fs.stage();
+        int32_t* si = reinterpret_cast<int32_t*>(sk + p.cand_cap);
         auto put = [&](int pos, int j) {
-            ck[pos] = keys.at(j);
-            ci[pos] = gidx(j);
+            if (staged) {
+                sk[pos] = keys.at(j);
+                si[pos] = gidx(j);
+            } else {
+                ck[pos] = keys.at(j);
+                ci[pos] = gidx(j);
+            }
         };
         const int got = compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put, c.win_lo,
                                      c.win_lo > 0 ? p.cand_cap : INT_MAX);
         if (got < 0) return false;
         const int written = min(got, p.cand_cap);
+        if (staged) {
+            __syncthreads();
+            for (int i = tid; i < written; i += kSpecThreads) {
+                ck[i] = sk[i];
+                ci[i] = si[i];
+            }
+        }
         // (a merge reads the candidate arrays whole only when they exceed its LDS)
         if (static_cast<int64_t>(p.slices) * p.cand_cap > kSpecMaxRows)
             for (int i = written + tid; i < p.cand_cap; i += kSpecThreads) ck[i] = 0u;
@@ -450,13 +467,19 @@ __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, in
         int32_t* out = p.idx + static_cast<size_t>(bh) * p.max_out;
         int written;
         if constexpr (std::is_same<GIdx, IdentityIdx>::value || std::is_same<GIdx, LdsIdx>::value) {
-            // the row index of each selected key is at hand: written as the key is placed
+            // the row index of each selected key is at hand: staged in LDS as the key is placed (beyond
+            // the staging words, written straight out), then written out coalesced
             auto keep = [&](int pos, int j) {
                 const int g = gidx(j);
-                out[pos] = g;
-                if (pos < kFastStage) stage[pos] = static_cast<uint32_t>(g);
+                if (pos < kFastStage)
+                    stage[pos] = static_cast<uint32_t>(g);
+                else
+                    out[pos] = g;
             };
             written = compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
+            __syncthreads();
+            const int ws = min(min(written, p.max_out), kFastStage);
+            for (int i = tid; i < ws; i += kSpecThreads) out[i] = static_cast<int32_t>(stage[i]);
         } else {
             // key positions first, then every position mapped to its row index with batched loads
             written = compact_keys(keys, m, kth, need_eq, eq_total, out, p.max_out, fs, NoVisit());
@@ -479,10 +502,10 @@ __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, in
                     }
                 }
             }
+            __syncthreads();
         }
         if (tid == 0) p.count[bh] = min(written, p.max_out);
         if (!crow) return true;
-        __syncthreads();
         if (p.bits) {
             // the row's selection as a bitmap of its n slots, built in LDS and written out whole
             const int nw = (n + 31) / 32;
