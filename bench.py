@@ -5,9 +5,11 @@ Default workload: the long-context Llama-2-7B-shaped decode layer (hidden 4096, 
 batch 4, context 131072, 32 partial channels, bf16 storage, fp32 accumulation), top 4% of the
 context (5243 rows) per head, all KV resident in HBM -- the largest of the single-GPU workloads.
 One step = one decode step through ``--layers`` distinct layer buffers (distinct HBM buffers with
-the same contents, so that the 256 MB Infinity Cache cannot serve the working set), each running
-the whole hot path: partial query, speculated scores, selection, counters (the speculation for
-layer l+1) and the sparse attention of layer l, one ig_decode_layer call per layer.
+the same contents, so that the 256 MB Infinity Cache cannot serve the working set; by default the
+model's 32 layers, as many as fit in 96 GB: 9 at the default workload), each running the whole hot
+path: partial query, speculated scores, selection, counters (the speculation for layer l+1) and the
+sparse attention of layer l, one ig_decode_layer call per layer (the first layer's speculation and
+the last layer's attention run alone).
 
 Prints one JSON line: tokens/s per layer (= batch x layers x steps / time), the roofline of the
 dominant call (algorithmic bytes per call over its average duration from HIP events, against
@@ -57,7 +59,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=0,
-                    help="distinct layer buffers per step (default: 32 for opt-6.7b, else as many as make 2 GB, "
+                    help="distinct layer buffers per step (default: the model's 32 layers, as many as fit in 96 GB, "
                          "at least 2)")
     ap.add_argument("--mode", choices=["topk", "threshold"], default="topk")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
@@ -161,6 +163,10 @@ def emit(out: dict) -> int:
     return 0
 
 
+MODEL_LAYERS = 32            # decoder layers of OPT-6.7B and Llama-2-7B
+LAYER_BUDGET_BYTES = 96e9    # HBM given to a step's distinct layer buffers
+
+
 def layer_workload(name: str, mode: str, n: int = 0, batch: int = 0, frac: float = 0.04):
     """(spec, step kwargs, workload name) of a single-layer workload."""
     from sparse_attention_ig_amd import gen
@@ -189,7 +195,9 @@ def bench_layer(args, spec, step_kw, wl, quiet: bool = False):
     print(f"[bench] preparing {wl}", file=sys.stderr, flush=True)
     host = prepare_layer(spec)
     base = DeviceLayer(host, max_out=step_kw["max_out"])
-    n_layers = args.layers or (32 if args.workload == "opt-6.7b" else max(2, int(math.ceil(2e9 / base.nbytes()))))
+    # a decode step through as many distinct layer buffers as the model has (32 for OPT-6.7B and
+    # Llama-2-7B), as far as 96 GB of them fit (a third of the HBM), at least 2
+    n_layers = args.layers or max(2, min(MODEL_LAYERS, int(LAYER_BUDGET_BYTES // base.nbytes())))
     base.keep_scores = args.path == "unfused"   # the fused path keeps the scores on chip
     layers = [base] + [base.clone() for _ in range(n_layers - 1)]
     del host

@@ -8,16 +8,17 @@
 // One grid holds three roles: the partial-query projection workgroups for
 // layer l+1 first, then one spec_row workgroup per (b, h) (or per slice of a
 // long row) for layer l+1, which waits only for the projection workgroups
-// (lower indices, never waiting themselves), and the attention items of layer
-// l (one (b, h, split) each, all 1024 threads of the workgroup on it): whole
-// rows all before the attention items, which take the slots the projection
-// leaves; slices interleaved with them (a merge launch then selects among the
-// slices' candidates).  The row workgroups are resident from the start, with
-// their first partial-key loads in flight while the partial sums are made.  The attention and the
-// speculation touch disjoint buffers; a CU holds two workgroups, and the
-// attention's K/V gathers fill the memory pipeline while the speculation is in
-// its latency-bound selection.  Splits of an attention row are merged by the
-// usual combine kernel afterwards.
+// (lower indices, never waiting themselves), then the attention items of
+// layer l (one (b, h, split) each, all 1024 threads of the workgroup on it).
+// The attention items take the slots the rows leave as they finish, so the
+// two roles overlap where the speculation's rows end and are in their
+// latency-bound selection.  (With long rows cut into slices, placing the
+// attention items among the slices instead measured slower: their scattered
+// K/V row reads and the slices' partial-key streams share the memory system
+// worse than the two phases do one after the other.)  The attention and the
+// speculation touch disjoint buffers; a CU holds two workgroups.  Sliced rows
+// are merged by a launch of their own, which also combines the attention's
+// splits; otherwise the usual combine kernel follows.
 #include "ig_attn_dev.h"
 #include "ig_spec_dev.h"
 
@@ -40,36 +41,8 @@ union DecodeShared {
 // faster at 205-218 rows per item).
 constexpr int kDecodeSpecBatch = 4;
 
-// The roles of the nr + na workgroups after the projection's (nr row workgroups, na attention items):
-// with a_per > 0 (sliced rows, whose many slice workgroups come in several waves), blocks of a_per row
-// workgroups and one attention item, until one kind runs out, then the rest of the other, so that the
-// attention's gathers run beside the slices' streams; else every row workgroup first.  Row and item
-// indices each count up from 0 in position order.
-__device__ __forceinline__ void decode_role(int c, int nr, int na, int a_per, int* row, int* item) {
-    *row = -1;
-    *item = -1;
-    if (a_per <= 0) {
-        if (c < nr) *row = c; else *item = c - nr;
-        return;
-    }
-    const int64_t per = a_per + 1;
-    // the position where the pattern runs out of one kind: the end of the last attention item's block,
-    // or just after the last row's slot
-    const bool items_first = static_cast<int64_t>(na) * a_per <= nr;
-    const int64_t c_end = items_first ? na * per : (nr / a_per) * per + nr % a_per;
-    if (c < c_end) {
-        const int blk = static_cast<int>(c / per), off = static_cast<int>(c - blk * per);
-        if (off < a_per) *row = blk * a_per + off; else *item = blk;
-    } else if (items_first) {
-        *row = static_cast<int>(static_cast<int64_t>(na) * a_per + (c - c_end));
-    } else {
-        *item = static_cast<int>(nr / a_per + (c - c_end));
-    }
-}
-
 template <typename T, int LPR_S, int LPR_A, int ROWS>
-__global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int bh_attn,
-                                                                     int a_per) {
+__global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p, AttnArgs a, int bh_attn) {
     extern __shared__ __align__(16) uint32_t keys[];  // staged x (projection) or the speculation's score keys
     __shared__ DecodeShared<LPR_S * Vec<T>::N, LPR_A, Vec<T>::N> sm;
     const int wg = blockIdx.x;
@@ -77,12 +50,14 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void k_decode_layer(SpecParams p
         proj_role<T>(p, wg, keys);
         return;
     }
-    int row, item;
-    decode_role(wg - p.proj_wgs, p.row_wgs, a.nsplit * bh_attn, a_per, &row, &item);
-    if (row >= 0)
-        spec_row<T, LPR_S, kDecodeSpecBatch>(p, row, keys, sm.spec);
-    else
+    // every row workgroup (or slice) first, then the attention items
+    const int c = wg - p.proj_wgs;
+    if (c < p.row_wgs) {
+        spec_row<T, LPR_S, kDecodeSpecBatch>(p, c, keys, sm.spec);
+    } else {
+        const int item = c - p.row_wgs;
         attn_item<T, LPR_A, kDecodeThreads, ROWS>(a, item % bh_attn, item / bh_attn, sm.attn);
+    }
 }
 
 template <typename T, int LPR_S, int LPR_A, int ROWS>
@@ -97,9 +72,8 @@ static int launch_fused(const SpecParams& p, const AttnArgs& a, int bh_attn, hip
     }
     const int items = a.nsplit * bh_attn;
     const int grid = p.proj_wgs + p.row_wgs + items;
-    const int a_per = p.slices > 1 ? (p.row_wgs + items - 1) / items : 0;
     hipLaunchKernelGGL((k_decode_layer<T, LPR_S, LPR_A, ROWS>), dim3(grid), dim3(kDecodeThreads),
-                       speculate_lds_bytes(p.slice_rows), s, p, a, bh_attn, a_per);
+                       speculate_lds_bytes(p.slice_rows), s, p, a, bh_attn);
     return static_cast<int>(hipGetLastError());
 }
 

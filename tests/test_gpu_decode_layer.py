@@ -63,7 +63,7 @@ CASES = [
     ("bf16-rows2-218", lambda: _spec(gen.opt_6_7b(n=4352, B=8), topk=218),
      lambda: _spec(gen.opt_6_7b(n=4352, B=8), topk=218, seed=2008), dict(mode="topk", k=218, max_out=218)),
     # a long speculated row cut into 16 slices of 2500 rows (tight top-k candidates, a merge launch),
-    # its slice workgroups interleaved with the attention items in the one launch
+    # its slice workgroups before the attention items in the one launch
     ("bf16-sliced-topk", lambda: _spec(gen.opt_6_7b(n=3000, B=1), H=4, topk=400),
      lambda: _spec(gen.llama2_7b_long(n=40000, B=1), H=4, topk=400, seed=2009), dict(mode="topk", k=400, max_out=400)),
     # the head average (every head of a sequence takes the mean threshold count): whole rows hand on

@@ -154,7 +154,7 @@ def test_long_context_b4_full_size():
 def test_long_context_b4_decode_layer_full_size():
     """ig_decode_layer at the benchmark's workload (B4, n = 131072, top 4%): the attention of a layer
     over its own speculated rows beside the speculation of a copy of it (16 slices of 8192 rows per row,
-    interleaved with the attention items; a merge and the bitmap counter kernels after).  Every head of
+    then the attention items, in one launch; a merge and the bitmap counter kernels after).  Every head of
     both halves against the oracle (one layer's draws serve both: a copy has the same caches)."""
     import torch
     from sparse_attention_ig_amd.runtime import DeviceLayer, decode_layer
