@@ -16,6 +16,8 @@
 // Gather: 16-byte copies of whole rows; the source may be pinned host memory
 // mapped into the device address space, in which case the reads travel over
 // the host link (zero-copy) and the writes land in HBM.
+#include <algorithm>
+
 #include "ig_device.h"
 #include "ig_internal.h"
 #include "ig_pool_dev.h"
@@ -236,41 +238,67 @@ int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, i
     return static_cast<int>(hipGetLastError());
 }
 
-// rows of RB bytes (RB % 16 == 0), LPR = RB / 16 lanes per row
+// rows of RB bytes (RB % 16 == 0), LPR = RB / 16 lanes per row.  The work is cut into units of
+// kGatherRows rows of one (b, h); a grid of at most kGatherMaxWgs workgroups walks the units (workgroup w
+// takes units w, w + gridDim.x, ..), so that a gather over the host link, which needs only enough reads
+// in flight to cover the link's latency, leaves most of the GPU to kernels on other streams.  Every
+// lane issues the loads of all its rows of a unit before any store.
+constexpr int kGatherRows = 64;
+constexpr int kGatherMaxWgs = 128;
 __global__ __launch_bounds__(kGatherThreads) void k_gather(const char* __restrict__ K, const char* __restrict__ V,
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ count, int row_bytes,
-                                                          int n_cap, int max_out, int rows_per_block,
+                                                          int n_cap, int max_out, int chunks, int64_t units,
                                                           char* __restrict__ Kc, char* __restrict__ Vc) {
-    const int bh = blockIdx.y;
-    const int c = min(count[bh], max_out);
+    constexpr int U = kGatherRows / (kGatherThreads / 16);  // rows per lane and unit at the widest row
     const int lpr = row_bytes / 16;
     const int rows_per_step = kGatherThreads / lpr;
     const int li = threadIdx.x % lpr, ri = threadIdx.x / lpr;
     if (ri >= rows_per_step) return;
-    const int i0 = blockIdx.x * rows_per_block;
-    const int i1 = min(c, i0 + rows_per_block);
-    const size_t src_head = static_cast<size_t>(bh) * n_cap * row_bytes;
-    const size_t dst_head = static_cast<size_t>(bh) * max_out * row_bytes;
-    for (int i = i0 + ri; i < i1; i += rows_per_step) {
-        int j = idx[static_cast<size_t>(bh) * max_out + i];
-        j = min(max(j, 0), n_cap - 1);
-        const size_t so = src_head + static_cast<size_t>(j) * row_bytes + li * 16;
-        const size_t dof = dst_head + static_cast<size_t>(i) * row_bytes + li * 16;
-        const uint4 kv = load_raw16(K + so);
-        const uint4 vv = load_raw16(V + so);
-        store_raw16(Kc + dof, kv);
-        store_raw16(Vc + dof, vv);
+    for (int64_t u0 = blockIdx.x; u0 < units; u0 += gridDim.x) {
+        const int64_t bh = u0 / chunks;
+        const int chunk = static_cast<int>(u0 - bh * chunks);
+        const int c = min(count[bh], max_out);
+        const int i0 = chunk * kGatherRows;
+        const int i1 = min(c, i0 + kGatherRows);
+        const size_t src_head = static_cast<size_t>(bh) * n_cap * row_bytes;
+        const size_t dst_head = static_cast<size_t>(bh) * max_out * row_bytes;
+        for (int ib = i0 + ri; ib < i1; ib += rows_per_step * U) {
+            int j[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = ib + u * rows_per_step;
+                j[u] = i < i1 ? min(max(idx[static_cast<size_t>(bh) * max_out + i], 0), n_cap - 1) : -1;
+            }
+            uint4 kv[U], vv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j[u] >= 0) {
+                    const size_t so = src_head + static_cast<size_t>(j[u]) * row_bytes + li * 16;
+                    kv[u] = load_raw16(K + so);
+                    vv[u] = load_raw16(V + so);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j[u] >= 0) {
+                    const size_t dof = dst_head + static_cast<size_t>(ib + u * rows_per_step) * row_bytes + li * 16;
+                    store_raw16(Kc + dof, kv[u]);
+                    store_raw16(Vc + dof, vv[u]);
+                }
+            }
+        }
     }
 }
 
 int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_t* count, int B, int H, int d,
                   int n_cap, int max_out, int dtype, void* Kc, void* Vc, hipStream_t s) {
     const int row_bytes = d * (dtype == IG_BF16 ? 2 : 4);
-    const int rows_per_block = 64;
-    const dim3 grid((max_out + rows_per_block - 1) / rows_per_block, B * H);
-    hipLaunchKernelGGL(k_gather, grid, dim3(kGatherThreads), 0, s, static_cast<const char*>(K),
-                       static_cast<const char*>(V), idx, count, row_bytes, n_cap, max_out, rows_per_block,
+    const int chunks = (max_out + kGatherRows - 1) / kGatherRows;
+    const int64_t units = static_cast<int64_t>(chunks) * B * H;
+    const int grid = static_cast<int>(std::min<int64_t>(units, kGatherMaxWgs));
+    hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kGatherThreads), 0, s, static_cast<const char*>(K),
+                       static_cast<const char*>(V), idx, count, row_bytes, n_cap, max_out, chunks, units,
                        static_cast<char*>(Kc), static_cast<char*>(Vc));
     return static_cast<int>(hipGetLastError());
 }

@@ -22,6 +22,7 @@
 //   k_gather_q4      one thread per group of a selected record (device or
 //                    host-mapped memory): dequantised, v = m16 + code * s16 in
 //                    float32, into compact K and V rows
+#include <algorithm>
 #include <hip/hip_fp16.h>
 
 #include "ig_device.h"
@@ -124,29 +125,41 @@ __device__ __forceinline__ void dequant_group(const unsigned char* r, int d, int
         v[e] = mf + static_cast<float>((w[e / 8] >> (4 * (e % 8))) & 15u) * sf;
 }
 
-// grid (row blocks, B*H); one thread per group of a selected row
+// One thread per group of a selected row.  As in the row gather, the work is cut into units of
+// kGatherQ4Rows rows of one (b, h) and a grid of at most kGatherQ4MaxWgs workgroups walks them, so that
+// the host-link reads leave most of the GPU to kernels on other streams; each thread has two rows'
+// records in flight.
+constexpr int kGatherQ4Rows = 64;
+constexpr int kGatherQ4MaxWgs = 128;
 template <typename TO>
 __global__ __launch_bounds__(kQThreads) void k_gather_q4(const unsigned char* __restrict__ KVq,
                                                          const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ count, int d, int q_rows,
-                                                         int max_out, int rec, int rows_per_block,
+                                                         int max_out, int rec, int chunks, int64_t units,
                                                          TO* __restrict__ Kc, TO* __restrict__ Vc) {
-    const int bh = blockIdx.y;
-    const int c = min(count[bh], max_out);
     const int gpr = d / kQGroup;
     const int rows_per_step = kQThreads / (2 * gpr);
     const int g = threadIdx.x % (2 * gpr), ri = threadIdx.x / (2 * gpr);  // K groups, then V groups
     if (ri >= rows_per_step) return;
-    const int i0 = blockIdx.x * rows_per_block;
-    const int i1 = min(c, i0 + rows_per_block);
-    for (int i = i0 + ri; i < i1; i += rows_per_step) {
-        int j = idx[static_cast<size_t>(bh) * max_out + i];
-        j = min(max(j, 0), q_rows - 1);
-        const size_t src = (static_cast<size_t>(bh) * q_rows + j) * rec;
-        const size_t dst = (static_cast<size_t>(bh) * max_out + i) * d + (g % gpr) * kQGroup;
-        float v[kQGroup];
-        dequant_group(KVq + src, d, g, v);
-        store_group((g < gpr ? Kc : Vc) + dst, v);
+    TO* dst_base = g < gpr ? Kc : Vc;
+    for (int64_t u0 = blockIdx.x; u0 < units; u0 += gridDim.x) {
+        const int64_t bh = u0 / chunks;
+        const int i0 = static_cast<int>(u0 - bh * chunks) * kGatherQ4Rows;
+        const int c = min(count[bh], max_out);
+        const int i1 = min(c, i0 + kGatherQ4Rows);
+        for (int i = i0 + ri; i < i1; i += 2 * rows_per_step) {
+            const int ib = i + rows_per_step;
+            const bool two = ib < i1;
+            int j0 = idx[static_cast<size_t>(bh) * max_out + i];
+            int j1 = two ? idx[static_cast<size_t>(bh) * max_out + ib] : 0;
+            j0 = min(max(j0, 0), q_rows - 1);
+            j1 = min(max(j1, 0), q_rows - 1);
+            float v0[kQGroup], v1[kQGroup];
+            dequant_group(KVq + (static_cast<size_t>(bh) * q_rows + j0) * rec, d, g, v0);
+            if (two) dequant_group(KVq + (static_cast<size_t>(bh) * q_rows + j1) * rec, d, g, v1);
+            store_group(dst_base + (static_cast<size_t>(bh) * max_out + i) * d + (g % gpr) * kQGroup, v0);
+            if (two) store_group(dst_base + (static_cast<size_t>(bh) * max_out + ib) * d + (g % gpr) * kQGroup, v1);
+        }
     }
 }
 
@@ -169,16 +182,17 @@ int launch_quantize(const void* K, const void* V, int B, int H, int d, int ld_ro
 
 int launch_gather_q4(const void* KVq, const int32_t* idx, const int32_t* count, int B, int H, int d, int q_rows,
                      int max_out, int dtype_out, void* Kc, void* Vc, hipStream_t s) {
-    const int rows_per_block = 64;
-    const dim3 grid((max_out + rows_per_block - 1) / rows_per_block, B * H);
+    const int chunks = (max_out + kGatherQ4Rows - 1) / kGatherQ4Rows;
+    const int64_t units = static_cast<int64_t>(chunks) * B * H;
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, kGatherQ4MaxWgs)));
     const int rec = static_cast<int>(int4_record_bytes(d));
     const auto* kv = static_cast<const unsigned char*>(KVq);
     if (dtype_out == IG_BF16)
         hipLaunchKernelGGL((k_gather_q4<uint16_t>), grid, dim3(kQThreads), 0, s, kv, idx, count, d, q_rows, max_out,
-                           rec, rows_per_block, static_cast<uint16_t*>(Kc), static_cast<uint16_t*>(Vc));
+                           rec, chunks, units, static_cast<uint16_t*>(Kc), static_cast<uint16_t*>(Vc));
     else
         hipLaunchKernelGGL((k_gather_q4<float>), grid, dim3(kQThreads), 0, s, kv, idx, count, d, q_rows, max_out,
-                           rec, rows_per_block, static_cast<float*>(Kc), static_cast<float*>(Vc));
+                           rec, chunks, units, static_cast<float*>(Kc), static_cast<float*>(Vc));
     return static_cast<int>(hipGetLastError());
 }
 
