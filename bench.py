@@ -683,11 +683,12 @@ def kernel_sources_digest() -> str:
 # for sliced rows, the merge (which also combines a split attention) and the counter kernels; where the
 # two halves are not fused it is the speculation's kernels and the attention's
 CALL_KERNELS = {
-    "ig_decode_layer": ("void ig::k_decode_layer<", "void ig::k_spec_merge<", "ig::k_touch_bits",
-                        "ig::k_touch_finish"),
-    "ig_decode_layer/unfused": ("void ig::k_speculate<", "void ig::k_spec_merge<", "ig::k_touch_bits",
-                                "ig::k_touch_finish", "void ig::k_attn_split<", "ig::k_attn_combine"),
-    "ig_speculate": ("void ig::k_speculate<", "void ig::k_spec_merge<", "ig::k_touch_bits", "ig::k_touch_finish"),
+    "ig_decode_layer": ("void ig::k_decode_layer<", "void ig::k_spec_merge<", "ig::k_touch_bits(",
+                        "ig::k_touch_finish("),
+    "ig_decode_layer/unfused": ("void ig::k_speculate<", "void ig::k_spec_merge<", "ig::k_touch_bits(",
+                                "ig::k_touch_finish(", "void ig::k_attn_split<", "ig::k_attn_combine("),
+    "ig_speculate": ("void ig::k_speculate<", "void ig::k_spec_merge<", "ig::k_touch_bits(",
+                     "ig::k_touch_finish("),
 }
 
 

@@ -229,9 +229,9 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * offset 0, see ig_workspace_status) and the shape stamp (uint64 at offset 8),
  * then one uint32 arrival word per sequence ([B] at offset 256) and the
  * projection's split partial sums, then the slices' candidates (when there
- * are slices) and the counter kernels' bitmaps and per-sequence records; it
+ * are slices) and the counter kernels' bitmaps and per-sequence flags; it
  * must have been zero-filled once with ig_workspace_init, and every call
- * returns the arrival words, the partial-sum slots and those records to zero.  The first call after the zero-fill stamps
+ * returns the arrival words, the partial-sum slots and those flags to zero.  The first call after the zero-fill stamps
  * the workspace with its (B, H, D, r) (the places of those regions depend on
  * them; n, max_out and the mode may change from call to call); a call of
  * another (B, H, D, r) sets IG_WS_SHAPE instead of running: run

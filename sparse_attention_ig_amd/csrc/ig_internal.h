@@ -96,15 +96,8 @@ int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n,
                  int n_cap, int max_out, uint32_t cmax, int32_t* victim, void* ws, hipStream_t s);
 size_t touch_ws_bytes(int B);
-// Scratch of the bitmap counter kernels (in the speculation workspace): one saturation flag per sequence
-// [B] (zero between calls), then for every workgroup of 256 slots [B][ceil(n / 256)] the smallest
-// (counter << 32 | slot) over its slots, as is and clamped-and-halved (rewritten by every call).
-struct TouchMin {
-    unsigned long long raw, half;
-};
-size_t touch_bits_ws_bytes(int B, int n);
 int launch_touch_bits(uint32_t* counters, const uint32_t* bits, int B, int H, int n, int n_cap, uint32_t cmax,
-                      void* ws, int32_t* victim, hipStream_t s);
+                      uint32_t* flags, int32_t* victim, hipStream_t s);
 bool touch_single_kernel(int H, int max_out);
 int launch_speculate(const void* x, const void* Wq_part, const float* bq_part, const void* Kp, int B, int D, int H,
                      int r, int n, int n_cap, int dtype, float scale, int mode, float alpha, int k, int max_sel,

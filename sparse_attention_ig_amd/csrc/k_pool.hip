@@ -101,118 +101,46 @@ __global__ __launch_bounds__(kTouchThreads) void k_touch_finish(uint32_t* __rest
 }
 
 // Counters from the heads' selection bitmaps [B*H][ceil(n / 32)]: a workgroup owns 256 consecutive slots
-// of sequence b (8 bitmap words per head).  It stages those words of every head in LDS (coalesced loads,
-// its slots' counters read with them), then the thread of slot j adds the number of heads whose bit j is
-// set to its counter (each slot has one owner: no atomics; the counters are read and written coalesced).
-// For the finish it leaves its slots' smallest (counter, slot) pairs, as is and halved, in its own
-// record, and flags its sequence when a slot saturated.
+// of sequence b (8 bitmap words per head).  It stages those words of every head in LDS (coalesced loads),
+// then the thread of slot j adds the number of heads whose bit j is set to its counter (each slot has one
+// owner: no atomics; the counters are read and written coalesced); a workgroup that saturated a slot
+// flags its sequence for the finish.
 constexpr int kBitsHeadsMax = 128;
-constexpr int kBitsThreads = 256;
-
-size_t touch_bits_ws_bytes(int B, int n) {
-    const size_t nblk = (static_cast<size_t>(n) + kBitsThreads - 1) / kBitsThreads;
-    return (static_cast<size_t>(B) * sizeof(uint32_t) + 255) / 256 * 256 + static_cast<size_t>(B) * nblk * sizeof(TouchMin);
-}
-
-__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const unsigned long long o = __shfl_xor(v, m, kWave);
-        v = o < v ? o : v;
-    }
-    return v;
-}
-
-__global__ __launch_bounds__(kBitsThreads) void k_touch_bits(uint32_t* __restrict__ C, const uint32_t* __restrict__ bits,
-                                                            int H, int n, int n_cap, uint32_t cmax,
-                                                            uint32_t* __restrict__ flags, TouchMin* __restrict__ mins) {
+__global__ __launch_bounds__(256) void k_touch_bits(uint32_t* __restrict__ C, const uint32_t* __restrict__ bits,
+                                                   int H, int n, int n_cap, uint32_t cmax,
+                                                   uint32_t* __restrict__ flags) {
     __shared__ uint32_t s_w[kBitsHeadsMax * 8];
-    __shared__ unsigned long long s_min[2][kBitsThreads / kWave];
     const int b = blockIdx.y, tid = threadIdx.x;
     const int nw = (n + 31) / 32;
     const int w0 = blockIdx.x * 8;
-    const int j = blockIdx.x * kBitsThreads + tid;
-    uint32_t* c = C + static_cast<size_t>(b) * n_cap + j;
-    const uint32_t old = j < n ? *c : 0u;
-    for (int e = tid; e < H * 8; e += kBitsThreads) {
+    for (int e = tid; e < H * 8; e += 256) {
         const int h = e / 8, w = w0 + e % 8;
         s_w[e] = w < nw ? bits[(static_cast<size_t>(b) * H + h) * nw + w] : 0u;
     }
     __syncthreads();
+    const int j = blockIdx.x * 256 + tid;
     int sat = 0;
-    unsigned long long raw = ~0ull, half = ~0ull;
     if (j < n) {
         uint32_t inc = 0;
         const uint32_t* col = s_w + tid / 32;
         for (int h = 0; h < H; ++h) inc += (col[h * 8] >> (tid & 31)) & 1u;
-        uint32_t v = old;
         if (inc) {
-            v = old + inc;
+            uint32_t* c = C + static_cast<size_t>(b) * n_cap + j;
+            const uint32_t v = *c + inc;
             *c = v;
             sat = v >= cmax ? 1 : 0;
         }
-        raw = (static_cast<unsigned long long>(v) << 32) | static_cast<uint32_t>(j);
-        half = (static_cast<unsigned long long>((v < cmax ? v : cmax) >> 1) << 32) | static_cast<uint32_t>(j);
     }
-    raw = wave_min_u64(raw);
-    half = wave_min_u64(half);
-    const int lane = tid % kWave, wave = tid / kWave;
-    if (lane == 0) {
-        s_min[0][wave] = raw;
-        s_min[1][wave] = half;
-    }
-    sat = __syncthreads_or(sat);
-    if (tid == 0) {
-#pragma unroll
-        for (int w = 1; w < kBitsThreads / kWave; ++w) {
-            raw = s_min[0][w] < raw ? s_min[0][w] : raw;
-            half = s_min[1][w] < half ? s_min[1][w] : half;
-        }
-        mins[static_cast<size_t>(b) * gridDim.x + blockIdx.x] = TouchMin{raw, half};
-        if (sat) atomicOr(&flags[b], 1u);
-    }
-}
-
-// Per-sequence finish of the bitmap counters: halve if flagged (the flag returns to zero); the victim is
-// the smallest of the workgroups' pairs (the halved ones after a halving).
-__global__ __launch_bounds__(kTouchThreads) void k_touch_bits_finish(uint32_t* __restrict__ C, int n, int n_cap,
-                                                                    uint32_t cmax, uint32_t* __restrict__ flags,
-                                                                    const TouchMin* __restrict__ mins, int nblk,
-                                                                    int32_t* __restrict__ victim) {
-    __shared__ unsigned long long s_min[kTouchThreads / kWave];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const bool halve = flags[b] != 0u;
-    unsigned long long best = ~0ull;
-    if (victim) {
-        for (int i = tid; i < nblk; i += kTouchThreads) {
-            const TouchMin& t = mins[static_cast<size_t>(b) * nblk + i];
-            const unsigned long long v = halve ? t.half : t.raw;
-            best = v < best ? v : best;
-        }
-    }
-    if (halve) pool_finish<kTouchThreads>(C + static_cast<size_t>(b) * n_cap, n, cmax, true, false, nullptr, nullptr);
-    best = wave_min_u64(best);
-    if (tid % kWave == 0) s_min[tid / kWave] = best;
-    __syncthreads();  // (also: every thread has read the flag)
-    if (tid == 0) {
-        for (int w = 1; w < kTouchThreads / kWave; ++w) best = s_min[w] < best ? s_min[w] : best;
-        if (victim) victim[b] = static_cast<int32_t>(static_cast<uint32_t>(best));
-        flags[b] = 0u;
-    }
+    if (__syncthreads_or(sat) && tid == 0) atomicOr(&flags[b], 1u);
 }
 
 int launch_touch_bits(uint32_t* counters, const uint32_t* bits, int B, int H, int n, int n_cap, uint32_t cmax,
-                      void* ws, int32_t* victim, hipStream_t s) {
-    const int nblk = (n + kBitsThreads - 1) / kBitsThreads;
-    uint32_t* flags = static_cast<uint32_t*>(ws);
-    TouchMin* mins = reinterpret_cast<TouchMin*>(static_cast<char*>(ws) +
-                                                 (static_cast<size_t>(B) * sizeof(uint32_t) + 255) / 256 * 256);
-    hipLaunchKernelGGL(k_touch_bits, dim3(nblk, B), dim3(kBitsThreads), 0, s, counters, bits, H, n, n_cap, cmax, flags,
-                       mins);
+                      uint32_t* flags, int32_t* victim, hipStream_t s) {
+    hipLaunchKernelGGL(k_touch_bits, dim3((n + 255) / 256, B), dim3(256), 0, s, counters, bits, H, n, n_cap, cmax,
+                       flags);
     const int e = static_cast<int>(hipGetLastError());
     if (e) return e;
-    hipLaunchKernelGGL(k_touch_bits_finish, dim3(B), dim3(kTouchThreads), 0, s, counters, n, n_cap, cmax, flags, mins,
-                       nblk, victim);
+    hipLaunchKernelGGL(k_touch_finish, dim3(B), dim3(kTouchThreads), 0, s, counters, n, n_cap, cmax, flags, victim);
     return static_cast<int>(hipGetLastError());
 }
 

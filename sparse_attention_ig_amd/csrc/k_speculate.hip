@@ -134,7 +134,7 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     const size_t nw = (static_cast<size_t>(n) + 31) / 32;
     sp.off_bits = sp.off_idx + (sliced ? align256(cands * sizeof(int32_t)) : 0);
     sp.off_flags = sp.off_bits + (any_bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
-    sp.off_hcount = sp.off_flags + (any_bits ? align256(touch_bits_ws_bytes(B, n)) : 0);
+    sp.off_hcount = sp.off_flags + (any_bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
     sp.ws_bytes = sp.off_hcount + (ha.ok ? align256(static_cast<size_t>(rows) * sizeof(int32_t)) : 0);
     return sp;
 }
@@ -281,7 +281,7 @@ int finish_speculate(const SpecParams& p, int dtype, void* ws, hipStream_t s, co
     if (e || !p.bits) return e;
     const SpecPlan sp = plan_speculate(p.B, p.H, p.D, p.r, p.n, p.max_out, dtype, p.mode);
     return launch_touch_bits(p.counters, p.bits, p.B, p.H, p.n, p.n_cap, p.cmax,
-                             static_cast<char*>(ws) + sp.off_flags, p.victim, s);
+                             reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), p.victim, s);
 }
 
 // ------------------------------------------------------------------ ig_speculate_noalloc
