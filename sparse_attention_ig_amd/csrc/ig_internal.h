@@ -91,6 +91,7 @@ int launch_select(const float* scores, int B, int H, int n, int ld, int mode, fl
 int launch_attn(const void* q, const void* K, const void* V, int ld_rows, const int32_t* idx,
                 const int32_t* count, int B, int H, int d, int max_out, int dtype, float scale,
                 float* out, float* lse, void* ws, hipStream_t s);
+bool host_resident(const void* p);  // host memory (pinned, device-mapped), or a pointer the runtime does not know
 int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_t* count, int B, int H,
                   int d, int n_cap, int max_out, int dtype, void* Kc, void* Vc, hipStream_t s);
 int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, int B, int H, int n,

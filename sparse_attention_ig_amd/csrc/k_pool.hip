@@ -167,12 +167,24 @@ int launch_touch(uint32_t* counters, const int32_t* idx, const int32_t* count, i
 }
 
 // rows of RB bytes (RB % 16 == 0), LPR = RB / 16 lanes per row.  The work is cut into units of
-// kGatherRows rows of one (b, h); a grid of at most kGatherMaxWgs workgroups walks the units (workgroup w
-// takes units w, w + gridDim.x, ..), so that a gather over the host link, which needs only enough reads
-// in flight to cover the link's latency, leaves most of the GPU to kernels on other streams.  Every
-// lane issues the loads of all its rows of a unit before any store.
+// kGatherRows rows of one (b, h); the workgroups walk the units (workgroup w takes units w, w + gridDim.x,
+// ..).  A gather from host memory runs at most kGatherHostWgs workgroups: the host link needs only enough
+// reads in flight to cover its latency, and the rest of the GPU stays free for kernels on other streams
+// (a flood of slow host reads holds them back); a gather from device memory runs one workgroup per unit.
+// Every lane issues the loads of all its rows of a unit before any store.
 constexpr int kGatherRows = 64;
-constexpr int kGatherMaxWgs = 128;
+constexpr int kGatherHostWgs = 128;
+
+// Whether p points to host memory (pinned, mapped into the device's address space); pointers the runtime
+// does not know count as host memory.
+bool host_resident(const void* p) {
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();  // (not a launch error)
+        return true;
+    }
+    return a.type != hipMemoryTypeDevice;
+}
 __global__ __launch_bounds__(kGatherThreads) void k_gather(const char* __restrict__ K, const char* __restrict__ V,
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ count, int row_bytes,
@@ -224,7 +236,7 @@ int launch_gather(const void* K, const void* V, const int32_t* idx, const int32_
     const int row_bytes = d * (dtype == IG_BF16 ? 2 : 4);
     const int chunks = (max_out + kGatherRows - 1) / kGatherRows;
     const int64_t units = static_cast<int64_t>(chunks) * B * H;
-    const int grid = static_cast<int>(std::min<int64_t>(units, kGatherMaxWgs));
+    const int grid = static_cast<int>(std::min<int64_t>(units, host_resident(K) ? kGatherHostWgs : (1 << 30)));
     hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kGatherThreads), 0, s, static_cast<const char*>(K),
                        static_cast<const char*>(V), idx, count, row_bytes, n_cap, max_out, chunks, units,
                        static_cast<char*>(Kc), static_cast<char*>(Vc));

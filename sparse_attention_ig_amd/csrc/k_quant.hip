@@ -126,11 +126,11 @@ __device__ __forceinline__ void dequant_group(const unsigned char* r, int d, int
 }
 
 // One thread per group of a selected row.  As in the row gather, the work is cut into units of
-// kGatherQ4Rows rows of one (b, h) and a grid of at most kGatherQ4MaxWgs workgroups walks them, so that
-// the host-link reads leave most of the GPU to kernels on other streams; each thread has two rows'
-// records in flight.
+// kGatherQ4Rows rows of one (b, h) that the workgroups walk, at most kGatherQ4HostWgs of them when the
+// records are in host memory (so that the host-link reads leave most of the GPU to kernels on other
+// streams), one per unit otherwise; each thread has two rows' records in flight.
 constexpr int kGatherQ4Rows = 64;
-constexpr int kGatherQ4MaxWgs = 128;
+constexpr int kGatherQ4HostWgs = 128;
 template <typename TO>
 __global__ __launch_bounds__(kQThreads) void k_gather_q4(const unsigned char* __restrict__ KVq,
                                                          const int32_t* __restrict__ idx,
@@ -184,7 +184,7 @@ int launch_gather_q4(const void* KVq, const int32_t* idx, const int32_t* count, 
                      int max_out, int dtype_out, void* Kc, void* Vc, hipStream_t s) {
     const int chunks = (max_out + kGatherQ4Rows - 1) / kGatherQ4Rows;
     const int64_t units = static_cast<int64_t>(chunks) * B * H;
-    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, kGatherQ4MaxWgs)));
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, host_resident(KVq) ? kGatherQ4HostWgs : (1 << 30))));
     const int rec = static_cast<int>(int4_record_bytes(d));
     const auto* kv = static_cast<const unsigned char*>(KVq);
     if (dtype_out == IG_BF16)
