@@ -63,7 +63,9 @@ const char* ig_last_error(void);
  * launch, whose split partial sums follow the sequences' arrival words in
  * the workspace; 9: ig_select takes a workspace for rows longer than 32768 keys;
  * 10: the speculation workspace starts with a status word and a shape stamp,
- * ig_workspace_status, ig_set_handover_test_mode). */
+ * ig_workspace_status, ig_set_handover_test_mode; 11: the bitmap counter
+ * kernels' flags follow the arrival words, at a place that does not depend on
+ * n). */
 int ig_version(void);
 
 /* ------------------------------------------------------------------ host, offline setup */
@@ -227,11 +229,12 @@ int ig_rehearse(const void* x, const void* Wq_part, const float* bq_part, const 
  * with slices, a merge launch follows.  The workspace (IG_OP_SPECULATE bytes,
  * required) starts with a 256-byte region holding the status word (uint32 at
  * offset 0, see ig_workspace_status) and the shape stamp (uint64 at offset 8),
- * then one uint32 arrival word per sequence ([B] at offset 256) and the
- * projection's split partial sums, then the slices' candidates (when there
- * are slices) and the counter kernels' bitmaps and per-sequence flags; it
- * must have been zero-filled once with ig_workspace_init, and every call
- * returns the arrival words, the partial-sum slots and those flags to zero.  The first call after the zero-fill stamps
+ * then two uint32 words per sequence at offset 256 (the rows' arrivals [B],
+ * then the bitmap counter kernels' saturation flags [B]) and the projection's
+ * split partial sums, then the slices' candidates (when there are slices)
+ * and the counter kernels' bitmaps; it must have been zero-filled once with
+ * ig_workspace_init, and every call returns the per-sequence words and the
+ * partial-sum slots to zero.  The first call after the zero-fill stamps
  * the workspace with its (B, H, D, r) (the places of those regions depend on
  * them; n, max_out and the mode may change from call to call); a call of
  * another (B, H, D, r) sets IG_WS_SHAPE instead of running: run

@@ -62,7 +62,7 @@ extern "C" {
 
 const char* ig_last_error(void) { return g_err; }
 
-int ig_version(void) { return 10; }
+int ig_version(void) { return 11; }
 
 int ig_skew_weights(const ig_skew_args* args) { return skew_weights(args); }
 

@@ -66,8 +66,8 @@ struct SpecPlan {
     bool tight;                       // top-k slices with tight candidates (the merge checks, or recomputes)
     bool headavg;                     // head average: whole rows hand on candidates, the merge averages
     bool ok;                          // false: rows too long for the candidates to fit one merge
-    size_t off_status, off_arrive, off_part, off_cnt, off_lo, off_q, off_key, off_idx, off_bits,
-        off_flags, off_hcount, ws_bytes;
+    size_t off_status, off_arrive, off_part, off_cnt, off_lo, off_q, off_key, off_idx, off_bits, off_hcount,
+        ws_bytes;
 };
 SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtype, int mode);
 size_t speculate_ws_bytes(int B, int H, int D, int r, int n, int max_out, int dtype);

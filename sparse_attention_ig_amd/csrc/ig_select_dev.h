@@ -253,9 +253,11 @@ struct __align__(16) FastSel {  // 16-byte aligned: the histograms are read 4 bi
     __device__ uint32_t* stage() { return words; }
 };
 
-// Clears histograms 0 and 1; a barrier must follow before radix_kth_lds.
+// Clears histograms 0 and 1 (the first NT threads of the block); a barrier must follow before
+// radix_kth_lds.
+template <int NT = kSelThreads>
 __device__ __forceinline__ void fast_sel_init(FastSel& fs) {
-    if (threadIdx.x < 512) fs.words[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < 512; i += NT) fs.words[i] = 0u;
 }
 
 // E consecutive keys of lk from j (j % E == 0, lk 16-byte aligned); positions at or past `end` read 0.
@@ -340,6 +342,7 @@ __device__ __forceinline__ void radix_hist(KS lk, int n, uint32_t* h, int shift,
 template <int NT = kSelThreads, class KS>
 __device__ __forceinline__ void radix_kth_keys(KS lk, int n, int kk, FastSel& fs, uint32_t* T_out, int* need_eq_out,
                                                int* eq_total_out, uint32_t base = 0u, uint32_t hi = ~0u) {
+    static_assert(NT >= 256, "a pass clears a 256-bin histogram with one thread per bin");
     const int tid = threadIdx.x, lane = tid % kWave;
     constexpr int E = KS::kE;
     const bool wide = n >= E * NT;
@@ -547,7 +550,7 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
     const bool want_hi = r_hi >= 1 && static_cast<double>(r_lo) * n / NT > 0.75 * band_cap;
     if (want_hi) {
         __syncthreads();  // every wave has read the last histogram before it is cleared
-        fast_sel_init(fs);
+        fast_sel_init<NT>(fs);
         __syncthreads();
         radix_kth_lds<NT>(sample, NT, r_hi, fs, &U, &ne, &et);
     }
@@ -580,11 +583,11 @@ __device__ bool sampled_kth(KS lk, int n, int kk, FastSel& fs, SelScratch& sh, u
     c_hi = block_sum<NT>(c_hi, sh);
     if (c_hi >= kk || c_hi + c_band < kk || c_band > band_cap) {  // uniform: block-wide counts
         // the sample's passes left counts in the histograms: the full radix starts from clean ones
-        fast_sel_init(fs);
+        fast_sel_init<NT>(fs);
         __syncthreads();
         return false;
     }
-    fast_sel_init(fs);  // fresh histograms for the band select
+    fast_sel_init<NT>(fs);  // fresh histograms for the band select
     __syncthreads();
     uint32_t T;
     radix_kth_lds<NT>(cand, c_band, kk - c_hi, fs, &T, need_eq_out, eq_total_out);

@@ -43,6 +43,7 @@
 namespace ig {
 
 constexpr int kSpecThreads = 1024;
+constexpr int kRowSelThreads = 512;  // threads that select a whole row once its keys are in LDS
 constexpr int kSpecBatch = 8;  // default partial-key rows per lane per batch
 
 struct SpecParams {
@@ -302,6 +303,7 @@ __device__ __forceinline__ void spec_bh(const SpecParams& p, int row_wg, int* b,
     }
 }
 
+template <int NT = kSpecThreads>
 __device__ __forceinline__ void seq_arrive(const SpecParams& p, int b, bool sat, uint32_t* lds, SelScratch& sh,
                                            int& s_last);
 
@@ -338,10 +340,10 @@ __device__ __forceinline__ int tight_slice_k(int kk_row, int rows, int n, int ca
 
 // The exact cut of the top kk of ks[0..m) (fast_sel_init and a barrier before): the sampled bracket
 // pays off on long rows; below kSampledMin keys the radix over every key is faster.
-template <class KS>
+template <int NT = kSpecThreads, class KS>
 __device__ __forceinline__ void exact_cut(KS keys, int m, int kk, FastSel& fs, SelScratch& sh, SelCut& c) {
-    if (m < kSampledMin || !sampled_kth(keys, m, kk, fs, sh, &c.kth, &c.need_eq, &c.eq_total))
-        radix_kth_keys(keys, m, kk, fs, &c.kth, &c.need_eq, &c.eq_total);
+    if (m < kSampledMin || !sampled_kth<NT>(keys, m, kk, fs, sh, &c.kth, &c.need_eq, &c.eq_total))
+        radix_kth_keys<NT>(keys, m, kk, fs, &c.kth, &c.need_eq, &c.eq_total);
 }
 
 // The cut of the selection over the keys ks[0..m) (held in LDS, a merge's candidates in global memory,
@@ -350,7 +352,7 @@ __device__ __forceinline__ void exact_cut(KS keys, int m, int kk, FastSel& fs, S
 // selection of at most cand_cap keys -- every key at or above a sampled lower bound of the slice's cut,
 // to be checked by the compaction (win_lo); with tight top-k candidates, of the slice's share of the
 // row's budget.
-template <bool TO_CANDS, class KS>
+template <bool TO_CANDS, int NT = kSpecThreads, class KS>
 __device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, int m, int rows, uint32_t kmax_all,
                                            KS keys, SelScratch& sh, FastSel& fs) {
     int limit = min(rows, p.max_out);
@@ -362,7 +364,7 @@ __device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, i
             // a whole row of a head-average call: its threshold count for the sequence's average, and as
             // candidates every key an averaged count could take, the row's top min(n, max_out, max_sel)
             const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
-            const int cnt = count_ge<kSpecThreads>(keys, m, kc, sh);
+            const int cnt = count_ge<NT>(keys, m, kc, sh);
             if (threadIdx.x == 0) p.hcount[bh] = cnt;
             kk = p.max_sel > 0 ? min(limit, p.max_sel) : limit;
         } else {
@@ -380,7 +382,7 @@ __device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, i
         }
     } else if (p.mode == IG_SEL_THRESHOLD) {
         const uint32_t kc = score_key(key_score(kmax_all) - p.alpha);
-        const int cnt = count_ge<kSpecThreads>(keys, m, kc, sh);
+        const int cnt = count_ge<NT>(keys, m, kc, sh);
         if (p.max_sel > 0) limit = min(limit, p.max_sel);
         if (cnt <= limit) {
             c.kth = kc;
@@ -396,12 +398,12 @@ __device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, i
     }
     c.kk = kk;
     if constexpr (TO_CANDS) {
-        if (!done && p.cand_cap > kk + kk / 8 && sampled_bound(keys, m, kk, p.cand_cap, fs, &c.kth)) {
+        if (!done && p.cand_cap > kk + kk / 8 && sampled_bound<NT>(keys, m, kk, p.cand_cap, fs, &c.kth)) {
             c.win_lo = kk;  // every key >= the bound, when there are kk to cand_cap of them
             return c;
         }
     }
-    if (!done) exact_cut(keys, m, kk, fs, sh, c);
+    if (!done) exact_cut<NT>(keys, m, kk, fs, sh, c);
     return c;
 }
 
@@ -413,7 +415,7 @@ __device__ __forceinline__ SelCut spec_cut(const SpecParams& p, int b, int bh, i
 // its window.  Otherwise write idx / count and update the counters (one integer atomic per selected
 // slot, all in flight together; the last workgroup of sequence b halves if any slot saturated and picks
 // the victim).
-template <bool TO_CANDS, class KS, typename GIdx>
+template <bool TO_CANDS, int NT = kSpecThreads, class KS, typename GIdx>
 __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, int slice, int m, const SelCut& c,
                                           KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs, int& s_last,
                                           GIdx gidx) {
@@ -438,20 +440,20 @@ __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, in
                 ci[pos] = gidx(j);
             }
         };
-        const int got = compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put, c.win_lo,
+        const int got = compact_keys<NT>(keys, m, kth, need_eq, eq_total, nullptr, p.cand_cap, fs, put, c.win_lo,
                                      c.win_lo > 0 ? p.cand_cap : INT_MAX);
         if (got < 0) return false;
         const int written = min(got, p.cand_cap);
         if (staged) {
             __syncthreads();
-            for (int i = tid; i < written; i += kSpecThreads) {
+            for (int i = tid; i < written; i += NT) {
                 ck[i] = sk[i];
                 ci[i] = si[i];
             }
         }
         // (a merge reads the candidate arrays whole only when they exceed its LDS)
         if (static_cast<int64_t>(p.slices) * p.cand_cap > kSpecMaxRows)
-            for (int i = written + tid; i < p.cand_cap; i += kSpecThreads) ck[i] = 0u;
+            for (int i = written + tid; i < p.cand_cap; i += NT) ck[i] = 0u;
         if (tid == 0) {
             p.cand_cnt[static_cast<size_t>(bh) * p.slices + slice] = written;
             // every key above kth was handed on, and every key equal to it unless only some of the ties
@@ -476,26 +478,26 @@ __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, in
                 else
                     out[pos] = g;
             };
-            written = compact_keys(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
+            written = compact_keys<NT>(keys, m, kth, need_eq, eq_total, nullptr, p.max_out, fs, keep);
             __syncthreads();
             const int ws = min(min(written, p.max_out), kFastStage);
-            for (int i = tid; i < ws; i += kSpecThreads) out[i] = static_cast<int32_t>(stage[i]);
+            for (int i = tid; i < ws; i += NT) out[i] = static_cast<int32_t>(stage[i]);
         } else {
             // key positions first, then every position mapped to its row index with batched loads
-            written = compact_keys(keys, m, kth, need_eq, eq_total, out, p.max_out, fs, NoVisit());
+            written = compact_keys<NT>(keys, m, kth, need_eq, eq_total, out, p.max_out, fs, NoVisit());
             __syncthreads();
             const int w = min(written, p.max_out);
             constexpr int U = 8;
-            for (int i0 = tid; i0 < w; i0 += kSpecThreads * U) {
+            for (int i0 = tid; i0 < w; i0 += NT * U) {
                 int pos[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) pos[u] = i0 + u * kSpecThreads < w ? out[i0 + u * kSpecThreads] : 0;
+                for (int u = 0; u < U; ++u) pos[u] = i0 + u * NT < w ? out[i0 + u * NT] : 0;
                 int g[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) g[u] = i0 + u * kSpecThreads < w ? gidx(pos[u]) : 0;
+                for (int u = 0; u < U; ++u) g[u] = i0 + u * NT < w ? gidx(pos[u]) : 0;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int i = i0 + u * kSpecThreads;
+                    const int i = i0 + u * NT;
                     if (i < w) {
                         out[i] = g[u];
                         if (i < kFastStage) stage[i] = static_cast<uint32_t>(g[u]);
@@ -510,15 +512,15 @@ __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, in
             // the row's selection as a bitmap of its n slots, built in LDS and written out whole
             const int nw = (n + 31) / 32;
             const int w = min(written, p.max_out);
-            for (int i = tid; i < nw; i += kSpecThreads) lds[i] = 0u;
+            for (int i = tid; i < nw; i += NT) lds[i] = 0u;
             __syncthreads();
-            for (int i = tid; i < w; i += kSpecThreads) {
+            for (int i = tid; i < w; i += NT) {
                 const uint32_t j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
                 if (j < static_cast<uint32_t>(n)) atomicOr(&lds[j >> 5], 1u << (j & 31u));
             }
             __syncthreads();
             uint32_t* dst = p.bits + static_cast<size_t>(bh) * nw;
-            for (int i = tid; i < nw; i += kSpecThreads) dst[i] = lds[i];
+            for (int i = tid; i < nw; i += NT) dst[i] = lds[i];
             return true;
         }
         int sat = 0;
@@ -527,48 +529,48 @@ __device__ __forceinline__ bool spec_emit(const SpecParams& p, int b, int bh, in
         // at most one atomic per lane when the selection is small, else 8 per lane in flight at a time,
         // their returns checked afterwards
         const int touched = min(written, p.max_out);
-        if (touched <= kSpecThreads) {
+        if (touched <= NT) {
             if (tid < touched) {
                 const uint32_t j = tid < kFastStage ? stage[tid] : static_cast<uint32_t>(out[tid]);
                 if (j < static_cast<uint32_t>(n) && atomicAdd(&crow[j], 1u) + 1u >= cmax) sat = 1;
             }
         } else {
         constexpr int U = 8;
-        for (int i0 = tid; i0 < touched; i0 += kSpecThreads * U) {
+        for (int i0 = tid; i0 < touched; i0 += NT * U) {
             uint32_t old[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * kSpecThreads;
+                const int i = i0 + u * NT;
                 uint32_t j = 0xFFFFFFFFu;
                 if (i < touched) j = i < kFastStage ? stage[i] : static_cast<uint32_t>(out[i]);
                 old[u] = j < static_cast<uint32_t>(n) ? atomicAdd(&crow[j], 1u) : 0u;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * kSpecThreads;
+                const int i = i0 + u * NT;
                 if (i < touched && old[u] + 1u >= cmax) sat = 1;
             }
         }
         }
-        seq_arrive(p, b, __syncthreads_or(sat) != 0, lds, sh, s_last);
+        seq_arrive<NT>(p, b, __syncthreads_or(sat) != 0, lds, sh, s_last);
         return true;
     }
 }
 
 // Selection over ks[0..m) and its results (spec_cut, then spec_emit).
-template <bool TO_CANDS, class KS, typename GIdx>
+template <bool TO_CANDS, int NT = kSpecThreads, class KS, typename GIdx>
 __device__ __forceinline__ void spec_select(const SpecParams& p, int b, int bh, int slice, int m, int rows,
                                             uint32_t kmax_all, KS keys, uint32_t* lds, SelScratch& sh, FastSel& fs,
                                             int& s_last, GIdx gidx) {
-    const SelCut c = spec_cut<TO_CANDS>(p, b, bh, m, rows, kmax_all, keys, sh, fs);
-    if (spec_emit<TO_CANDS>(p, b, bh, slice, m, c, keys, lds, sh, fs, s_last, gidx)) return;
+    const SelCut c = spec_cut<TO_CANDS, NT>(p, b, bh, m, rows, kmax_all, keys, sh, fs);
+    if (spec_emit<TO_CANDS, NT>(p, b, bh, slice, m, c, keys, lds, sh, fs, s_last, gidx)) return;
     // a sampled bound whose superset held too few or too many keys: the exact cut of the slice's kk
     __syncthreads();  // every wave is done with the sample's histograms
-    fast_sel_init(fs);
+    fast_sel_init<NT>(fs);
     __syncthreads();
     SelCut e{0u, INT_MAX, INT_MAX, c.kk, 0};
-    exact_cut(keys, m, c.kk, fs, sh, e);
-    spec_emit<TO_CANDS>(p, b, bh, slice, m, e, keys, lds, sh, fs, s_last, gidx);
+    exact_cut<NT>(keys, m, c.kk, fs, sh, e);
+    spec_emit<TO_CANDS, NT>(p, b, bh, slice, m, e, keys, lds, sh, fs, s_last, gidx);
 }
 
 // Score keys of a whole row recomputed from its partial keys (the exact fallback of a merge whose tight
@@ -616,6 +618,7 @@ struct RowKeys {
 // XCD's whole L2) is needed.  One word per sequence carries the arrivals (high half) and the workgroups
 // that saw a saturation (low half); the last of the H rows halves the sequence's counters if any row
 // saturated, picks the victim and returns the word to zero.
+template <int NT>
 __device__ __forceinline__ void seq_arrive(const SpecParams& p, int b, bool sat, uint32_t* lds, SelScratch& sh,
                                            int& s_last) {
     const int tid = threadIdx.x;
@@ -628,7 +631,7 @@ __device__ __forceinline__ void seq_arrive(const SpecParams& p, int b, bool sat,
     if (!s_last) return;
     const bool halve = s_last == 2;
     uint32_t* crow = p.counters + static_cast<size_t>(b) * p.n_cap;
-    const int v = pool_finish<kSpecThreads>(crow, p.n, p.cmax, halve, p.victim != nullptr, lds, &sh.wtot[0]);
+    const int v = pool_finish<NT>(crow, p.n, p.cmax, halve, p.victim != nullptr, lds, &sh.wtot[0]);
     if (tid == 0) {
         if (p.victim) p.victim[b] = v;
         __hip_atomic_store(&p.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -748,11 +751,19 @@ __device__ __forceinline__ void spec_row(const SpecParams& p, int wg, uint32_t* 
 
     // 3. selection (and, for a whole row, counters; a slice, or a row of a head-average call, hands on
     // candidates to the merge instead)
-    if (p.slices > 1 || p.mode == IG_SEL_HEADAVG)
+    if (p.slices > 1 || p.mode == IG_SEL_HEADAVG) {
         spec_select<true>(p, b, bh, slice, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last,
                           [&](int j) { return r0 + j; });
-    else
-        spec_select<false>(p, b, bh, 0, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last, IdentityIdx());
+        return;
+    }
+    // A whole row is selected by its first kRowSelThreads threads; the other waves end here (a barrier
+    // waits only for the waves still running).  Every wave that takes part repeats the radix digit
+    // search and the compaction's scans, which cost issue slots on SIMDs shared with the workgroup
+    // beside it: eight waves finish sooner than sixteen (measured at 2048 keys); four expose too much
+    // LDS latency and are slower.
+    if (__builtin_amdgcn_readfirstlane(tid / kWave) >= kRowSelThreads / kWave) return;  // wave-uniform
+    spec_select<false, kRowSelThreads>(p, b, bh, 0, n, n, kmax_all, LdsKeys{keys}, keys, sh, fs, sm.last,
+                                       IdentityIdx());
 }
 
 // The partial-sum slots of row (b, h): every slice of the row read them in the launch before, so the

@@ -117,8 +117,10 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     sp.splits = (D + kProjSplit - 1) / kProjSplit;
     sp.proj_wgs = sp.proj_blocks * sp.splits;
     sp.off_status = 0;  // status word at 0, shape stamp at 8 (one 256-byte region)
+    // the rows' arrival words [B], then the bitmap counter kernels' per-sequence saturation flags [B]: both
+    // must be zero on entry, so they sit where no other region reaches whatever n is
     sp.off_arrive = 256;
-    sp.off_part = sp.off_arrive + align256(static_cast<size_t>(B) * sizeof(uint32_t));
+    sp.off_part = sp.off_arrive + align256(2 * static_cast<size_t>(B) * sizeof(uint32_t));
     sp.off_cnt = sp.off_part + align256(static_cast<size_t>(sp.splits) * B * H * r * sizeof(float));
     const bool sliced = s_max > 1 || ha.ok;  // (candidate regions: slices, or head-average rows)
     sp.off_lo = sp.off_cnt + (sliced ? align256(static_cast<size_t>(rows) * s_max * sizeof(int32_t)) : 0);
@@ -133,8 +135,7 @@ SpecPlan plan_speculate(int B, int H, int D, int r, int n, int max_out, int dtyp
     const bool any_bits = uses_bits(thr) || uses_bits(tk);
     const size_t nw = (static_cast<size_t>(n) + 31) / 32;
     sp.off_bits = sp.off_idx + (sliced ? align256(cands * sizeof(int32_t)) : 0);
-    sp.off_flags = sp.off_bits + (any_bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
-    sp.off_hcount = sp.off_flags + (any_bits ? align256(static_cast<size_t>(B) * sizeof(uint32_t)) : 0);
+    sp.off_hcount = sp.off_bits + (any_bits ? align256(static_cast<size_t>(rows) * nw * sizeof(uint32_t)) : 0);
     sp.ws_bytes = sp.off_hcount + (ha.ok ? align256(static_cast<size_t>(rows) * sizeof(int32_t)) : 0);
     return sp;
 }
@@ -281,7 +282,7 @@ int finish_speculate(const SpecParams& p, int dtype, void* ws, hipStream_t s, co
     if (e || !p.bits) return e;
     const SpecPlan sp = plan_speculate(p.B, p.H, p.D, p.r, p.n, p.max_out, dtype, p.mode);
     return launch_touch_bits(p.counters, p.bits, p.B, p.H, p.n, p.n_cap, p.cmax,
-                             reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags), p.victim, s);
+                             reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_arrive) + p.B, p.victim, s);
 }
 
 // ------------------------------------------------------------------ ig_speculate_noalloc
@@ -314,13 +315,10 @@ static int noalloc_scratch(void** out) {
 }
 
 // Start of a no-allocation call: every word of [0, words) to zero except the shape stamp (words 2-3),
-// which gets this call's key, and the counter kernels' per-sequence flags (flag_words words, when the
-// call has them).
-__global__ void k_scratch_reset(uint32_t* ws, size_t words, unsigned long long key, uint32_t* flags,
-                                size_t flag_words) {
+// which gets this call's key.
+__global__ void k_scratch_reset(uint32_t* ws, size_t words, unsigned long long key) {
     const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < words) ws[i] = i == 2 ? static_cast<uint32_t>(key) : i == 3 ? static_cast<uint32_t>(key >> 32) : 0u;
-    if (flags && i < flag_words) flags[i] = 0u;
 }
 
 int launch_speculate_noalloc(const SpecCall& c, hipStream_t s) {
@@ -329,16 +327,12 @@ int launch_speculate_noalloc(const SpecCall& c, hipStream_t s) {
     void* ws = nullptr;
     int e = noalloc_scratch(&ws);
     if (e) return e;
-    // the status word, the stamp, the arrival words, the slices' per-row counts and the partial-sum slots
-    // come first (off_cnt is where the candidates start); the candidates and bitmaps are written before
-    // they are read in every call
+    // the status word, the stamp, the arrival words and flags and the partial-sum slots come first
+    // (off_cnt is where the candidates start); the candidates and bitmaps are written before they are
+    // read in every call
     const size_t words = sp.off_cnt / sizeof(uint32_t);
-    uint32_t* flags = sp.bits && c.counters ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sp.off_flags)
-                                            : nullptr;
-    const size_t flag_words = static_cast<size_t>(c.B);  // the counter kernels' saturation flags
-    const size_t span = std::max(words, flag_words);
-    hipLaunchKernelGGL(k_scratch_reset, dim3(static_cast<unsigned>((span + 255) / 256)), dim3(256), 0, s,
-                       static_cast<uint32_t*>(ws), words, spec_shape_key(c.B, c.H, c.D, c.r), flags, flag_words);
+    hipLaunchKernelGGL(k_scratch_reset, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ws), words, spec_shape_key(c.B, c.H, c.D, c.r));
     if ((e = static_cast<int>(hipGetLastError()))) return e;
     return launch_speculate(c.x, c.Wq_part, c.bq_part, c.Kp, c.B, c.D, c.H, c.r, c.n, c.n_cap, c.dtype, c.scale,
                             c.mode, c.alpha, c.k, c.max_sel, c.idx, c.count, c.max_out, c.counters, c.cmax, c.victim,

@@ -100,7 +100,7 @@ def check_step(name, spec, mode, kw, lib_in=None, ora_in=None, path="unfused"):
     if path == "fused":
         # the arrival words (B words from byte 256 of the workspace) are back to zero, the status is clear
         from sparse_attention_ig_amd import _lib as L
-        assert not host(layer.ws_spec)[256:256 + 4 * spec.B].any(), "arrival words must return to zero"
+        assert not host(layer.ws_spec)[256:256 + 8 * spec.B].any(), "per-sequence words must return to zero"
         assert L.ig_workspace_status(layer.ws_spec) == 0
     say(f"[case {name}] gpu step done")
     ref = harness.oracle_step(ora_in, mode=mode, alpha=alpha, k=k, max_sel=max_sel, max_out=max_out, cmax=cmax,

@@ -102,3 +102,28 @@ def test_sliced_rows_changing_n_and_mode(lib):
             say(f"[shared workspace] sliced rows, call {i} {kw}")
             _same(_run(layer, kw, shared), ref[i], f"sliced call {i} rep {rep}")
             assert lib.ig_workspace_status(shared) == 0
+
+
+def test_bitmap_counters_changing_n(lib):
+    """Sliced rows whose selections are large enough for the bitmap counter kernels (32 rows x 8192
+    selected slots), with n changing from call to call on one workspace: the kernels' per-sequence
+    saturation flags must start every call at zero, so they sit at a place that does not move with n
+    (the bitmaps and candidates that do move hold nonzero words after a call)."""
+    import torch
+    from sparse_attention_ig_amd.runtime import DeviceLayer, prepare_layer
+    spec = _spec(gen.llama2_7b_long(n=16384), topk=8192)
+    layer = DeviceLayer(prepare_layer(spec), max_out=8192)
+    calls = [dict(mode="topk", k=8192, max_out=8192),
+             dict(mode="topk", k=8192, max_out=8192, n=12000),
+             dict(mode="topk", k=6000, max_out=8192, n=14000),
+             dict(mode="topk", k=8192, max_out=8192)]
+    ref = [_run(layer, kw) for kw in calls]
+    shared = layer.ws_spec
+    B = spec.B
+    for i, kw in enumerate(calls):
+        say(f"[shared workspace] bitmap counters, call {i} {kw}")
+        _same(_run(layer, kw, shared), ref[i], f"bitmap call {i}")
+        assert lib.ig_workspace_status(shared) == 0
+        torch.cuda.synchronize()
+        words = shared[256:256 + 8 * B].cpu().numpy()
+        assert not words.any(), f"per-sequence words must return to zero after call {i}"

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(L.exported_symbols())
     for name in declared:
         assert hasattr(lib, name)
-    assert L.ig_version() == 10
+    assert L.ig_version() == 11
 
 
 @pytest.mark.parametrize("m,d", [(256, 64), (128, 128), (64, 16)])
@@ -169,13 +169,13 @@ def test_workspace_sizes(lib):
 
 def test_speculation_workspace_holds_its_documented_regions(lib):
     """The speculation workspace holds (in this order, each 256-byte aligned) the status word and the
-    shape stamp (256 bytes), one arrival word per sequence and the projection's split partial sums
-    [ceil(D/512)][B][H*r] float32, then the slices' candidates when rows are sliced; its size only
-    grows with n."""
+    shape stamp (256 bytes), two words per sequence (the rows' arrivals, then the counter flags) and
+    the projection's split partial sums [ceil(D/512)][B][H*r] float32, then the slices' candidates when
+    rows are sliced; its size only grows with n."""
     a256 = lambda v: (v + 255) // 256 * 256
     for B, H, D, r, n, max_out in [(8, 32, 4096, 32, 2048, 128), (16, 40, 5120, 32, 4352, 218),
                                    (1, 4, 256, 16, 256, 32), (20, 3, 384, 16, 600, 50), (4, 32, 4096, 32, 131072, 5243)]:
-        need = 256 + a256(4 * B) + a256(-(-D // 512) * B * H * r * 4)
+        need = 256 + a256(8 * B) + a256(-(-D // 512) * B * H * r * 4)
         sizes = [L.ig_workspace_size(L.IG_OP_SPECULATE, B, H, D, 128, r, nn, max_out) for nn in (max(1, n // 4), n)]
         assert sizes[1] >= need, (B, H, D, r, n)
         assert sizes[1] >= sizes[0], (B, H, D, r, n)
