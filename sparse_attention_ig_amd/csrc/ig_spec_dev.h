@@ -121,8 +121,8 @@ struct SpecShared {
 
 // Projection workgroups (summary section 3.4 "Decoding Stage" step 1, the partial query
 // x . W~_Q^partial, a dense contraction: M = batch rows, N = H*r partial columns, K = D).  Workgroup
-// pw takes column block pw % proj_blocks (kProjCols columns) and split pw / proj_blocks of the D
-// inputs (kProjSplit of them).  Wave w owns 16-column tile w % kProjTiles and input slice
+// pw takes column block pw / splits (kProjCols columns) and split pw % splits of the D inputs
+// (kProjSplit of them).  Wave w owns 16-column tile w % kProjTiles and input slice
 // w / kProjTiles (kProjSplit / kProjSlices inputs) and runs it on the matrix cores (16x16x32 bf16 or
 // 16x16x4 f32 MFMA, x rows as A in blocks of 16 batch rows, weight columns as B, both loaded 16 bytes
 // (bf16) along k: the weight straight from HBM, x from L2); the slices' 16x16 results meet in LDS and
@@ -160,7 +160,9 @@ __device__ __forceinline__ void proj_role(const SpecParams& p, int pw, uint32_t*
     const int tile = wave % kProjTiles, slice = wave / kProjTiles;
     const int kg = lane / 16;
     const int N = p.H * p.r, D = p.D, B = p.B;
-    const int blk = pw % p.proj_blocks, s = pw / p.proj_blocks;
+    // head-major: the splits of a column block are dispatched together, so the first blocks' partial
+    // queries are complete early and their rows start streaming while later blocks are projected
+    const int blk = pw / p.splits, s = pw - blk * p.splits;
     const int col = blk * kProjCols + tile * 16 + lane % 16;
     const bool col_ok = col < N;
     const int k0 = s * kProjSplit + slice * KPS + kg * M::E;  // this lane's first input (D % E == 0)
