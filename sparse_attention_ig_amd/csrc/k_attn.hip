@@ -26,10 +26,11 @@ AttnPlan plan_attn(int B, int H, int d, int max_out) {
     AttnPlan p{};
     const int64_t bh = static_cast<int64_t>(B) * H;
     // one workgroup per (b, h) when there are enough of them to fill the chip; otherwise split the
-    // selected rows so that about 512 workgroups run, each with at least 128 rows
+    // selected rows so that about 768 workgroups run (three per CU: the last ones to start are short
+    // enough not to trail the rest; measured against 512 and 1024), each with at least 128 rows
     int64_t nsplit = 1;
     if (bh < 256) {
-        nsplit = (512 + bh - 1) / bh;
+        nsplit = (768 + bh - 1) / bh;
         nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, (max_out + 127) / 128));
     }
     int64_t rps = (max_out + nsplit - 1) / nsplit;
