@@ -58,6 +58,7 @@ class Spec:
     frame: str             # "raw": K given unskewed, rotated by the setup; "skewed": K drawn rotated
     skew: str              # "query_svd": A from sample query X_s W_Q; "gauss_block": A from random d x d block
     heavy_shared: bool = False   # same heavy positions for every head (tiny workload)
+    heavy_span: int = 0          # > 0: heavy positions drawn from the first heavy_span rows only
     lognormal: bool = True       # per-channel log-normal K / V scales
     n_cap: int = 0               # allocated rows (0 -> n)
     seed: int = 1000
@@ -212,7 +213,9 @@ def _heavy_positions(spec: Spec, layer: int, b: int, h: int) -> np.ndarray:
         return np.zeros(0, dtype=np.int64)
     key = (0, 0) if spec.heavy_shared else (b, h)
     g = _rng(spec, layer, _P_HEAVY, *key)
-    return np.sort(g.choice(spec.n, size=min(spec.heavy, spec.n), replace=False))
+    span = min(spec.heavy_span, spec.n) if spec.heavy_span > 0 else spec.n
+    assert spec.heavy_span <= 0 or spec.heavy <= span, "heavy rows must fit their span"
+    return np.sort(g.choice(span, size=min(spec.heavy, span), replace=False))
 
 
 def _raw_cache(spec: Spec, layer: int, q_raw: np.ndarray):

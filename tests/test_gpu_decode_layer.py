@@ -170,3 +170,30 @@ def test_decode_layer_single_halves_and_aliasing():
     # the speculation may not write the index list the attention reads
     with pytest.raises(RuntimeError, match="must not be the attention's"):
         L.ig_decode_layer(attn_call(A), spec_call(A, mode="topk", k=64, max_out=64))
+
+
+def test_sliced_merge_recomputes_concentrated_rows():
+    """Tight top-k candidates: each slice hands on about its share of the row's top k.  With every heavy
+    key of a row inside its first slice, that slice holds far more of the top k than it hands on, so
+    the merge finds fewer than k candidates at or above the slices' largest bound and recomputes the
+    row's scores from its partial keys.  The selection must still be the oracle's and the counters
+    exact, and the workspace counts the rows recomputed."""
+    from sparse_attention_ig_amd import _lib as L
+    kw = dict(mode="topk", k=400, max_out=400)
+    spec_fn = lambda: _spec(gen.llama2_7b_long(n=40000, B=1), H=4, topk=400, heavy=400, heavy_span=2400,
+                            gamma=6.0, seed=2012)
+    sb, li_b, Bl, _ = _layers(spec_fn, kw)
+    say(f"[sliced recompute] B{sb.B} H{sb.H} n{sb.n} {kw}")
+    Bl.step(**kw, parts=("speculate",))
+    st, rec = L.ig_workspace_status(Bl.ws_spec, recomputed=True)
+    say(f"[sliced recompute] status {st}, rows recomputed {rec}")
+    assert st == 0
+    assert rec == sb.B * sb.H, "every row's heavy keys sit in one slice: every merge must recompute"
+    g = to_host(dict(idx=Bl.idx, count=Bl.count, counters=Bl.counters, q_part=Bl.q_part))
+    oi = harness.oracle_inputs(sb)
+    ref, ri, rc = harness.oracle_heads(oi, mode="topk", alpha=np.inf, k=kw["k"], max_sel=0,
+                                       max_out=kw["max_out"], attn=False)
+    inexact = harness.check_heads(g["idx"], g["count"], ref, "topk", np.inf, g_q_part=g["q_part"])
+    assert len(inexact) <= max(1, sb.B * sb.H // 50), inexact
+    rC, _ = O.pool_touch(np.zeros((sb.B, sb.cap), np.uint32), ri, rc, sb.n, 65535)
+    harness.check_counters(g["counters"].view(np.uint32), rC, g["idx"], g["count"], ri, rc, sb.n)
